@@ -1,0 +1,192 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the speculative-decoding verify step of one
+ * Gated-DeltaNet (GDN) layer on AMD Instinct MI355X (gfx950).
+ *
+ * The step, as the pages on the subject describe it:
+ *   1. a fused depthwise causal conv1d over the verify window: history window,
+ *      silu(conv), history written back in place, and the window kept so that
+ *      a partial accept can restore the conv state (lucebox PR #637
+ *      "NVLink fix for PR625": commit message on ggml_ssm_conv_step, review
+ *      note on its sources x, weights, conv_state, conv_input_out; atlas
+ *      PR #297 "dflash scheduler/server verify-step glue": commit message on
+ *      causal_conv1d_update_prefill_inter and its per-token conv-state
+ *      intermediates);
+ *   2. the gated delta rule over the K window tokens with raw gates applied
+ *      inside the kernel, q and k L2-normalised and broadcast from key heads
+ *      to value heads, evaluated chunkwise in WY form, writing the final state
+ *      plus every intermediate state H_0..H_{K-2} (lucebox PR #637: commit
+ *      messages on raw-gate gated_delta_net and the single l2_norm over the
+ *      q|k slab, review excerpt of gated_delta_net.cu; atlas PR #297: commit
+ *      message on gated_delta_rule_wy16.cu and its opt-in fp32 output);
+ *   3. rollback of the conv and GDN state to the accepted length (the same
+ *      pages; strix-llama.cpp PR #14 "DSv4 + Qwen3.8 Flash runtime fixes":
+ *      commit messages on recurrent snapshot rollback and device-resident
+ *      checkpoints);
+ *   4. chunked prefill of the same layer, final state only.
+ *
+ * Recurrence, per sequence b and value head h (key head hk = h / (Hv/Hk)):
+ *   beta_t = sigmoid(beta_raw_t)
+ *   g_t    = -softplus(alpha_t + dt_bias[h]) * exp(A_log[h])
+ *   q^, k^ = q / sqrt(|q|^2 + l2_eps), k / sqrt(|k|^2 + l2_eps)
+ *   S_t    = exp(g_t) S_{t-1} (I - beta_t k^_t k^_t^T) + beta_t v_t k^_t^T
+ *   o_t    = S_t q^_t
+ * S is dv x dk (row i is value index i, columns are key dims), fp32.
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or keeps device memory, never
+ *     synchronises, and launches only on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Calls are stream-ordered; two calls that write the
+ *     same buffer must not run concurrently on different streams.
+ *   - Arrays are dense and row-major in the index order written next to them.
+ *   - dtype codes: GDN_F32 (float) or GDN_BF16 (bfloat16 bits, uint16).
+ *   - Pointers must be 16-byte aligned.
+ *   - Arguments are checked on the host before anything is launched; a bad
+ *     argument returns a negative code, launches nothing and leaves every
+ *     buffer untouched.  gdn_last_error() gives a message (thread-local).
+ *   - B == 0 is a valid empty call: GDN_OK, nothing launched.
+ *   - Thread-safe: the only global state is the thread-local error message.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_VERSION 1
+
+enum gdn_status {
+    GDN_OK = 0,
+    GDN_EINVAL = -1,       /* null / misaligned / overlapping pointer, bad size */
+    GDN_EUNSUPPORTED = -2, /* valid request outside what the kernels implement */
+    GDN_EHIP = -3          /* the HIP runtime reported an error at launch */
+};
+
+enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 };
+
+/* GDN_VERSION of the built library. */
+int gdn_version(void);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *gdn_last_error(void);
+
+/*
+ * gdn_conv_step -- fused causal depthwise conv1d decode / verify step.
+ *
+ * For each sequence b and channel c the window is
+ *     win[j] = hist[b][j][c]          for j < W-1
+ *     win[j] = x[b][j-(W-1)][c]       for W-1 <= j < W-1+T
+ * and for every new token t < T
+ *     pre_t = sum_{j<W} w[c][j] * win[t+j]     (w[c][W-1] meets token t)
+ *     y[b][t][c] = silu(pre_t) = pre_t / (1 + exp(-pre_t))
+ * The history is then written back in place: hist[b][j][c] = win[T+j].
+ * If win_out is not NULL it receives the whole window,
+ *     win_out[b][j][c] = win[j],  j < W-1+T,
+ * so that the conv state after a accepted tokens is rows a..a+W-2
+ * (see gdn_rollback).
+ *
+ * Numerics: pre is an fmaf chain over j = 0..W-1 starting from 0; exp is
+ * the library's own float exp (Cody-Waite reduction by ln 2, degree-7
+ * Taylor polynomial in Horner form with fmaf, exact scaling by 2^n); the
+ * division is correctly rounded; bf16 outputs are rounded to nearest even.
+ * The result is therefore a fixed function of the inputs, reproducible bit
+ * for bit by any implementation of the same steps.
+ *
+ *   x        [B][T][C]        io_dtype, the T new tokens
+ *   w        [C][W]           float, depthwise taps
+ *   hist     [B][W-1][C]      io_dtype, read then overwritten
+ *   y        [B][T][C]        io_dtype, output (q|k|v slab for gdn_verify)
+ *   win_out  [B][W-1+T][C]    io_dtype, output, may be NULL
+ *   B >= 0, T >= 1, C >= 1, 2 <= W <= 8
+ * y and win_out must not overlap x, w, hist or each other.
+ */
+int gdn_conv_step(const void *x, const float *w, void *hist, void *y, void *win_out,
+                  int B, int T, int C, int W, int io_dtype, void *stream);
+
+/*
+ * gdn_verify -- gated delta rule over a K-token verify window, with capture.
+ *
+ * Gate mode: if dt_bias and A_log are both non-NULL, beta_raw and alpha are
+ * raw projections and the gates above are applied in the kernel (softplus
+ * switches to the identity above 20).  If both are NULL, beta_raw holds beta
+ * and alpha holds g already activated.  One NULL and one not is GDN_EINVAL.
+ *
+ * Evaluation: chunkwise WY form over the window.  With G_t = sum_{s<=t} g_s,
+ *   A[t][s] = beta_t exp(G_t - G_s) k^_t.k^_s  (s < t),  T = (I + A)^{-1},
+ *   u = T (beta (v - exp(G) S_in k^))          (per state row),
+ *   o_t = exp(G_t) S_in q^_t + sum_{s<=t} exp(G_t - G_s) (q^_t.k^_s) u_s,
+ *   H_t = exp(g_t) H_{t-1} + u_t k^_t^T,       H_{-1} = S_in.
+ *
+ *   qkv      [B][K][C]    in_dtype; C = 2*Hk*dk + Hv*dv; per token the q of
+ *                         all key heads, then their k, then the v of all
+ *                         value heads (the gdn_conv_step output)
+ *   beta_raw [B][K][Hv]   in_dtype
+ *   alpha    [B][K][Hv]   in_dtype
+ *   dt_bias  [Hv]         float or NULL
+ *   A_log    [Hv]         float or NULL
+ *   S_in     [B][Hv][dv][dk] float, the state before the window
+ *   S_out    [B][Hv][dv][dk] float, the state after all K tokens; may be
+ *                         exactly S_in (in place; then rollback to 0 tokens
+ *                         is impossible); any other overlap is GDN_EINVAL
+ *   H        [B][K-1][Hv][dv][dk] float, H[b][t] = state after tokens
+ *                         0..t; may be NULL (no capture); must not overlap
+ *                         S_in / S_out
+ *   o        [B][K][Hv][dv] o_dtype, o_t = S_t q^_t
+ *   B >= 0; 1 <= K <= 32; Hk >= 1; Hv % Hk == 0;
+ *   dk in {32, 64, 128}; dv a multiple of 8
+ *   l2_eps >= 0
+ */
+int gdn_verify(const void *qkv, const void *beta_raw, const void *alpha,
+               const float *dt_bias, const float *A_log,
+               const float *S_in, float *S_out, float *H, void *o,
+               int B, int K, int Hk, int Hv, int dk, int dv,
+               int in_dtype, int o_dtype, float l2_eps, void *stream);
+
+/*
+ * gdn_rollback -- restore conv and GDN state to the accepted length.
+ *
+ * For each sequence b, a = accept[b] (device int32; values outside 0..K are
+ * clamped) is the number of window tokens kept:
+ *   state: S_out[b] <- S_in[b]      if a == 0
+ *          S_out[b] <- H[b][a-1]    if 0 < a < K
+ *          unchanged                if a == K (gdn_verify already wrote it)
+ *   conv:  hist[b][j] <- win[b][a+j], j < W-1
+ * Bit-exact copies.  Needs the pre-window state, so S_out must not be S_in.
+ *
+ *   accept   [B] int32, device
+ *   S_in     [B][Hv][dv][dk] float
+ *   H        [B][K-1][Hv][dv][dk] float (may be NULL only when K == 1)
+ *   S_out    [B][Hv][dv][dk] float
+ *   hist     [B][W-1][C] io_dtype, or NULL together with win to skip conv
+ *   win      [B][W-1+K][C] io_dtype (gdn_conv_step's win_out)
+ *   B >= 0, K >= 1, 2 <= W <= 8 when hist is given
+ */
+int gdn_rollback(const int32_t *accept, int K,
+                 const float *S_in, const float *H, float *S_out,
+                 void *hist, const void *win,
+                 int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void *stream);
+
+/*
+ * gdn_prefill_chunked -- the same recurrence over a long prompt, processed
+ * in chunks of `chunk` tokens, writing only the final state and the outputs.
+ *
+ *   qkv      [B][T][C], beta_raw/alpha [B][T][Hv]: as gdn_verify with K -> T
+ *   S_in, S_out [B][Hv][dv][dk] float (S_out may be exactly S_in)
+ *   o        [B][T][Hv][dv] o_dtype
+ *   B >= 0, T >= 1 (the last chunk may be shorter), chunk in {16, 32, 64},
+ *   the other sizes as gdn_verify
+ */
+int gdn_prefill_chunked(const void *qkv, const void *beta_raw, const void *alpha,
+                        const float *dt_bias, const float *A_log,
+                        const float *S_in, float *S_out, void *o,
+                        int B, int T, int chunk, int Hk, int Hv, int dk, int dv,
+                        int in_dtype, int o_dtype, float l2_eps, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

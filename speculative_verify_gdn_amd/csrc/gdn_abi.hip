@@ -1,0 +1,221 @@
+// gdn_abi.hip -- the extern "C" entry points of libgdn (declared in
+// include/gdn.h): argument validation on the host, then one launch on the
+// caller's stream.  Nothing is allocated, nothing is synchronised.
+//
+// Every check happens before any launch, because a device fault takes the
+// whole context down with it (the pages report exactly that failure mode:
+// atlas PR #297, commit message on the illegal-address crash that poisoned
+// the CUDA context).
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return GDN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlap(Span a, Span b)
+{
+    if (a.p == nullptr || b.p == nullptr || a.bytes == 0 || b.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+int launch_status(hipError_t e, const char* what)
+{
+    if (e != hipSuccess) return fail(GDN_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+size_t elem_size(int dtype) { return dtype == GDN_BF16 ? 2 : 4; }
+
+bool valid_dtype(int d) { return d == GDN_F32 || d == GDN_BF16; }
+
+#define REQUIRE(cond, code, ...)          \
+    do {                                  \
+        if (!(cond)) return fail(code, __VA_ARGS__); \
+    } while (0)
+
+// shared checks of the GDN shapes (verify and prefill)
+int check_gdn_shape(const char* fn, int B, int K, int Hk, int Hv, int dk, int dv, int in_dtype, int o_dtype,
+                    float eps)
+{
+    REQUIRE(B >= 0, GDN_EINVAL, "%s: B = %d < 0", fn, B);
+    REQUIRE(K >= 1, GDN_EINVAL, "%s: token count %d < 1", fn, K);
+    REQUIRE(Hk >= 1 && Hv >= 1, GDN_EINVAL, "%s: Hk = %d, Hv = %d must be >= 1", fn, Hk, Hv);
+    REQUIRE(Hv % Hk == 0, GDN_EINVAL, "%s: Hv = %d is not a multiple of Hk = %d", fn, Hv, Hk);
+    REQUIRE(dk >= 1 && dv >= 1, GDN_EINVAL, "%s: dk = %d, dv = %d must be >= 1", fn, dk, dv);
+    REQUIRE(dk == 32 || dk == 64 || dk == 128, GDN_EUNSUPPORTED, "%s: dk = %d not in {32, 64, 128}", fn, dk);
+    REQUIRE(dv % 8 == 0, GDN_EUNSUPPORTED, "%s: dv = %d is not a multiple of 8", fn, dv);
+    REQUIRE(valid_dtype(in_dtype) && valid_dtype(o_dtype), GDN_EINVAL, "%s: bad dtype code (%d, %d)", fn,
+            in_dtype, o_dtype);
+    REQUIRE(eps >= 0.0f, GDN_EINVAL, "%s: l2_eps < 0", fn);
+    return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return GDN_VERSION; }
+
+const char* gdn_last_error(void) { return g_err; }
+
+int gdn_conv_step(const void* x, const float* w, void* hist, void* y, void* win_out, int B, int T, int C, int W,
+                  int io_dtype, void* stream)
+{
+    const char* fn = "gdn_conv_step";
+    REQUIRE(B >= 0, GDN_EINVAL, "%s: B = %d < 0", fn, B);
+    REQUIRE(T >= 1, GDN_EINVAL, "%s: T = %d < 1", fn, T);
+    REQUIRE(C >= 1, GDN_EINVAL, "%s: C = %d < 1", fn, C);
+    REQUIRE(W >= 2 && W <= 8, GDN_EUNSUPPORTED, "%s: W = %d not in 2..8", fn, W);
+    REQUIRE(valid_dtype(io_dtype), GDN_EINVAL, "%s: bad dtype code %d", fn, io_dtype);
+    REQUIRE((long long)B * T * C < (1LL << 40), GDN_EUNSUPPORTED, "%s: problem too large", fn);
+    if (B == 0) return ok();
+    REQUIRE(x && w && hist && y, GDN_EINVAL, "%s: null pointer (x, w, hist and y are required)", fn);
+    REQUIRE(aligned16(x) && aligned16(w) && aligned16(hist) && aligned16(y) && (!win_out || aligned16(win_out)),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    const size_t es = elem_size(io_dtype);
+    const Span sx{x, (size_t)B * T * C * es}, sw{w, (size_t)C * W * 4}, sh{hist, (size_t)B * (W - 1) * C * es},
+        sy{y, (size_t)B * T * C * es}, swin{win_out, win_out ? (size_t)B * (W - 1 + T) * C * es : 0};
+    REQUIRE(!overlap(sy, sx) && !overlap(sy, sw) && !overlap(sy, sh), GDN_EINVAL, "%s: y overlaps an input", fn);
+    REQUIRE(!overlap(swin, sx) && !overlap(swin, sw) && !overlap(swin, sh) && !overlap(swin, sy), GDN_EINVAL,
+            "%s: win_out overlaps another buffer", fn);
+    REQUIRE(!overlap(sh, sx) && !overlap(sh, sw), GDN_EINVAL, "%s: hist overlaps x or w", fn);
+    REQUIRE(T <= 65535 * 8, GDN_EUNSUPPORTED, "%s: T = %d too large", fn, T);
+    REQUIRE(B <= 65535, GDN_EUNSUPPORTED, "%s: B = %d too large", fn, B);
+    gdn::ConvArgs a{x, w, hist, y, win_out, B, T, C, W};
+    return launch_status(gdn::launch_conv_step(a, io_dtype == GDN_BF16, (hipStream_t)stream), fn);
+}
+
+int gdn_verify(const void* qkv, const void* beta_raw, const void* alpha, const float* dt_bias, const float* A_log,
+               const float* S_in, float* S_out, float* H, void* o, int B, int K, int Hk, int Hv, int dk, int dv,
+               int in_dtype, int o_dtype, float l2_eps, void* stream)
+{
+    const char* fn = "gdn_verify";
+    int rc = check_gdn_shape(fn, B, K, Hk, Hv, dk, dv, in_dtype, o_dtype, l2_eps);
+    if (rc) return rc;
+    REQUIRE(K <= 32, GDN_EUNSUPPORTED, "%s: K = %d > 32", fn, K);
+    REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
+    REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
+            "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
+    if (B == 0) return ok();
+    REQUIRE(qkv && beta_raw && alpha && S_in && S_out && o, GDN_EINVAL, "%s: null pointer", fn);
+    REQUIRE(aligned16(qkv) && aligned16(beta_raw) && aligned16(alpha) && aligned16(S_in) && aligned16(S_out) &&
+                aligned16(o) && (!H || aligned16(H)) && (!dt_bias || (aligned16(dt_bias) && aligned16(A_log))),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    const size_t ie = elem_size(in_dtype), oe = elem_size(o_dtype);
+    const size_t C = (size_t)2 * Hk * dk + (size_t)Hv * dv;
+    const size_t SD = (size_t)B * Hv * dv * dk * 4;
+    const Span sq{qkv, (size_t)B * K * C * ie}, sb{beta_raw, (size_t)B * K * Hv * ie},
+        sa{alpha, (size_t)B * K * Hv * ie}, ssi{S_in, SD}, sso{S_out, SD},
+        sH{H, H ? (size_t)B * (K - 1) * Hv * dv * dk * 4 : 0}, so{o, (size_t)B * K * Hv * dv * oe},
+        sdt{dt_bias, dt_bias ? (size_t)Hv * 4 : 0}, sal{A_log, A_log ? (size_t)Hv * 4 : 0};
+    REQUIRE(!(overlap(sso, ssi) && S_out != S_in), GDN_EINVAL, "%s: S_out partially overlaps S_in", fn);
+    const Span ins[] = {sq, sb, sa, sdt, sal};
+    for (const Span& s : ins) {
+        REQUIRE(!overlap(sso, s), GDN_EINVAL, "%s: S_out overlaps an input", fn);
+        REQUIRE(!overlap(sH, s) && !overlap(so, s), GDN_EINVAL, "%s: H or o overlaps an input", fn);
+    }
+    REQUIRE(!overlap(sH, ssi) && !overlap(sH, sso) && !overlap(so, ssi) && !overlap(so, sso) && !overlap(so, sH),
+            GDN_EINVAL, "%s: H, o and the state buffers must not overlap", fn);
+    gdn::VerifyArgs a{qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o, B, K, Hk, Hv, dk, dv, l2_eps};
+    return launch_status(gdn::launch_verify(a, in_dtype == GDN_BF16, o_dtype == GDN_BF16, (hipStream_t)stream), fn);
+}
+
+int gdn_rollback(const int32_t* accept, int K, const float* S_in, const float* H, float* S_out, void* hist,
+                 const void* win, int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void* stream)
+{
+    const char* fn = "gdn_rollback";
+    REQUIRE(B >= 0, GDN_EINVAL, "%s: B = %d < 0", fn, B);
+    REQUIRE(K >= 1, GDN_EINVAL, "%s: K = %d < 1", fn, K);
+    REQUIRE(Hv >= 1 && dv >= 1 && dk >= 1, GDN_EINVAL, "%s: bad state shape", fn);
+    REQUIRE(((long long)Hv * dv * dk) % 4 == 0, GDN_EUNSUPPORTED, "%s: Hv*dv*dk must be a multiple of 4", fn);
+    REQUIRE((hist == nullptr) == (win == nullptr), GDN_EINVAL, "%s: hist and win must be both given or both NULL",
+            fn);
+    if (hist) {
+        REQUIRE(C >= 1, GDN_EINVAL, "%s: C = %d < 1", fn, C);
+        REQUIRE(W >= 2 && W <= 8, GDN_EUNSUPPORTED, "%s: W = %d not in 2..8", fn, W);
+        REQUIRE(valid_dtype(io_dtype), GDN_EINVAL, "%s: bad dtype code %d", fn, io_dtype);
+    }
+    REQUIRE(B <= 65535, GDN_EUNSUPPORTED, "%s: B = %d too large", fn, B);
+    if (B == 0) return ok();
+    REQUIRE(accept && S_in && S_out, GDN_EINVAL, "%s: null pointer", fn);
+    REQUIRE(H || K == 1, GDN_EINVAL, "%s: H is required when K > 1", fn);
+    REQUIRE(S_in != S_out, GDN_EINVAL, "%s: S_out must not be S_in (the pre-window state is needed)", fn);
+    REQUIRE(aligned16(S_in) && aligned16(S_out) && (!H || aligned16(H)) && aligned16(accept) &&
+                (!hist || (aligned16(hist) && aligned16(win))),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    const size_t st = (size_t)Hv * dv * dk * 4;
+    const Span ssi{S_in, B * st}, sso{S_out, B * st}, sH{H, H ? (size_t)B * (K - 1) * st : 0};
+    REQUIRE(!overlap(sso, ssi) && !overlap(sso, sH), GDN_EINVAL, "%s: S_out overlaps S_in or H", fn);
+    if (hist) {
+        const size_t es = elem_size(io_dtype);
+        const Span sh{hist, (size_t)B * (W - 1) * C * es}, sw{win, (size_t)B * (W - 1 + K) * C * es};
+        REQUIRE(!overlap(sh, sw) && !overlap(sh, sso) && !overlap(sh, ssi) && !overlap(sh, sH), GDN_EINVAL,
+                "%s: hist overlaps another buffer", fn);
+    }
+    gdn::RollbackArgs a{accept, S_in, H, S_out, hist, win, B, K, (long long)Hv * dv * dk, C, W,
+                        (int)elem_size(io_dtype)};
+    return launch_status(gdn::launch_rollback(a, (hipStream_t)stream), fn);
+}
+
+int gdn_prefill_chunked(const void* qkv, const void* beta_raw, const void* alpha, const float* dt_bias,
+                        const float* A_log, const float* S_in, float* S_out, void* o, int B, int T, int chunk,
+                        int Hk, int Hv, int dk, int dv, int in_dtype, int o_dtype, float l2_eps, void* stream)
+{
+    const char* fn = "gdn_prefill_chunked";
+    int rc = check_gdn_shape(fn, B, T, Hk, Hv, dk, dv, in_dtype, o_dtype, l2_eps);
+    if (rc) return rc;
+    REQUIRE(chunk == 16 || chunk == 32 || chunk == 64, GDN_EUNSUPPORTED, "%s: chunk = %d not in {16, 32, 64}", fn,
+            chunk);
+    REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
+    REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
+            "%s: dt_bias and A_log must be both given or both NULL", fn);
+    if (B == 0) return ok();
+    REQUIRE(qkv && beta_raw && alpha && S_in && S_out && o, GDN_EINVAL, "%s: null pointer", fn);
+    REQUIRE(aligned16(qkv) && aligned16(beta_raw) && aligned16(alpha) && aligned16(S_in) && aligned16(S_out) &&
+                aligned16(o) && (!dt_bias || (aligned16(dt_bias) && aligned16(A_log))),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    const size_t ie = elem_size(in_dtype), oe = elem_size(o_dtype);
+    const size_t C = (size_t)2 * Hk * dk + (size_t)Hv * dv;
+    const size_t SD = (size_t)B * Hv * dv * dk * 4;
+    const Span sq{qkv, (size_t)B * T * C * ie}, sb{beta_raw, (size_t)B * T * Hv * ie},
+        sa{alpha, (size_t)B * T * Hv * ie}, ssi{S_in, SD}, sso{S_out, SD}, so{o, (size_t)B * T * Hv * dv * oe};
+    REQUIRE(!(overlap(sso, ssi) && S_out != S_in), GDN_EINVAL, "%s: S_out partially overlaps S_in", fn);
+    const Span ins[] = {sq, sb, sa};
+    for (const Span& s : ins)
+        REQUIRE(!overlap(sso, s) && !overlap(so, s), GDN_EINVAL, "%s: an output overlaps an input", fn);
+    REQUIRE(!overlap(so, ssi) && !overlap(so, sso), GDN_EINVAL, "%s: o overlaps the state", fn);
+    gdn::PrefillArgs a{qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, o, B, T, chunk, Hk, Hv, dk, dv, l2_eps};
+    return launch_status(gdn::launch_prefill(a, in_dtype == GDN_BF16, o_dtype == GDN_BF16, (hipStream_t)stream),
+                         fn);
+}
+
+}  // extern "C"

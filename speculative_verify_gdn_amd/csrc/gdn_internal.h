@@ -1,0 +1,64 @@
+// gdn_internal.h -- launchers behind the C ABI of libgdn (include/gdn.h).
+// The ABI layer validates every argument on the host; the launchers assume
+// valid arguments and only pick a kernel instance and a grid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct ConvArgs {
+    const void* x;      // [B][T][C]
+    const float* w;     // [C][W]
+    void* hist;         // [B][W-1][C], read then written
+    void* y;            // [B][T][C]
+    void* win;          // [B][W-1+T][C] or nullptr
+    int B, T, C, W;
+};
+
+struct VerifyArgs {
+    const void* qkv;       // [B][K][C]
+    const void* beta_raw;  // [B][K][Hv]
+    const void* alpha;     // [B][K][Hv]
+    const float* dt_bias;  // [Hv] or nullptr (activated gates)
+    const float* A_log;    // [Hv] or nullptr
+    const float* S_in;     // [B][Hv][dv][dk]
+    float* S_out;          // [B][Hv][dv][dk]
+    float* H;              // [B][K-1][Hv][dv][dk] or nullptr
+    void* o;               // [B][K][Hv][dv]
+    int B, K, Hk, Hv, dk, dv;
+    float eps;
+};
+
+struct RollbackArgs {
+    const int32_t* accept;  // [B]
+    const float* S_in;      // [B][Hv][dv][dk]
+    const float* H;         // [B][K-1][Hv][dv][dk]
+    float* S_out;           // [B][Hv][dv][dk]
+    void* hist;             // [B][W-1][C] or nullptr
+    const void* win;        // [B][W-1+K][C] or nullptr
+    int B, K;
+    long long state_elems;  // Hv*dv*dk
+    int C, W, elem_bytes;
+};
+
+struct PrefillArgs {
+    const void* qkv;       // [B][T][C]
+    const void* beta_raw;  // [B][T][Hv]
+    const void* alpha;     // [B][T][Hv]
+    const float* dt_bias;
+    const float* A_log;
+    const float* S_in;
+    float* S_out;
+    void* o;               // [B][T][Hv][dv]
+    int B, T, chunk, Hk, Hv, dk, dv;
+    float eps;
+};
+
+hipError_t launch_conv_step(const ConvArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_verify(const VerifyArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
+hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
+
+}  // namespace gdn

@@ -1,0 +1,89 @@
+// gdn_rollback.hip -- restore the conv and GDN state to the accepted length.
+//
+// After a verify window of K tokens the host (or a later device step) decides
+// how many tokens a in 0..K each sequence keeps.  The states after every
+// prefix were captured by gdn_verify (H) and gdn_conv_step (the window), so
+// rollback is a pure copy (the pages' recurrent snapshot rollback planes and
+// per-token conv_state intermediates: strix-llama.cpp PR #14 commit messages;
+// atlas PR #297 commit message on causal_conv1d_update_prefill_inter):
+//   S_out[b] <- S_in[b] (a = 0) | H[b][a-1] (0 < a < K) | unchanged (a = K)
+//   hist[b][j] <- win[b][a+j],  j < W-1
+// The accept lengths are read on the device, so the copy needs no host sync.
+//
+// Grid: x covers one sequence's state in 16 KB slabs (256 threads x 4 float4)
+// followed by its conv rows; y is the sequence.  Workgroups of sequences with
+// a == K return at once.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVecPerThread = 4;
+constexpr long long kSlab = (long long)kThreads * kVecPerThread * 4;  // floats per workgroup
+
+__global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int state_blocks)
+{
+    const int b = blockIdx.y;
+    const int K = a.K;
+    int acc = a.accept[b];
+    acc = acc < 0 ? 0 : (acc > K ? K : acc);
+    if (acc == K) return;
+
+    if ((int)blockIdx.x < state_blocks) {
+        const float* src = acc == 0 ? a.S_in + (size_t)b * a.state_elems
+                                    : a.H + ((size_t)b * (K - 1) + (acc - 1)) * a.state_elems;
+        float* dst = a.S_out + (size_t)b * a.state_elems;
+        const long long base = (long long)blockIdx.x * kSlab;
+        f32x4_t v[kVecPerThread];
+#pragma unroll
+        for (int j = 0; j < kVecPerThread; ++j) {
+            const long long e = base + ((long long)j * kThreads + threadIdx.x) * 4;
+            if (e < a.state_elems) v[j] = load_f4(src + e);
+        }
+#pragma unroll
+        for (int j = 0; j < kVecPerThread; ++j) {
+            const long long e = base + ((long long)j * kThreads + threadIdx.x) * 4;
+            if (e < a.state_elems) store_f4<false>(dst + e, v[j]);
+        }
+        return;
+    }
+
+    // conv rows: (W-1)*C elements, copied as 16-bit units (bf16) or 32-bit units (f32)
+    if (a.hist == nullptr) return;
+    const long long n = (long long)(a.W - 1) * a.C;
+    const long long e = ((long long)(blockIdx.x - state_blocks) * kThreads + threadIdx.x) * 8;
+    const size_t src0 = ((size_t)b * (a.W - 1 + K) + acc) * a.C;
+    const size_t dst0 = (size_t)b * (a.W - 1) * a.C;
+    if (a.elem_bytes == 2) {
+        const uint16_t* s = reinterpret_cast<const uint16_t*>(a.win) + src0;
+        uint16_t* d = reinterpret_cast<uint16_t*>(a.hist) + dst0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (e + j < n) d[e + j] = s[e + j];
+    } else {
+        const uint32_t* s = reinterpret_cast<const uint32_t*>(a.win) + src0;
+        uint32_t* d = reinterpret_cast<uint32_t*>(a.hist) + dst0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (e + j < n) d[e + j] = s[e + j];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s)
+{
+    const int state_blocks = (int)((a.state_elems + kSlab - 1) / kSlab);
+    int conv_blocks = 0;
+    if (a.hist != nullptr) {
+        const long long n = (long long)(a.W - 1) * a.C;
+        conv_blocks = (int)((n + kThreads * 8 - 1) / (kThreads * 8));
+    }
+    dim3 grid(state_blocks + conv_blocks, a.B);
+    rollback_kernel<<<grid, dim3(kThreads), 0, s>>>(a, state_blocks);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -1,0 +1,135 @@
+"""ctypes binding of libgdn.so (include/gdn.h) for torch device tensors.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels.  Each function takes torch tensors that already live on the GPU,
+passes their device pointers, the sizes and torch's current HIP stream to the
+C entry point of the same name, and raises GdnError on a non-zero status.
+There is no fallback: if libgdn.so is missing or cannot be loaded, the first
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
+
+GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
+GDN_F32, GDN_BF16 = 0, 1
+EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("libgdn error %d: %s" % (code, msg))
+        self.code = code
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load(path: str = LIB_PATH):
+    """Load libgdn.so (once) and declare the C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise FileNotFoundError("libgdn.so not built (%s); run python -m speculative_verify_gdn_amd.build"
+                                    % path)
+        lib = ctypes.CDLL(path)
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.gdn_version.restype = I
+        lib.gdn_last_error.restype = ctypes.c_char_p
+        lib.gdn_conv_step.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+        lib.gdn_verify.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+        lib.gdn_rollback.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        lib.gdn_prefill_chunked.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P]
+        for name in EXPORTS:
+            getattr(lib, name).restype = ctypes.c_char_p if name == "gdn_last_error" else I
+        _lib = lib
+        return lib
+
+
+def _check(rc: int):
+    if rc != GDN_OK:
+        raise GdnError(rc, load().gdn_last_error().decode())
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("libgdn takes device tensors")
+            if not t.is_contiguous():
+                raise ValueError("libgdn takes contiguous tensors")
+
+
+def version() -> int:
+    return load().gdn_version()
+
+
+def conv_step(x, w, hist, y, win=None, stream=None):
+    """gdn_conv_step: x [B][T][C], w [C][W] f32, hist [B][W-1][C] (updated), y, win [B][W-1+T][C]."""
+    _dev(x, w, hist, y, win)
+    B, T, C = x.shape
+    W = w.shape[1]
+    _check(load().gdn_conv_step(_p(x), _p(w), _p(hist), _p(y), _p(win), B, T, C, W, _dtype(x), _stream(stream)))
+
+
+def verify(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o, Hk, eps=1e-6, stream=None):
+    """gdn_verify: qkv [B][K][C], gates [B][K][Hv], S [B][Hv][dv][dk] f32, H [B][K-1][Hv][dv][dk] or None,
+    o [B][K][Hv][dv]."""
+    _dev(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o)
+    B, K, _ = qkv.shape
+    _, Hv, dv, dk = S_in.shape
+    _check(load().gdn_verify(_p(qkv), _p(beta_raw), _p(alpha), _p(dt_bias), _p(A_log), _p(S_in), _p(S_out),
+                             _p(H), _p(o), B, K, Hk, Hv, dk, dv, _dtype(qkv), _dtype(o), float(eps),
+                             _stream(stream)))
+
+
+def rollback(accept, K, S_in, H, S_out, hist=None, win=None, stream=None):
+    """gdn_rollback: accept [B] int32 (device), S_in/S_out [B][Hv][dv][dk], H [B][K-1][...] or None."""
+    _dev(accept, S_in, H, S_out, hist, win)
+    B, Hv, dv, dk = S_in.shape
+    if hist is not None:
+        W = hist.shape[1] + 1
+        C = hist.shape[2]
+        io = _dtype(hist)
+    else:
+        W, C, io = 2, 1, GDN_F32
+    _check(load().gdn_rollback(_p(accept), int(K), _p(S_in), _p(H), _p(S_out), _p(hist), _p(win),
+                               B, Hv, dv, dk, C, W, io, _stream(stream)))
+
+
+def prefill_chunked(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, o, Hk, chunk=64, eps=1e-6, stream=None):
+    """gdn_prefill_chunked: qkv [B][T][C], gates [B][T][Hv], S [B][Hv][dv][dk], o [B][T][Hv][dv]."""
+    _dev(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, o)
+    B, T, _ = qkv.shape
+    _, Hv, dv, dk = S_in.shape
+    _check(load().gdn_prefill_chunked(_p(qkv), _p(beta_raw), _p(alpha), _p(dt_bias), _p(A_log), _p(S_in),
+                                      _p(S_out), _p(o), B, T, int(chunk), Hk, Hv, dk, dv, _dtype(qkv), _dtype(o),
+                                      float(eps), _stream(stream)))

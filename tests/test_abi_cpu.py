@@ -1,0 +1,171 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/gdn.h declares, and rejects every invalid argument on the host with
+the documented status code before anything is launched.
+
+Fake device addresses are fine here because validation fails (or B == 0
+returns) before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from speculative_verify_gdn_amd import gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+A = 0x7F0000000000  # a fake, 16-byte aligned "device" address; never dereferenced
+MB = 1 << 24
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.skip("libgdn.so not built")
+    return gdn.load()
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(gdn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (gdn_[a-z_]+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_matches_header(lib):
+    m = re.search(r"#define GDN_VERSION (\d+)", open(HEADER).read())
+    assert lib.gdn_version() == int(m.group(1))
+
+
+def p(off=0):
+    return ctypes.c_void_p(A + off * MB)
+
+
+def verify_call(lib, **kw):
+    args = dict(qkv=p(0), beta=p(1), alpha=p(2), dt=p(3), alog=p(4), S_in=p(5), S_out=p(6), H=p(8), o=p(12),
+                B=1, K=4, Hk=2, Hv=2, dk=32, dv=32, ind=gdn.GDN_F32, od=gdn.GDN_F32, eps=1e-6)
+    args.update(kw)
+    return lib.gdn_verify(args["qkv"], args["beta"], args["alpha"], args["dt"], args["alog"], args["S_in"],
+                          args["S_out"], args["H"], args["o"], args["B"], args["K"], args["Hk"], args["Hv"],
+                          args["dk"], args["dv"], args["ind"], args["od"], args["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qkv=None), gdn.GDN_EINVAL),
+    (dict(S_in=None), gdn.GDN_EINVAL),
+    (dict(o=None), gdn.GDN_EINVAL),
+    (dict(qkv=ctypes.c_void_p(A + 4)), gdn.GDN_EINVAL),          # misaligned
+    (dict(K=0), gdn.GDN_EINVAL),
+    (dict(K=33), gdn.GDN_EUNSUPPORTED),
+    (dict(dk=48, dv=48), gdn.GDN_EUNSUPPORTED),
+    (dict(dv=20), gdn.GDN_EUNSUPPORTED),
+    (dict(Hk=2, Hv=3), gdn.GDN_EINVAL),
+    (dict(Hk=0), gdn.GDN_EINVAL),
+    (dict(B=-1), gdn.GDN_EINVAL),
+    (dict(dt=None), gdn.GDN_EINVAL),                              # one of the two gate params
+    (dict(ind=7), gdn.GDN_EINVAL),
+    (dict(eps=-1.0), gdn.GDN_EINVAL),
+    (dict(S_out=ctypes.c_void_p(A + 5 * MB + 64)), gdn.GDN_EINVAL),  # partial overlap with S_in
+    (dict(H=ctypes.c_void_p(A + 5 * MB)), gdn.GDN_EINVAL),        # H overlaps S_in
+    (dict(o=ctypes.c_void_p(A + 0)), gdn.GDN_EINVAL),             # o overlaps qkv
+])
+def test_verify_rejects(lib, kw, code):
+    assert verify_call(lib, **kw) == code
+    assert lib.gdn_last_error().decode().startswith("gdn_verify")
+
+
+def test_verify_empty_batch_is_ok(lib):
+    assert verify_call(lib, B=0) == gdn.GDN_OK
+    assert lib.gdn_last_error().decode() == ""
+
+
+def conv_call(lib, **kw):
+    a = dict(x=p(0), w=p(1), hist=p(2), y=p(3), win=p(4), B=1, T=4, C=192, W=4, io=gdn.GDN_BF16)
+    a.update(kw)
+    return lib.gdn_conv_step(a["x"], a["w"], a["hist"], a["y"], a["win"], a["B"], a["T"], a["C"], a["W"], a["io"],
+                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), gdn.GDN_EINVAL),
+    (dict(hist=None), gdn.GDN_EINVAL),
+    (dict(T=0), gdn.GDN_EINVAL),
+    (dict(C=0), gdn.GDN_EINVAL),
+    (dict(W=1), gdn.GDN_EUNSUPPORTED),
+    (dict(W=9), gdn.GDN_EUNSUPPORTED),
+    (dict(io=5), gdn.GDN_EINVAL),
+    (dict(y=p(0)), gdn.GDN_EINVAL),                                # y aliases x
+    (dict(win=p(3)), gdn.GDN_EINVAL),                              # win aliases y
+    (dict(hist=ctypes.c_void_p(A + 2 * MB + 2)), gdn.GDN_EINVAL),  # misaligned
+])
+def test_conv_rejects(lib, kw, code):
+    assert conv_call(lib, **kw) == code
+
+
+def test_conv_empty_batch_is_ok(lib):
+    assert conv_call(lib, B=0) == gdn.GDN_OK
+
+
+def rollback_call(lib, **kw):
+    a = dict(acc=p(0), K=4, S_in=p(1), H=p(2), S_out=p(6), hist=p(8), win=p(9), B=1, Hv=2, dv=32, dk=32, C=192,
+             W=4, io=gdn.GDN_BF16)
+    a.update(kw)
+    return lib.gdn_rollback(a["acc"], a["K"], a["S_in"], a["H"], a["S_out"], a["hist"], a["win"], a["B"], a["Hv"],
+                            a["dv"], a["dk"], a["C"], a["W"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(acc=None), gdn.GDN_EINVAL),
+    (dict(K=0), gdn.GDN_EINVAL),
+    (dict(H=None), gdn.GDN_EINVAL),             # needed for K > 1
+    (dict(S_out=p(1)), gdn.GDN_EINVAL),         # in place is not recoverable
+    (dict(hist=None), gdn.GDN_EINVAL),          # hist without win
+    (dict(W=1), gdn.GDN_EUNSUPPORTED),
+    (dict(S_out=p(2)), gdn.GDN_EINVAL),         # overlaps H
+])
+def test_rollback_rejects(lib, kw, code):
+    assert rollback_call(lib, **kw) == code
+
+
+def test_rollback_k1_without_capture_and_empty_batch(lib):
+    assert rollback_call(lib, B=0) == gdn.GDN_OK
+
+
+def prefill_call(lib, **kw):
+    a = dict(qkv=p(0), beta=p(1), alpha=p(2), dt=p(3), alog=p(4), S_in=p(5), S_out=p(6), o=p(8), B=1, T=100,
+             chunk=64, Hk=2, Hv=2, dk=32, dv=32, ind=gdn.GDN_BF16, od=gdn.GDN_BF16, eps=1e-6)
+    a.update(kw)
+    return lib.gdn_prefill_chunked(a["qkv"], a["beta"], a["alpha"], a["dt"], a["alog"], a["S_in"], a["S_out"],
+                                   a["o"], a["B"], a["T"], a["chunk"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["ind"],
+                                   a["od"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(chunk=48), gdn.GDN_EUNSUPPORTED),
+    (dict(T=0), gdn.GDN_EINVAL),
+    (dict(o=None), gdn.GDN_EINVAL),
+    (dict(alog=None), gdn.GDN_EINVAL),
+    (dict(dk=16, dv=16), gdn.GDN_EUNSUPPORTED),
+])
+def test_prefill_rejects(lib, kw, code):
+    assert prefill_call(lib, **kw) == code
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(gdn, "_lib", None)
+    with pytest.raises(FileNotFoundError):
+        gdn.load(str(tmp_path / "missing.so"))

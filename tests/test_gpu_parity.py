@@ -1,0 +1,388 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars:
+  - conv step: bit-exact against the oracle's same-precision float conv
+    (y, the written-back history and the rollback window);
+  - GDN: for every sequence, head and state (S_out and every H_t)
+    max |S_gpu - S_ref| <= 2e-3 * ||S_ref||_F (fp32 state, bf16 inputs);
+    outputs: |o_gpu - o_ref| <= 2e-3 * ||S_t||_F (|o_t| <= ||S_t||_F when
+    ||q^|| = 1), plus half a bf16 ulp of o when o is bf16;
+  - rollback: bit-exact copies.
+Every test prints the case it runs before touching the device.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_verify_gdn_amd import gdn, synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def say(*a):
+    print("[gpu case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(t):
+    return t.contiguous().cuda()
+
+
+def f64(t):
+    return t.double().cpu().numpy()
+
+
+# ------------------------------------------------------------------ helpers
+def run_verify_gpu(wl, inp, qkv, capture=True, o_dtype=None, raw=True, S_out_inplace=False):
+    B, K, Hv, dv, dk = wl.B, wl.T, wl.Hv, wl.dv, wl.dk
+    io = torch.bfloat16 if wl.bf16 else torch.float32
+    o_dtype = o_dtype or torch.float32
+    d = {k: dev(v) for k, v in inp.items()}
+    d_qkv = dev(qkv)
+    S_out = d["S_in"] if S_out_inplace else torch.empty_like(d["S_in"])
+    H = torch.empty(B, K - 1, Hv, dv, dk, device="cuda") if (capture and K > 1) else None
+    o = torch.empty(B, K, Hv, dv, device="cuda", dtype=o_dtype)
+    dt, alog = (d["dt_bias"], d["A_log"]) if raw else (None, None)
+    gdn.verify(d_qkv, d["beta_raw"], d["alpha"], dt, alog, d["S_in"], S_out, H, o, wl.Hk)
+    torch.cuda.synchronize()
+    return S_out, H, o, d
+
+
+def check_states(gpu, ref, what):
+    gpu = gpu.astype(np.float64)
+    err = np.abs(gpu - ref).max(axis=(-1, -2))
+    fro = np.linalg.norm(ref, axis=(-1, -2))
+    bad = err > TOL * fro
+    assert not np.any(bad), "%s: worst err/fro = %.3g" % (what, float(np.max(err / np.maximum(fro, 1e-30))))
+    return float(np.max(err / np.maximum(fro, 1e-30)))
+
+
+def check_outputs(o_gpu, o_ref, states_ref, bf16_out):
+    # states_ref [B][K][Hv][dv][dk]: the state after each token
+    fro = np.linalg.norm(states_ref, axis=(-1, -2))  # [B][K][Hv]
+    o = o_gpu.astype(np.float64)
+    bound = TOL * fro[..., None] + (np.abs(o_ref) * 2.0 ** -8 if bf16_out else 0.0)
+    err = np.abs(o - o_ref)
+    assert np.all(err <= bound), "o: worst err = %.3g" % float(np.max(err / np.maximum(bound, 1e-30)))
+
+
+def oracle_verify(wl, inp, qkv, raw=True, capture=True):
+    dt, alog = (f64(inp["dt_bias"]), f64(inp["A_log"])) if raw else (None, None)
+    return oracle.gdn_recurrent_f64(f64(qkv), f64(inp["beta_raw"]), f64(inp["alpha"]), dt, alog,
+                                    f64(inp["S_in"]), wl.Hk, capture=capture)
+
+
+def all_states(S_out, H):
+    # [B][K][Hv][dv][dk]: H_0..H_{K-2}, then the final state
+    if H is None or H.shape[1] == 0:
+        return S_out[:, None]
+    return np.concatenate([H, S_out[:, None]], axis=1)
+
+
+# ------------------------------------------------------------------ conv step
+CONV_CASES = [
+    ("tiny", dict()),
+    ("verify16", dict()),
+    ("decode", dict()),
+    ("batched", dict()),
+    ("tiny", dict(T=13, B=3)),
+    ("verify16", dict(T=5, B=2)),
+    ("verify16", dict(T=1, B=2, W=2)),
+    ("verify16", dict(T=2, B=2, W=8)),
+    ("verify16", dict(T=9, B=1, W=3)),
+    ("tiny", dict(Hk=1, Hv=3, dk=32, dv=40, T=7)),    # C = 184: not a multiple of 8 -> ragged tail
+]
+
+
+@pytest.mark.parametrize("name,over", CONV_CASES)
+def test_conv_step_bit_exact(name, over):
+    wl = synth.small(name, **over)
+    say("conv", name, over, "C=%d" % wl.C)
+    inp = synth.make_inputs(wl, seed=1)
+    x, w, hist = dev(inp["x"]), dev(inp["w"]), dev(inp["hist"])
+    y = torch.empty_like(x)
+    win = torch.empty(wl.B, wl.W - 1 + wl.T, wl.C, dtype=x.dtype, device="cuda")
+    gdn.conv_step(x, w, hist, y, win)
+    torch.cuda.synchronize()
+    y_ref, hist_ref, win_ref = oracle.conv_step_f32(inp["x"].float().numpy(), inp["w"].numpy(),
+                                                    inp["hist"].float().numpy(), round_bf16=wl.bf16)
+    yg = y.float().cpu().numpy()
+    assert np.array_equal(yg.view(np.uint32), y_ref.view(np.uint32)), \
+        "y mismatch at %d of %d" % (int(np.sum(yg.view(np.uint32) != y_ref.view(np.uint32))), y_ref.size)
+    assert np.array_equal(hist.float().cpu().numpy().view(np.uint32), hist_ref.view(np.uint32))
+    assert np.array_equal(win.float().cpu().numpy().view(np.uint32), win_ref.view(np.uint32))
+
+
+def test_conv_step_without_window_and_empty_batch():
+    wl = synth.small("verify16", B=2, T=3)
+    say("conv no-window")
+    inp = synth.make_inputs(wl, seed=2)
+    x, w, hist = dev(inp["x"]), dev(inp["w"]), dev(inp["hist"])
+    y = torch.empty_like(x)
+    gdn.conv_step(x, w, hist, y, None)
+    torch.cuda.synchronize()
+    y_ref, hist_ref, _ = oracle.conv_step_f32(inp["x"].float().numpy(), inp["w"].numpy(),
+                                              inp["hist"].float().numpy(), round_bf16=True)
+    assert np.array_equal(y.float().cpu().numpy(), y_ref)
+    assert np.array_equal(hist.float().cpu().numpy(), hist_ref)
+    e = torch.empty(0, 3, wl.C, dtype=torch.bfloat16, device="cuda")
+    gdn.conv_step(e, w, torch.empty(0, 3, wl.C, dtype=torch.bfloat16, device="cuda"), torch.empty_like(e), None)
+
+
+# ------------------------------------------------------------------ verify
+VERIFY_CASES = [
+    ("tiny", dict(), {}),
+    ("verify16", dict(), {}),
+    ("decode", dict(), {}),
+    ("batched", dict(), {}),
+    ("verify16", dict(T=3, Hk=2, Hv=6), {}),
+    ("verify16", dict(T=5, Hk=4, Hv=4, dk=64, dv=64), {}),
+    ("verify16", dict(T=12, Hk=2, Hv=4, dk=32, dv=32), {}),
+    ("verify16", dict(T=20, Hk=2, Hv=6), {}),
+    ("verify16", dict(T=32, Hk=2, Hv=4), {}),
+    ("verify16", dict(T=16, Hk=2, Hv=4, dk=64, dv=128), {}),
+    ("verify16", dict(T=16, Hk=2, Hv=4, dk=128, dv=24), {}),
+    ("verify16", dict(Hk=4, Hv=12), dict(weak=True)),
+    ("verify16", dict(Hk=4, Hv=12), dict(o_bf16=True)),
+    ("verify16", dict(Hk=4, Hv=12), dict(activated=True)),
+    ("tiny", dict(T=16, B=3), dict(weak=True)),
+]
+
+
+@pytest.mark.parametrize("name,over,opt", VERIFY_CASES)
+def test_verify_parity(name, over, opt):
+    wl = synth.small(name, **over)
+    say("verify", name, over, opt)
+    inp = synth.make_inputs(wl, seed=3, weak_decay=opt.get("weak", False))
+    if opt.get("activated"):
+        # already-activated gates: beta in (0,1), g <= 0
+        inp["beta_raw"] = torch.sigmoid(inp["beta_raw"].float()).to(inp["beta_raw"].dtype)
+        inp["alpha"] = (-torch.nn.functional.softplus(inp["alpha"].float())).to(inp["alpha"].dtype)
+    qkv = synth.make_qkv(wl, seed=3)
+    o_dtype = torch.bfloat16 if opt.get("o_bf16") else torch.float32
+    raw = not opt.get("activated")
+    capture = wl.T > 1
+    S_out, H, o, _ = run_verify_gpu(wl, inp, qkv, capture=capture, o_dtype=o_dtype, raw=raw)
+    S_ref, H_ref, o_ref = oracle_verify(wl, inp, qkv, raw=raw, capture=capture)
+    check_states(S_out.cpu().numpy(), S_ref, "S_out")
+    if capture:
+        check_states(H.cpu().numpy(), H_ref, "H")
+    check_outputs(o.float().cpu().numpy(), o_ref, all_states(S_ref, H_ref), o_dtype == torch.bfloat16)
+
+
+def test_verify_zero_gates_leave_state():
+    """beta = 0, g = 0 (activated mode): every H_t and S_out equal S_in."""
+    wl = synth.small("verify16", Hk=2, Hv=4)
+    say("verify zero gates")
+    inp = synth.make_inputs(wl, seed=4)
+    inp["beta_raw"] = torch.zeros_like(inp["beta_raw"])
+    inp["alpha"] = torch.zeros_like(inp["alpha"])
+    qkv = synth.make_qkv(wl, seed=4)
+    S_out, H, o, d = run_verify_gpu(wl, inp, qkv, raw=False)
+    S_in = inp["S_in"].numpy()
+    assert np.array_equal(S_out.cpu().numpy(), S_in)
+    for t in range(wl.T - 1):
+        assert np.array_equal(H[:, t].cpu().numpy(), S_in)
+
+
+def test_verify_in_place_decode():
+    wl = synth.WORKLOADS["decode"]
+    say("verify decode in place")
+    inp = synth.make_inputs(wl, seed=5)
+    qkv = synth.make_qkv(wl, seed=5)
+    S_out, _, o, d = run_verify_gpu(wl, inp, qkv, capture=False, S_out_inplace=True)
+    S_ref, _, o_ref = oracle_verify(wl, inp, qkv, capture=False)
+    assert S_out.data_ptr() == d["S_in"].data_ptr()
+    check_states(S_out.cpu().numpy(), S_ref, "S_out in place")
+    check_outputs(o.cpu().numpy(), o_ref, S_ref[:, None], False)
+
+
+def test_verify_deterministic_and_k_invariant():
+    """Two identical runs agree bit for bit; H_{j-1} of a K=16 window equals the final state of a j-window."""
+    wl = synth.WORKLOADS["verify16"]
+    say("verify determinism / K invariance")
+    inp = synth.make_inputs(wl, seed=6)
+    qkv = synth.make_qkv(wl, seed=6)
+    S1, H1, o1, _ = run_verify_gpu(wl, inp, qkv)
+    S2, H2, o2, _ = run_verify_gpu(wl, inp, qkv)
+    assert torch.equal(S1, S2) and torch.equal(H1, H2) and torch.equal(o1, o2)
+    for j in (1, 3, 8, 15):
+        wj = synth.small("verify16", T=j)
+        inj = dict(inp)
+        inj["beta_raw"], inj["alpha"] = inp["beta_raw"][:, :j].contiguous(), inp["alpha"][:, :j].contiguous()
+        Sj, _, oj, _ = run_verify_gpu(wj, inj, qkv[:, :j].contiguous(), capture=False)
+        ref = H1[:, j - 1]
+        err = (Sj - ref).abs().amax(dim=(-1, -2))
+        fro = torch.linalg.norm(ref, dim=(-1, -2))
+        assert torch.all(err <= 1e-5 * fro + 1e-30), j
+        assert torch.allclose(oj, o1[:, :j], rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------------------------ rollback
+@pytest.mark.parametrize("name", ["verify16", "batched", "tiny"])
+def test_rollback_bit_exact(name):
+    wl = synth.WORKLOADS[name]
+    say("rollback", name)
+    inp = synth.make_inputs(wl, seed=7)
+    B, K = wl.B, wl.T
+    acc = inp["accept"].clone()
+    if B >= 3:
+        acc[0], acc[1], acc[2] = 0, K, K - 1
+    qkv_x, w, hist0 = dev(inp["x"]), dev(inp["w"]), dev(inp["hist"])
+    hist = hist0.clone()
+    y = torch.empty_like(qkv_x)
+    win = torch.empty(B, wl.W - 1 + K, wl.C, dtype=qkv_x.dtype, device="cuda")
+    gdn.conv_step(qkv_x, w, hist, y, win)
+    S_out, H, o, d = run_verify_gpu(wl, inp, y.cpu(), capture=True)
+    S_before = S_out.clone()
+    hist_before = hist.clone()
+    gdn.rollback(dev(acc), K, d["S_in"], H, S_out, hist, win)
+    torch.cuda.synchronize()
+    # the oracle's byte-copy rollback applied to the GPU's own buffers
+    S_ref = S_before.cpu().numpy().copy()
+    hist_ref = hist_before.cpu().view(torch.int16).numpy().copy() if wl.bf16 else hist_before.cpu().numpy().copy()
+    win_np = win.cpu().view(torch.int16).numpy() if wl.bf16 else win.cpu().numpy()
+    oracle.rollback(acc.numpy(), K, d["S_in"].cpu().numpy(), H.cpu().numpy(), S_ref, win=win_np, hist=hist_ref)
+    assert np.array_equal(S_out.cpu().numpy(), S_ref)
+    hg = hist.cpu().view(torch.int16).numpy() if wl.bf16 else hist.cpu().numpy()
+    assert np.array_equal(hg, hist_ref)
+
+
+def test_rollback_equals_rerun_of_accepted_prefix():
+    """State after rollback(a) matches a fresh verify of the first a tokens (oracle and GPU)."""
+    wl = synth.WORKLOADS["verify16"]
+    say("rollback == rerun")
+    inp = synth.make_inputs(wl, seed=8)
+    qkv = synth.make_qkv(wl, seed=8)
+    S_out, H, _, d = run_verify_gpu(wl, inp, qkv)
+    for a in (0, 1, 7, 15, 16):
+        S = S_out.clone()
+        gdn.rollback(torch.tensor([a], dtype=torch.int32, device="cuda"), wl.T, d["S_in"], H, S)
+        torch.cuda.synchronize()
+        if a == 0:
+            ref = inp["S_in"].double().numpy()
+        else:
+            ref, _, _ = oracle.gdn_recurrent_f64(f64(qkv[:, :a]), f64(inp["beta_raw"][:, :a]),
+                                                 f64(inp["alpha"][:, :a]), f64(inp["dt_bias"]),
+                                                 f64(inp["A_log"]), f64(inp["S_in"]), wl.Hk, capture=False)
+        check_states(S.cpu().numpy(), ref, "rollback a=%d" % a)
+
+
+# ------------------------------------------------------------------ prefill
+PREFILL_CASES = [
+    ("tiny", dict(T=100), 64),
+    ("tiny", dict(T=37, B=2), 16),
+    ("tiny", dict(T=70, B=2, dk=64, dv=64), 32),
+    ("prefill", dict(B=1, T=130, Hk=2, Hv=6), 64),
+    ("prefill", dict(B=2, T=200, Hk=1, Hv=3, dk=64, dv=64), 64),
+]
+
+
+def oracle_segments(qkv, br, al, dt, alog, S_in, Hk, seg=64):
+    """The oracle over a long window in segments of `seg` tokens (state chained).
+
+    Returns the final state, every o_t and the Frobenius norm of the state after
+    every token, [B][T][Hv]."""
+    T = qkv.shape[1]
+    S = S_in
+    os_, norms = [], []
+    for t0 in range(0, T, seg):
+        t1 = min(T, t0 + seg)
+        S_new, H, o = oracle.gdn_recurrent_f64(qkv[:, t0:t1], br[:, t0:t1], al[:, t0:t1], dt, alog, S, Hk)
+        norms.append(np.linalg.norm(all_states(S_new, H), axis=(-1, -2)))
+        os_.append(o)
+        S = S_new
+    return S, np.concatenate(os_, axis=1), np.concatenate(norms, axis=1)
+
+
+@pytest.mark.parametrize("name,over,chunk", PREFILL_CASES)
+def test_prefill_parity(name, over, chunk):
+    wl = synth.small(name, **over)
+    say("prefill", name, over, chunk)
+    inp = synth.make_inputs(wl, seed=9)
+    qkv = synth.make_qkv(wl, seed=9)
+    d = {k: dev(v) for k, v in inp.items()}
+    S_out = torch.empty_like(d["S_in"])
+    o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda")
+    gdn.prefill_chunked(dev(qkv), d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, o,
+                        wl.Hk, chunk=chunk)
+    torch.cuda.synchronize()
+    S_ref, o_ref, norms = oracle_segments(f64(qkv), f64(inp["beta_raw"]), f64(inp["alpha"]), f64(inp["dt_bias"]),
+                                          f64(inp["A_log"]), f64(inp["S_in"]), wl.Hk)
+    check_states(S_out.cpu().numpy(), S_ref, "prefill S_out")
+    err = np.abs(o.cpu().numpy() - o_ref)
+    assert np.all(err <= TOL * norms[..., None])
+
+
+def test_prefill_full_size_sampled_heads():
+    """B=4 x T=4096, 48 value heads, d=128: six (sequence, head) pairs re-run on the oracle."""
+    wl = synth.WORKLOADS["prefill"]
+    say("prefill full size, sampled heads")
+    inp = synth.make_inputs(wl, seed=10)
+    qkv = synth.make_qkv(wl, seed=10)
+    d = {k: dev(v) for k, v in inp.items()}
+    S_out = torch.empty_like(d["S_in"])
+    o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda", dtype=torch.bfloat16)
+    gdn.prefill_chunked(dev(qkv), d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, o,
+                        wl.Hk, chunk=64)
+    torch.cuda.synchronize()
+    S_out = S_out.cpu().numpy()
+    o = o.float().cpu().numpy()
+    grp = wl.Hv // wl.Hk
+    for b, h in [(0, 0), (0, 47), (1, 17), (2, 30), (3, 5), (3, 46)]:
+        hk = h // grp
+        q = qkv[b:b + 1, :, hk * wl.dk:(hk + 1) * wl.dk]
+        k = qkv[b:b + 1, :, wl.Hk * wl.dk + hk * wl.dk: wl.Hk * wl.dk + (hk + 1) * wl.dk]
+        v = qkv[b:b + 1, :, 2 * wl.Hk * wl.dk + h * wl.dv: 2 * wl.Hk * wl.dk + (h + 1) * wl.dv]
+        sub = torch.cat([q, k, v], dim=-1)
+        S_ref, o_ref, norms = oracle_segments(
+            f64(sub), f64(inp["beta_raw"][b:b + 1, :, h:h + 1]), f64(inp["alpha"][b:b + 1, :, h:h + 1]),
+            f64(inp["dt_bias"][h:h + 1]), f64(inp["A_log"][h:h + 1]), f64(inp["S_in"][b:b + 1, h:h + 1]), 1)
+        check_states(S_out[b:b + 1, h:h + 1], S_ref, "prefill b=%d h=%d" % (b, h))
+        err = np.abs(o[b, :, h] - o_ref[0, :, 0])
+        assert np.all(err <= TOL * norms[0, :, 0][:, None] + np.abs(o_ref[0, :, 0]) * 2.0 ** -8)
+
+
+# ------------------------------------------------------------------ the whole step
+def test_full_step_verify16_end_to_end():
+    """conv -> verify -> rollback on the K=16 workload against the oracle's chain."""
+    wl = synth.WORKLOADS["verify16"]
+    say("end-to-end verify16")
+    inp = synth.make_inputs(wl, seed=0)
+    d = {k: dev(v) for k, v in inp.items()}
+    hist = d["hist"].clone()
+    y = torch.empty_like(d["x"])
+    win = torch.empty(wl.B, wl.W - 1 + wl.T, wl.C, dtype=torch.bfloat16, device="cuda")
+    S_out = torch.empty_like(d["S_in"])
+    H = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device="cuda")
+    o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda")
+    gdn.conv_step(d["x"], d["w"], hist, y, win)
+    gdn.verify(y, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, H, o, wl.Hk)
+    gdn.rollback(d["accept"], wl.T, d["S_in"], H, S_out, hist, win)
+    torch.cuda.synchronize()
+    a = int(inp["accept"][0])
+    say("accept length", a)
+    y_ref, hist_full, win_ref = oracle.conv_step_f32(inp["x"].float().numpy(), inp["w"].numpy(),
+                                                     inp["hist"].float().numpy(), round_bf16=True)
+    assert np.array_equal(y.float().cpu().numpy(), y_ref)
+    S_ref, H_ref, o_ref = oracle.gdn_recurrent_f64(y_ref.astype(np.float64), f64(inp["beta_raw"]),
+                                                   f64(inp["alpha"]), f64(inp["dt_bias"]), f64(inp["A_log"]),
+                                                   f64(inp["S_in"]), wl.Hk)
+    check_outputs(o.cpu().numpy(), o_ref, all_states(S_ref, H_ref), False)
+    states = np.concatenate([f64(inp["S_in"])[:, None], all_states(S_ref, H_ref)], axis=1)
+    check_states(S_out.cpu().numpy(), states[:, a], "state after rollback to %d" % a)
+    assert np.array_equal(hist.float().cpu().numpy(), win_ref[:, a:a + wl.W - 1])
