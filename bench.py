@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""GDN verify tokens/s per layer (K=16) and achieved HBM bandwidth on one MI355X.
+
+One step is one pass of the whole hot path of one GDN layer over one verify
+window: gdn_conv_step (fused causal conv1d + SiLU, history write-back, window
+capture) -> gdn_verify (gated delta rule over K=16 tokens, WY form, every
+intermediate state written) -> gdn_rollback (restore conv and GDN state to a
+drawn accept length).  Workload: B=1, Hk=16 key heads, Hv=48 value heads,
+d=128, conv width 4 over C=10240 channels, bf16 inputs, fp32 state; seeded
+synthetic inputs (speculative_verify_gdn_amd.synth), accept length ~ U{0..16}.
+
+Inputs are resident in HBM before timing starts.  The step cycles over R
+independent buffer sets whose total size is at least twice the 256 MB
+Infinity Cache, so the state traffic really goes to HBM.  Each buffer set's
+step is captured once in a HIP graph and the timed region replays exactly
+K steps.
+
+Printed: one JSON line with the metric, the roofline of the dominant kernel
+(gdn_verify: algorithmic bytes per launch / its average duration, timed with
+HIP events on the launch stream around graph-replayed back-to-back launches of
+that kernel alone), and the CPU oracle timed on the host as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GDN verify tokens/s per layer (K=16) + achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def verify_bytes(wl, o_bytes=4) -> int:
+    """Algorithmic bytes of one gdn_verify launch: every input read once,
+    every output written once.
+
+    per sequence: qkv slab K*C*ie + gates 2*K*Hv*ie + S_in Hv*dv*dk*4
+                  + H (K-1)*Hv*dv*dk*4 + S_out Hv*dv*dk*4 + o K*Hv*dv*ob
+    plus dt_bias and A_log (2*Hv*4) once.
+    """
+    ie = 2 if wl.bf16 else 4
+    st = wl.Hv * wl.dv * wl.dk * 4
+    per_b = wl.T * wl.C * ie + 2 * wl.T * wl.Hv * ie + st + (wl.T - 1) * st + st + wl.T * wl.Hv * wl.dv * o_bytes
+    return wl.B * per_b + 2 * wl.Hv * 4
+
+
+def conv_bytes(wl) -> int:
+    """x read, hist read + written, y written, window written, taps read."""
+    ie = 2 if wl.bf16 else 4
+    return wl.B * (wl.T * wl.C * ie * 2 + (wl.W - 1) * wl.C * ie * 2 + (wl.W - 1 + wl.T) * wl.C * ie) \
+        + wl.C * wl.W * 4
+
+
+def rollback_bytes(wl, accept) -> int:
+    """State copy (read + write) and conv-history copy for every sequence that rolls back."""
+    ie = 2 if wl.bf16 else 4
+    st = wl.Hv * wl.dv * wl.dk * 4
+    n = sum(1 for a in accept if a < wl.T)
+    return n * (2 * st + 2 * (wl.W - 1) * wl.C * ie) + 4 * wl.B
+
+
+def source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "speculative_verify_gdn_amd", "csrc", n), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "%s.%s.pmc.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle (single-threaded C: float conv, double GDN, rollback) on the
+    same workload, full steps until the time budget is spent."""
+    import numpy as np
+
+    import oracle
+    from speculative_verify_gdn_amd import synth
+
+    inp = synth.make_inputs(wl, seed=0)
+    x = inp["x"].float().numpy()
+    w = inp["w"].numpy()
+    hist = inp["hist"].float().numpy()
+    f = lambda k: inp[k].double().numpy()
+    br, al, dt, alog, S_in = f("beta_raw"), f("alpha"), f("dt_bias"), f("A_log"), f("S_in")
+    acc = inp["accept"].numpy()
+    o = oracle.default()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        y, hist_out, win = o.conv_step_f32(x, w, hist, round_bf16=wl.bf16)
+        S_out, H, _ = o.gdn_recurrent_f64(y.astype(np.float64), br, al, dt, alog, S_in, wl.Hk)
+        o.rollback(acc, wl.T, S_in, H, S_out, win=win, hist=hist_out)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": steps * wl.B * wl.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full steps of the %s workload (float conv + double GDN with capture + rollback), "
+                      "one thread, %.1f s" % (steps, wl.name, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="verify16")
+    ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled (0: enough to exceed 2x the MALL)")
+    ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of HIP graphs")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the verify step shards "
+              "by key-head group or by sequence with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from speculative_verify_gdn_amd import gdn, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    assert wl.chunk == 0, "the bench step is the verify path"
+    gdn.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    # ---------------------------------------------------------------- buffers
+    def make_set(seed):
+        inp = synth.make_inputs(wl, seed=seed)
+        d = {k: v.to(dev) for k, v in inp.items()}
+        d["y"] = torch.empty_like(d["x"])
+        d["win"] = torch.empty(wl.B, wl.W - 1 + wl.T, wl.C, dtype=d["x"].dtype, device=dev)
+        d["S_out"] = torch.empty_like(d["S_in"])
+        d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev) if wl.T > 1 else None
+        d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+        return d
+
+    probe = make_set(0)
+    set_bytes = sum(t.numel() * t.element_size() for t in probe.values() if t is not None)
+    R = args.sets or max(2, math.ceil(2 * MALL_BYTES / set_bytes))
+    sets = [probe] + [make_set(r) for r in range(1, R)]
+    accepts = [int(s["accept"][0]) for s in sets]
+
+    def conv(d):
+        gdn.conv_step(d["x"], d["w"], d["hist"], d["y"], d["win"])
+
+    def verify(d):
+        gdn.verify(d["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"], d["H"],
+                   d["o"], wl.Hk)
+
+    def rollback(d):
+        gdn.rollback(d["accept"], wl.T, d["S_in"], d["H"], d["S_out"], d["hist"], d["win"])
+
+    def step(d):
+        conv(d)
+        verify(d)
+        rollback(d)
+
+    # ---------------------------------------------------------------- warmup
+    for s in range(args.warmup):
+        step(sets[s % R])
+    torch.cuda.synchronize()
+
+    graphs = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for d in sets:
+                step(d)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for d in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(d)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed steps
+    K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record()
+    if graphs is not None:
+        for s in range(K):
+            graphs[s % R].replay()
+    else:
+        for s in range(K):
+            step(sets[s % R])
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / K
+    tokens = wl.B * wl.T
+    value = tokens / (ms_per_step * 1e-3)
+
+    # ---------------------------------------------------------------- per-kernel durations
+    # each kernel alone, back to back over the R buffer sets: one HIP graph of
+    # R launches per kernel, replayed; HIP events on the launch stream bracket
+    # the replays, so the figure is the kernel's duration plus the GPU's own
+    # gap between consecutive kernels (no host launch cost)
+    def kernel_us(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for d in sets:
+                fn(d)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, min(K, 400) // R)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * R)
+
+    if args.eager:
+        def kernel_us(fn):  # noqa: F811  (events around each eager launch)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(min(K, 200))]
+            torch.cuda.synchronize()
+            for s, (e0, e1) in enumerate(evs):
+                e0.record()
+                fn(sets[s % R])
+                e1.record()
+            torch.cuda.synchronize()
+            return sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) * 1e3
+
+    t_ver = kernel_us(verify)
+    t_conv = kernel_us(conv)
+    t_rb = kernel_us(rollback)
+
+    vb = verify_bytes(wl)
+    achieved = vb / (t_ver * 1e-6) / 1e9
+    sha = source_sha("gdn_verify.hip", "gdn_device.h")
+    traffic = read_traffic("gdn_verify", wl.name, sha)
+    mean_rb_bytes = sum(rollback_bytes(wl, [a]) for a in accepts) / len(accepts)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "B": wl.B, "K": wl.T, "Hk": wl.Hk, "Hv": wl.Hv, "dk": wl.dk, "dv": wl.dv,
+            "C": wl.C, "conv_width": wl.W, "io_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
+            "step": "conv_step + verify(capture) + rollback", "buffer_sets": R,
+            "working_set_MB": round(R * set_bytes / 2 ** 20, 1), "launch": "eager" if args.eager else "hip_graph",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "detail": {
+            "kernel": "gdn_verify",
+            "verify_bytes_per_launch": vb,
+            "verify_us": round(t_ver, 3),
+            "conv_us": round(t_conv, 3),
+            "rollback_us": round(t_rb, 3),
+            "conv_GBs": round(conv_bytes(wl) / (t_conv * 1e-6) / 1e9, 1),
+            "rollback_GBs": round(mean_rb_bytes / (t_rb * 1e-6) / 1e9, 1),
+            "verify_only_tokens_per_s": round(tokens / (t_ver * 1e-6), 1),
+            "wall_ms_timed": round(wall_ms, 3),
+            "source_sha": sha,
+            "accept_lengths": accepts,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

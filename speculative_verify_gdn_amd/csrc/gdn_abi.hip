@@ -108,7 +108,7 @@ int gdn_conv_step(const void* x, const float* w, void* hist, void* y, void* win_
     REQUIRE(!overlap(swin, sx) && !overlap(swin, sw) && !overlap(swin, sh) && !overlap(swin, sy), GDN_EINVAL,
             "%s: win_out overlaps another buffer", fn);
     REQUIRE(!overlap(sh, sx) && !overlap(sh, sw), GDN_EINVAL, "%s: hist overlaps x or w", fn);
-    REQUIRE(T <= 65535 * 8, GDN_EUNSUPPORTED, "%s: T = %d too large", fn, T);
+    REQUIRE(T <= 65535 * 16, GDN_EUNSUPPORTED, "%s: T = %d too large", fn, T);
     REQUIRE(B <= 65535, GDN_EUNSUPPORTED, "%s: B = %d too large", fn, B);
     gdn::ConvArgs a{x, w, hist, y, win_out, B, T, C, W};
     return launch_status(gdn::launch_conv_step(a, io_dtype == GDN_BF16, (hipStream_t)stream), fn);

@@ -15,13 +15,12 @@
 // This file is compiled with -ffp-contract=off, IEEE fp32 division and fp32
 // denormals kept.
 //
-// Thread mapping: a thread owns 8 consecutive channels of one sequence and a
-// segment of kSeg consecutive tokens; consecutive threads own consecutive
-// channels, so every row access is one coalesced 16-byte (bf16) or 32-byte
-// (f32) access per thread.  Segments after the first start at token
-// kSeg >= W-1 and therefore never read the history; the first segment reads
-// the old history and is also the only writer of the new one, so the in-place
-// update has no race.
+// Thread mapping: a thread computes one token of 4 consecutive channels; a
+// workgroup is 16 tokens x 16 channel groups (64 channels), so a row access
+// is 16 threads x 8 bytes (bf16) contiguous.  Only tokens
+// t < W-1 read the old history, and they all sit in the first token tile; the
+// threads of that tile that rewrite the history load their new rows first,
+// wait at a workgroup barrier for every read of the old history, then store.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -41,11 +40,12 @@ __device__ __forceinline__ float conv_exp(float x)
     constexpr float kLog2e = 0x1.715476p+0f;
     constexpr float kLn2Hi = 0x1.62e4p-1f;
     constexpr float kLn2Lo = 0x1.7f7d1cp-20f;
-    if (x != x) return x;
-    if (x >= 89.0f) return __builtin_inff();
-    if (x <= -104.0f) return 0.0f;
-    const float n = __builtin_rintf(x * kLog2e);
-    float r = __builtin_fmaf(-n, kLn2Hi, x);
+    // the special ranges are selected at the end instead of branching; inside
+    // (-104, 89) the clamp leaves x unchanged (a NaN clamps to -104 and is
+    // replaced by itself below)
+    const float xc = fminf(fmaxf(x, -104.0f), 89.0f);
+    const float n = __builtin_rintf(xc * kLog2e);
+    float r = __builtin_fmaf(-n, kLn2Hi, xc);
     r = __builtin_fmaf(-n, kLn2Lo, r);
     float p = 1.0f / 5040.0f;
     p = __builtin_fmaf(p, r, 1.0f / 720.0f);
@@ -60,7 +60,10 @@ __device__ __forceinline__ float conv_exp(float x)
     const int n2 = ni - n1;
     const float s1 = __uint_as_float((uint32_t)(n1 + 127) << 23);
     const float s2 = __uint_as_float((uint32_t)(n2 + 127) << 23);
-    return (p * s1) * s2;
+    float y = (p * s1) * s2;
+    y = x >= 89.0f ? __builtin_inff() : y;
+    y = x <= -104.0f ? 0.0f : y;
+    return x != x ? x : y;
 }
 
 __device__ __forceinline__ float conv_silu(float pre)
@@ -70,27 +73,26 @@ __device__ __forceinline__ float conv_silu(float pre)
     return pre / den;
 }
 
-constexpr int kCh = 8;    // channels per thread
-constexpr int kSeg = 8;   // tokens per thread; must be >= W-1
-constexpr int kThreads = 256;
+constexpr int kCh = 4;          // channels per thread
+constexpr int kTok = 16;        // tokens per workgroup; >= W-1
+constexpr int kGroups = 16;     // 4-channel groups per workgroup
+constexpr int kThreads = kTok * kGroups;
 
 template <bool BF16>
 __device__ __forceinline__ void load_row8(const void* base, size_t off, int nch, bool vec, float v[kCh])
 {
     if (vec) {
         if constexpr (BF16) {
-            const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + off);
+            const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
             v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-            v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
         } else {
             const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
-            const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off + 4);
             v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
         }
     } else {
+        // ragged channel tail: elements past the row end re-read its last element (unused)
 #pragma unroll
-        for (int e = 0; e < kCh; ++e) v[e] = e < nch ? load1<BF16>(base, off + e) : 0.0f;
+        for (int e = 0; e < kCh; ++e) v[e] = load1<BF16>(base, off + (e < nch ? e : nch - 1));
     }
 }
 
@@ -99,16 +101,12 @@ __device__ __forceinline__ void store_row8(void* base, size_t off, int nch, bool
 {
     if (vec) {
         if constexpr (BF16) {
-            uint4 u;
+            uint2 u;
             u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
             u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-            u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-            u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + off) = u;
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = u;
         } else {
-            float* p = reinterpret_cast<float*>(base) + off;
-            *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-            *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
         }
     } else {
 #pragma unroll
@@ -120,89 +118,87 @@ __device__ __forceinline__ void store_row8(void* base, size_t off, int nch, bool
 template <bool BF16, int W>
 __global__ __launch_bounds__(kThreads) void conv_step_kernel(ConvArgs a)
 {
-    constexpr int R = kSeg + W - 1;  // window rows a thread touches
-    const int c0 = (blockIdx.x * kThreads + threadIdx.x) * kCh;
-    if (c0 >= a.C) return;
+    const int g = threadIdx.x % kGroups, tl = threadIdx.x / kGroups;
+    const int c0 = (blockIdx.x * kGroups + g) * kCh;
+    const int t = blockIdx.y * kTok + tl;
     const int b = blockIdx.z;
-    const int t0 = blockIdx.y * kSeg;
     const int T = a.T, C = a.C;
-    const int tn = min(kSeg, T - t0);
-    const int nch = min(kCh, C - c0);
-    const bool vec = (nch == kCh) && ((C & 7) == 0);
+    const bool active = c0 < C && t < T;
+    const int nch = c0 < C ? min(kCh, C - c0) : 0;
+    const bool vec = (nch == kCh) && ((C & 3) == 0);
     const size_t xb = (size_t)b * T * C;
     const size_t hb = (size_t)b * (W - 1) * C;
 
-    // window row r (absolute) is history row r for r < W-1, else token r-(W-1)
-    float col[R][kCh];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int row = t0 + r;
-        if (r < tn + W - 1) {
-            if (row < W - 1) load_row8<BF16>(a.hist, hb + (size_t)row * C + c0, nch, vec, col[r]);
-            else load_row8<BF16>(a.x, xb + (size_t)(row - (W - 1)) * C + c0, nch, vec, col[r]);
-        }
-    }
+    // window row r (absolute) is history row r for r < W-1, else token r-(W-1);
+    // token t reads window rows t .. t+W-1
+    float col[W][kCh];
     float wt[kCh][W];
+    if (active) {
 #pragma unroll
-    for (int e = 0; e < kCh; ++e)
+        for (int jj = 0; jj < W; ++jj) {
+            const int row = t + jj;
+            if (row < W - 1) load_row8<BF16>(a.hist, hb + (size_t)row * C + c0, nch, vec, col[jj]);
+            else load_row8<BF16>(a.x, xb + (size_t)(row - (W - 1)) * C + c0, nch, vec, col[jj]);
+        }
+        // taps of the 4 channels: 4*W consecutive floats (16-byte aligned);
+        // channels past C read channel C-1 (unused)
+        if (vec) {
+            const float4* wp = reinterpret_cast<const float4*>(a.w + (size_t)c0 * W);
+            float wl[kCh * W];
 #pragma unroll
-        for (int j = 0; j < W; ++j) wt[e][j] = e < nch ? a.w[(size_t)(c0 + e) * W + j] : 0.0f;
-
+            for (int q4 = 0; q4 < kCh * W / 4; ++q4) {
+                const float4 f = wp[q4];
+                wl[4 * q4 + 0] = f.x; wl[4 * q4 + 1] = f.y; wl[4 * q4 + 2] = f.z; wl[4 * q4 + 3] = f.w;
+            }
 #pragma unroll
-    for (int t = 0; t < kSeg; ++t) {
-        if (t < tn) {
-            float out[kCh];
+            for (int e = 0; e < kCh; ++e)
+#pragma unroll
+                for (int jj = 0; jj < W; ++jj) wt[e][jj] = wl[e * W + jj];
+        } else {
 #pragma unroll
             for (int e = 0; e < kCh; ++e) {
-                float acc = 0.0f;
+                const int ce = c0 + e < C ? c0 + e : C - 1;
 #pragma unroll
-                for (int j = 0; j < W; ++j) acc = __builtin_fmaf(wt[e][j], col[t + j][e], acc);
-                out[e] = conv_silu(acc);
+                for (int jj = 0; jj < W; ++jj) wt[e][jj] = a.w[(size_t)ce * W + jj];
             }
-            store_row8<BF16>(a.y, xb + (size_t)(t0 + t) * C + c0, nch, vec, out);
         }
+    }
+    // first token tile, threads tl < W-1: history row tl of the window (old)
+    // and of the new history (window row T + tl)
+    float nh[kCh], oh[kCh];
+    const bool hist_writer = blockIdx.y == 0 && tl < W - 1 && c0 < C;
+    if (hist_writer) {
+        load_row8<BF16>(a.hist, hb + (size_t)tl * C + c0, nch, vec, oh);
+        const int row = T + tl;
+        if (row < W - 1) load_row8<BF16>(a.hist, hb + (size_t)row * C + c0, nch, vec, nh);
+        else load_row8<BF16>(a.x, xb + (size_t)(row - (W - 1)) * C + c0, nch, vec, nh);
+        if (a.win) store_row8<BF16>(a.win, (size_t)b * (W - 1 + T) * C + (size_t)tl * C + c0, nch, vec, oh);
     }
 
-    if (a.win) {
-        const size_t wb = (size_t)b * (W - 1 + T) * C;
-        // this thread's window rows t0 + W-1 .. t0 + W-1 + tn - 1 (its tokens)
+    if (active) {
+        float out[kCh];
 #pragma unroll
-        for (int t = 0; t < kSeg; ++t)
-            if (t < tn) store_row8<BF16>(a.win, wb + (size_t)(t0 + W - 1 + t) * C + c0, nch, vec, col[t + W - 1]);
-        if (t0 == 0) {
+        for (int e = 0; e < kCh; ++e) {
+            float acc = 0.0f;
 #pragma unroll
-            for (int r = 0; r < W - 1; ++r) store_row8<BF16>(a.win, wb + (size_t)r * C + c0, nch, vec, col[r]);
+            for (int jj = 0; jj < W; ++jj) acc = __builtin_fmaf(wt[e][jj], col[jj][e], acc);
+            out[e] = conv_silu(acc);
+        }
+        store_row8<BF16>(a.y, xb + (size_t)t * C + c0, nch, vec, out);
+        if (a.win) {
+            const size_t wb = (size_t)b * (W - 1 + T) * C;
+            store_row8<BF16>(a.win, wb + (size_t)(t + W - 1) * C + c0, nch, vec, col[W - 1]);
         }
     }
-
-    if (t0 == 0) {
-        // new history = window rows T .. T+W-2; the old history is already in
-        // registers, so overwriting it in place is safe
-#pragma unroll
-        for (int j = 0; j < W - 1; ++j) {
-            const int row = T + j;
-            float v[kCh];
-            if (row < tn + W - 1) {
-#pragma unroll
-                for (int e = 0; e < kCh; ++e) v[e] = col[0][e];
-#pragma unroll
-                for (int r = 1; r < R; ++r)
-                    if (r == row)
-#pragma unroll
-                        for (int e = 0; e < kCh; ++e) v[e] = col[r][e];
-            } else {
-                load_row8<BF16>(a.x, xb + (size_t)(row - (W - 1)) * C + c0, nch, vec, v);
-            }
-            store_row8<BF16>(a.hist, hb + (size_t)j * C + c0, nch, vec, v);
-        }
-    }
+    __syncthreads();  // every read of the old history in this channel tile is done
+    if (hist_writer) store_row8<BF16>(a.hist, hb + (size_t)tl * C + c0, nch, vec, nh);
 }
 
 template <bool BF16>
 hipError_t launch_w(const ConvArgs& a, hipStream_t s)
 {
     const int groups = (a.C + kCh - 1) / kCh;
-    dim3 grid((groups + kThreads - 1) / kThreads, (a.T + kSeg - 1) / kSeg, a.B);
+    dim3 grid((groups + kGroups - 1) / kGroups, (a.T + kTok - 1) / kTok, a.B);
     dim3 block(kThreads);
     switch (a.W) {
     case 2: conv_step_kernel<BF16, 2><<<grid, block, 0, s>>>(a); break;

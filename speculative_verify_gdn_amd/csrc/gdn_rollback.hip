@@ -36,11 +36,12 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int 
                                     : a.H + ((size_t)b * (K - 1) + (acc - 1)) * a.state_elems;
         float* dst = a.S_out + (size_t)b * a.state_elems;
         const long long base = (long long)blockIdx.x * kSlab;
+        // loads clamped into range (branch-free, all in flight together), stores guarded
         f32x4_t v[kVecPerThread];
 #pragma unroll
         for (int j = 0; j < kVecPerThread; ++j) {
             const long long e = base + ((long long)j * kThreads + threadIdx.x) * 4;
-            if (e < a.state_elems) v[j] = load_f4(src + e);
+            v[j] = load_f4(src + (e < a.state_elems ? e : a.state_elems - 4));
         }
 #pragma unroll
         for (int j = 0; j < kVecPerThread; ++j) {

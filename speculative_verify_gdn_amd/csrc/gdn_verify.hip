@@ -9,27 +9,34 @@
 // the DeltaNet block; review excerpt of gated_delta_net.cu).
 //
 // Math, per sequence b and value head h, with G_t = sum_{s<=t} g_s:
-//   A[t][s] = beta_t e^{G_t-G_s} k^_t.k^_s      (s < t)
-//   u       = (I + A)^{-1} beta (v - e^{G} S_in k^)     (one column per state row)
-//   o_t     = e^{G_t} S_in q^_t + sum_{s<=t} e^{G_t-G_s} (q^_t.k^_s) u_s
-//   H_t     = e^{g_t} H_{t-1} + u_t k^_t^T,  H_{-1} = S_in
-// Only exponentials of G_t - G_s with s <= t are formed (no ratio of decays).
+//   A[t][s] = beta_t e^{G_t-G_s} k^_t.k^_s        (s < t)
+//   M[t][s] = e^{G_t-G_s} q^_t.k^_s                (s <= t)
+//   (I + A) u = beta (v - e^{G} S_in k^)            (one column per state row)
+//   o_t = e^{G_t} S_in q^_t + sum_{s<=t} M[t][s] u_s
+//   H_t = e^{g_t} H_{t-1} + u_t k^_t^T,  H_{-1} = S_in
+// (I + A)^{-1} is the WY / UT transform of the window: it turns the K delta
+// corrections into one triangular solve that needs S_in only through the
+// contractions S_in K^T and S_in Q^T.  Only exponentials of G_t - G_s with
+// s <= t are formed (no ratio of decays).
 //
-// Mapping.  Each state row (a value index i) evolves on its own once the
-// per-head prologue (norms, gates, A, M) is known, so a workgroup is one wave
-// that owns 8 rows of one head: 8 lanes per row, each lane holding DK/8
-// columns as DK/32 float4 chunks at columns 32m + 4*sub.  A store instruction
-// then writes 8 rows x 128 contiguous bytes.  The wave:
-//   1. issues the loads of its 8 state rows and their v values;
-//   2. stages the raw q, k of the key head in LDS and computes the gates;
-//   3. forms the Gram matrices K K^T, Q K^T (and the diagonal of Q Q^T) with
-//      MFMA from the raw inputs -- 16x16x32 bf16 for bf16 inputs (products of
-//      bf16 are exact, accumulation fp32), 16x16x4 f32 for f32 inputs -- and
-//      scales them by the inverse norms to get A and M in LDS;
-//   4. per row: K dot products S_in k_t and S_in q_t (VALU, 8-lane DPP sums),
-//      forward substitution for u, the outputs o_t;
-//   5. streams H_t = gamma_t H_{t-1} + u_t k^_t^T, storing every H_t and the
-//      final state -- the bulk of the bytes of the whole step.
+// Mapping.  A workgroup is 4 waves holding RPG = 1024/DK consecutive state
+// rows of one head.  In the streaming phase a lane owns one float4 of one row
+// (a row is DK/4 lanes), so one store instruction of a wave writes whole rows
+// -- 1 KB contiguous at DK=128.
+//   1. the raw q, k of the key head and the workgroup's S_in rows go to LDS,
+//      the gates are computed; each lane also loads its own state float4, its
+//      k columns and its row's v for every token (branch-free, so the loads
+//      are in flight together);
+//   2. the contractions run on MFMA: wave 0 forms K K^T, Q K^T and diag(Q Q^T)
+//      (norms, decay sums, A and M follow in the same wave), waves 1 and 2
+//      form K S^T and Q S^T.  Operands: raw q, k in bf16 (products of bf16
+//      are exact, accumulation is fp32) against the state split into two bf16
+//      halves (hi + lo keeps about 16 bits), 16x16x32 bf16 instructions; for
+//      f32 inputs 16x16x4 f32 instructions on the unsplit values;
+//   3. per row: b_t, the forward substitution for u_t, o_t (one token per
+//      lane of the row), then H_t = gamma_t H_{t-1} + u_t k^_t streamed out
+//      with one 16-byte store per lane per token -- the bulk of the bytes of
+//      the whole step.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -38,21 +45,26 @@
 namespace gdn {
 namespace {
 
-constexpr int kLanes = 64;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
 
-template <int DK, int KMAX, bool IN_BF16>
+template <int DK, int KP, int RPG, bool IN_BF16>
 struct VerifySmem {
     using in_t = typename std::conditional<IN_BF16, uint16_t, float>::type;
-    in_t q[KMAX][DK];        // raw q of the key head, rows >= K zero
-    in_t k[KMAX][DK];        // raw k
-    float A[KMAX][KMAX];     // beta_t e^{G_t-G_s} k^_t.k^_s, s < t
-    float M[KMAX][KMAX];     // e^{G_t-G_s} q^_t.k^_s, s <= t
-    float nq2[KMAX], nk2[KMAX];
-    float rq[KMAX], rk[KMAX];
-    float beta[KMAX], g[KMAX], G[KMAX], eG[KMAX], gam[KMAX];
+    static constexpr int NP = RPG < 16 ? 16 : RPG;   // row tiles padded to 16
+    in_t q[KP][DK];                 // raw q of the key head, rows >= K zero
+    in_t k[KP][DK];                 // raw k
+    float S[NP][DK + 4];            // S_in rows of the workgroup (rows >= RPG zero)
+    float P[RPG][KP + 4];           // raw k_t . S_in[row]
+    float R[RPG][KP + 4];           // raw q_t . S_in[row]
+    float A[KP][KP + 4];            // beta_t e^{G_t-G_s} k^_t.k^_s, s < t
+    float M[KP][KP + 4];            // e^{G_t-G_s} q^_t.k^_s, s <= t
+    float4 tok[KP];                 // per token: beta, e^{G}, 1/|k|, 1/|q|
+    float gam[KP];                  // e^{g}
+    float g[KP];
 };
 
-// gates of token t for value head h
+// gates of one token for value head h
 __device__ __forceinline__ void gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
                                      float& beta, float& g)
 {
@@ -67,10 +79,24 @@ __device__ __forceinline__ void gate(float braw, float al, const float* dt_bias,
     }
 }
 
-// Gram tile D[m][n] = sum_k X[tm*16+m][k] Y[tn*16+n][k] over the DK columns,
-// X, Y raw in LDS.  Lane l feeds row l%16 of both operands with the same
-// k-slice, so the product is the Gram block whatever order the instruction
-// assigns to the k elements within a lane.
+// bf16 halves of 8 floats: hi = top 16 bits, lo = top 16 bits of the remainder
+__device__ __forceinline__ void split8(const float4& x0, const float4& x1, bf16x8_t& hi, bf16x8_t& lo)
+{
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t u = __float_as_uint(xs[e]);
+        const uint32_t uh = u & 0xffff0000u;
+        const float rem = xs[e] - __uint_as_float(uh);
+        hi[e] = (short)(uh >> 16);
+        lo[e] = (short)(__float_as_uint(rem) >> 16);
+    }
+}
+
+// D[m][n] = sum_c X[tm*16+m][c] Y[tn*16+n][c] over the DK columns.
+// X, Y raw q/k rows in LDS.  Lane l feeds row l%16 of both operands with the
+// same k-slice, so the product is the contraction whatever order the
+// instruction assigns to the k elements inside a lane.
 template <int DK, bool IN_BF16, typename in_t>
 __device__ __forceinline__ f32x4_t gram_tile(const in_t (*X)[DK], const in_t (*Y)[DK], int tm, int tn, int lane)
 {
@@ -94,220 +120,244 @@ __device__ __forceinline__ f32x4_t gram_tile(const in_t (*X)[DK], const in_t (*Y
     return acc;
 }
 
-template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT>
-__global__ __launch_bounds__(kLanes) void verify_kernel(VerifyArgs a)
+// D[m][n] = sum_c X[tm*16+m][c] S[tn*16+n][c]: raw q/k rows against fp32 state rows
+template <int DK, int SW, bool IN_BF16, typename in_t>
+__device__ __forceinline__ f32x4_t state_tile(const in_t (*X)[DK], const float (*S)[SW], int tm, int tn, int lane)
 {
-    constexpr int NCH = DK / 32;                 // float4 chunks per lane
-    constexpr int TB = (KMAX + 15) / 16;         // 16-token blocks for the MFMA tiles
-    constexpr int KP = TB * 16;                  // padded token count of the LDS tiles
-    using Smem = VerifySmem<DK, KP, IN_BF16>;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    const int r = lane & 15, ks = lane >> 4;
+    if constexpr (IN_BF16) {
+#pragma unroll
+        for (int kk = 0; kk < DK / 32; ++kk) {
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&X[tm * 16 + r][32 * kk + 8 * ks]);
+            const float* sp = &S[tn * 16 + r][32 * kk + 8 * ks];
+            bf16x8_t hi, lo;
+            split8(*reinterpret_cast<const float4*>(sp), *reinterpret_cast<const float4*>(sp + 4), hi, lo);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, acc, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < DK / 4; ++kk) {
+            const float a = X[tm * 16 + r][4 * kk + ks];
+            const float b = S[tn * 16 + r][4 * kk + ks];
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+        }
+    }
+    return acc;
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ float4 lds4(const void* p)
+{
+    if constexpr (IN_BF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(p);
+        return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+    } else {
+        return *reinterpret_cast<const float4*>(p);
+    }
+}
+
+template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT>
+__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
+{
+    constexpr int LPR = DK / 4;                  // lanes per state row (one float4 each)
+    constexpr int RPW = 64 / LPR;                // rows per wave
+    constexpr int RPG = kWaves * RPW;            // rows per workgroup
+    constexpr int TB = (KMAX + 15) / 16;         // 16-token MFMA blocks
+    constexpr int KP = TB * 16;
+    constexpr int NTL = (RPG + 15) / 16;         // 16-row MFMA blocks
+    using Smem = VerifySmem<DK, KP, RPG, IN_BF16>;
     using in_t = typename Smem::in_t;
     __shared__ Smem sm;
 
-    const int lane = threadIdx.x;
-    const int rloc = lane >> 3, sub = lane & 7;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane % LPR;                    // float4 index inside the row
+    const int c = 4 * j;
+    const int rloc = wave * RPW + lane / LPR;    // row inside the workgroup
     const int h = blockIdx.y, b = blockIdx.z;
-    const int i = blockIdx.x * 8 + rloc;
+    const int i = blockIdx.x * RPG + rloc;
     const int K = a.K, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
+    const bool live = i < dv;
+    const int ic = live ? i : dv - 1;            // clamped row for loads
     const int C = 2 * Hk * DK + Hv * dv;
     const int hk = h / (Hv / Hk);
     const size_t SD = (size_t)dv * DK;
+    const float* Sh = a.S_in + ((size_t)b * Hv + h) * SD;
+    const in_t* X = reinterpret_cast<const in_t*>(a.qkv) + (size_t)b * K * C;   // this sequence's rows
+    const size_t qoff = (size_t)hk * DK, koff = (size_t)(Hk + hk) * DK;
 
-    // ---- 1. state rows and v values (independent of the prologue)
-    const size_t srow = ((size_t)b * Hv + h) * SD + (size_t)i * DK;
-    f32x4_t S[NCH];
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) S[m] = load_f4(a.S_in + srow + 32 * m + 4 * sub);
-    float v[KMAX];
-#pragma unroll
-    for (int t = 0; t < KMAX; ++t)
-        v[t] = t < K ? load1<IN_BF16>(a.qkv, ((size_t)b * K + t) * C + 2 * (size_t)Hk * DK + (size_t)h * dv + i)
-                     : 0.0f;
-
-    // ---- 2. stage raw q, k (16 bytes per lane per step), gates
+    // ---- 1. stage q, k, the state rows; gates; loads for the streaming phase
+    // (addresses clamped into range instead of branching, so the loads issue together)
     {
         constexpr int EPV = IN_BF16 ? 8 : 4;     // elements per 16-byte vector
-        constexpr int VPR = DK / EPV;            // vectors per row
-        for (int idx = lane; idx < KP * VPR; idx += kLanes) {
-            const int t = idx / VPR, c = (idx % VPR) * EPV;
-            uint4 qv = make_uint4(0, 0, 0, 0), kv = make_uint4(0, 0, 0, 0);
-            if (t < K) {
-                const size_t rowoff = ((size_t)b * K + t) * C;
-                const in_t* base = reinterpret_cast<const in_t*>(a.qkv) + rowoff;
-                qv = *reinterpret_cast<const uint4*>(base + (size_t)hk * DK + c);
-                kv = *reinterpret_cast<const uint4*>(base + (size_t)Hk * DK + (size_t)hk * DK + c);
-            }
-            *reinterpret_cast<uint4*>(&sm.q[t][c]) = qv;
-            *reinterpret_cast<uint4*>(&sm.k[t][c]) = kv;
+        constexpr int VPR = DK / EPV;
+        for (int idx = tid; idx < KP * VPR; idx += kThreads) {
+            const int t = idx / VPR, cc = (idx % VPR) * EPV;
+            const in_t* row = X + (size_t)(t < K ? t : K - 1) * C;
+            uint4 qv = *reinterpret_cast<const uint4*>(row + qoff + cc);
+            uint4 kv = *reinterpret_cast<const uint4*>(row + koff + cc);
+            if (t >= K) qv = kv = make_uint4(0, 0, 0, 0);
+            *reinterpret_cast<uint4*>(&sm.q[t][cc]) = qv;
+            *reinterpret_cast<uint4*>(&sm.k[t][cc]) = kv;
         }
-        if (lane < KP) {
-            float be = 0.f, g = 0.f;
-            if (lane < K) {
-                const size_t gi = ((size_t)b * K + lane) * Hv + h;
-                gate(load1<IN_BF16>(a.beta_raw, gi), load1<IN_BF16>(a.alpha, gi), a.dt_bias, a.A_log, h, be, g);
-            }
-            sm.beta[lane] = be;
-            sm.g[lane] = g;
+        if (tid < KP) {
+            const int tc = tid < K ? tid : K - 1;
+            const size_t gi = ((size_t)b * K + tc) * Hv + h;
+            float be, g;
+            gate(load1<IN_BF16>(a.beta_raw, gi), load1<IN_BF16>(a.alpha, gi), a.dt_bias, a.A_log, h, be, g);
+            sm.g[tid] = tid < K ? g : 0.f;
+            sm.tok[tid].x = tid < K ? be : 0.f;
         }
+    }
+    f32x4_t S = load_f4(Sh + (size_t)ic * DK + c);
+    if (!live) S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4_t*>(&sm.S[rloc][c]) = S;
+    if constexpr (RPG < 16) {
+        for (int idx = tid; idx < (16 - RPG) * LPR; idx += kThreads)
+            *reinterpret_cast<f32x4_t*>(&sm.S[RPG + idx / LPR][4 * (idx % LPR)]) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    float v[KMAX];
+    float4 kr[KMAX];
+#pragma unroll
+    for (int t = 0; t < KMAX; ++t) {
+        const in_t* row = X + (size_t)(t < K ? t : K - 1) * C;
+        v[t] = load1<IN_BF16>(row, 2 * (size_t)Hk * DK + (size_t)h * dv + ic);
+        kr[t] = load4<IN_BF16>(row, koff + c);
     }
     __syncthreads();
 
-    // ---- 3. Gram tiles with MFMA; norms from their diagonals; A and M
-    {
-        // running sums of g; G_t for t >= K is never used
-        if (lane < KP) {
-            float G = 0.f;
-            for (int s = 0; s <= lane; ++s) G += sm.g[s];
-            sm.G[lane] = G;
-            sm.eG[lane] = __expf(G);
-            sm.gam[lane] = __expf(sm.g[lane]);
-        }
-        const int n = lane & 15, mq = (lane >> 4) * 4;
+    // ---- 2. contractions on MFMA
+    const int n16 = lane & 15, m0 = (lane >> 4) * 4;   // 16x16 result layout: row m0+e, column n16
+    if (wave == 0) {
+        // K K^T, Q K^T (lower blocks), diag(Q Q^T); then norms, decay sums, A, M
         f32x4_t kk[TB][TB], qk[TB][TB];
 #pragma unroll
-        for (int tm = 0; tm < TB; ++tm) {
+        for (int tm = 0; tm < TB; ++tm)
 #pragma unroll
             for (int tn = 0; tn <= tm; ++tn) {
                 kk[tm][tn] = gram_tile<DK, IN_BF16, in_t>(sm.k, sm.k, tm, tn, lane);
                 qk[tm][tn] = gram_tile<DK, IN_BF16, in_t>(sm.q, sm.k, tm, tn, lane);
             }
-            const f32x4_t qq = gram_tile<DK, IN_BF16, in_t>(sm.q, sm.q, tm, tm, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (mq + e == n) {
-                    sm.nk2[tm * 16 + n] = kk[tm][tm][e];
-                    sm.nq2[tm * 16 + n] = qq[e];
-                }
-            }
-        }
-        __syncthreads();
-        if (lane < KP) {
-            sm.rk[lane] = 1.0f / sqrtf(sm.nk2[lane] + a.eps);
-            sm.rq[lane] = 1.0f / sqrtf(sm.nq2[lane] + a.eps);
-        }
-        __syncthreads();
-        // D layout of a 16x16 MFMA tile: lane l, element e holds row 4*(l/16)+e, column l%16
 #pragma unroll
         for (int tm = 0; tm < TB; ++tm) {
+            const f32x4_t qq = gram_tile<DK, IN_BF16, in_t>(sm.q, sm.q, tm, tm, lane);
 #pragma unroll
-            for (int tn = 0; tn < TB; ++tn) {
+            for (int e = 0; e < 4; ++e)
+                if (m0 + e == n16) {
+                    const int t = tm * 16 + n16;
+                    // padded tokens keep k^ = q^ = 0 (never 0 * 1/sqrt(0))
+                    sm.tok[t].z = t < K ? 1.0f / sqrtf(kk[tm][tm][e] + a.eps) : 0.0f;
+                    sm.tok[t].w = t < K ? 1.0f / sqrtf(qq[e] + a.eps) : 0.0f;
+                }
+        }
+        float G = 0.f;
+        if (lane < KP) {
+            // running sum of g: lane t adds g_0..g_t in order
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = tm * 16 + mq + e, s = tn * 16 + n;
+            for (int s4 = 0; s4 < KP; s4 += 4) {
+                const float4 g4 = *reinterpret_cast<const float4*>(&sm.g[s4]);
+                if (s4 + 0 <= lane) G += g4.x;
+                if (s4 + 1 <= lane) G += g4.y;
+                if (s4 + 2 <= lane) G += g4.z;
+                if (s4 + 3 <= lane) G += g4.w;
+            }
+            sm.tok[lane].y = G;                 // G for now, e^{G} below
+            sm.gam[lane] = __expf(sm.g[lane]);
+        }
+        // LDS accesses of one wave complete in order: wait for this wave's
+        // writes before other lanes read them back
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        float Gs[TB];
+#pragma unroll
+        for (int tn = 0; tn < TB; ++tn) Gs[tn] = sm.tok[tn * 16 + n16].y;
+#pragma unroll
+        for (int tm = 0; tm < TB; ++tm)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = tm * 16 + m0 + e;
+                const float4 tt = sm.tok[t];
+#pragma unroll
+                for (int tn = 0; tn < TB; ++tn) {
+                    const int s2 = tn * 16 + n16;
                     float av = 0.f, mv = 0.f;
-                    if (tn <= tm && t < K && s <= t) {
-                        const float dec = __expf(sm.G[t] - sm.G[s]);
-                        const float rks = sm.rk[s];
-                        mv = dec * qk[tm][tn][e] * sm.rq[t] * rks;
-                        if (s < t) av = sm.beta[t] * dec * kk[tm][tn][e] * sm.rk[t] * rks;
+                    if (tn <= tm && s2 <= t) {
+                        const float dec = __expf(tt.y - Gs[tn]);
+                        const float rks = sm.tok[s2].z;
+                        mv = dec * qk[tm][tn][e] * tt.w * rks;
+                        if (s2 < t) av = tt.x * dec * kk[tm][tn][e] * tt.z * rks;
                     }
-                    sm.A[t][s] = av;
-                    sm.M[t][s] = mv;
+                    sm.A[t][s2] = av;
+                    sm.M[t][s2] = mv;
                 }
             }
-        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        if (lane < KP) sm.tok[lane].y = __expf(G);
+    } else if (wave == 1 || wave == 2) {
+        // raw K S^T (wave 1) or Q S^T (wave 2), stored per state row
+        const in_t(*Xs)[DK] = wave == 1 ? sm.k : sm.q;
+        float(*D)[KP + 4] = wave == 1 ? sm.P : sm.R;
+#pragma unroll
+        for (int tm = 0; tm < TB; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < NTL; ++tn) {
+                const f32x4_t d = state_tile<DK, DK + 4, IN_BF16, in_t>(Xs, sm.S, tm, tn, lane);
+                const int row = tn * 16 + n16;
+                if (row < RPG) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) D[row][tm * 16 + m0 + e] = d[e];
+                }
+            }
     }
     __syncthreads();
 
-    // ---- 4. per row: S_in k_t, S_in q_t, substitution, outputs
-    float p[KMAX], r[KMAX];
+    // ---- 3a. b_t = beta_t (v_t - e^{G_t} S_in k^_t);  u = (I + A)^{-1} b
+    float u[KMAX], r[KMAX];
 #pragma unroll
     for (int t = 0; t < KMAX; ++t) {
-        float pk = 0.f, pq = 0.f;
-        if (t < K) {
+        const float4 tt = sm.tok[t];            // beta, e^{G}, 1/|k|, 1/|q|
+        const float bt = tt.x * (v[t] - tt.y * (sm.P[rloc][t] * tt.z));
+        float acc = bt;
 #pragma unroll
-            for (int m = 0; m < NCH; ++m) {
-                const int c = 32 * m + 4 * sub;
-                float kx[4], qx[4];
-                if constexpr (IN_BF16) {
-                    const uint2 ku = *reinterpret_cast<const uint2*>(&sm.k[t][c]);
-                    const uint2 qu = *reinterpret_cast<const uint2*>(&sm.q[t][c]);
-                    kx[0] = bf16_lo(ku.x); kx[1] = bf16_hi(ku.x); kx[2] = bf16_lo(ku.y); kx[3] = bf16_hi(ku.y);
-                    qx[0] = bf16_lo(qu.x); qx[1] = bf16_hi(qu.x); qx[2] = bf16_lo(qu.y); qx[3] = bf16_hi(qu.y);
-                } else {
-                    const float4 kf = *reinterpret_cast<const float4*>(&sm.k[t][c]);
-                    const float4 qf = *reinterpret_cast<const float4*>(&sm.q[t][c]);
-                    kx[0] = kf.x; kx[1] = kf.y; kx[2] = kf.z; kx[3] = kf.w;
-                    qx[0] = qf.x; qx[1] = qf.y; qx[2] = qf.z; qx[3] = qf.w;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    pk = __builtin_fmaf(S[m][e], kx[e], pk);
-                    pq = __builtin_fmaf(S[m][e], qx[e], pq);
-                }
-            }
-        }
-        p[t] = pk;
-        r[t] = pq;
-    }
-#pragma unroll
-    for (int t = 0; t < KMAX; ++t) {
-        if (t < K) {
-            p[t] = sum8(p[t]) * sm.rk[t];
-            r[t] = sum8(r[t]) * sm.rq[t];
-        }
-    }
-    float u[KMAX];
-#pragma unroll
-    for (int t = 0; t < KMAX; ++t) {
-        float acc = 0.f;
-        if (t < K) {
-            acc = sm.beta[t] * (v[t] - sm.eG[t] * p[t]);
-#pragma unroll
-            for (int s = 0; s < t; ++s) acc = __builtin_fmaf(-sm.A[t][s], u[s], acc);
-        }
+        for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(-sm.A[t][s2], u[s2], acc);
         u[t] = acc;
+        r[t] = sm.R[rloc][t] * tt.w;
     }
-    {
-        float mine[(KMAX + 7) / 8];
+
+    // ---- 3b. o_t = e^{G_t} r_t + sum_{s<=t} M[t][s] u_s, one token per lane of the row
 #pragma unroll
-        for (int j = 0; j < (KMAX + 7) / 8; ++j) mine[j] = 0.f;
+    for (int t0 = 0; t0 < KMAX; t0 += LPR) {
+        const int t = t0 + j;
+        if (t < K && live) {
+            float rt = 0.f;
 #pragma unroll
-        for (int t = 0; t < KMAX; ++t) {
-            if (t < K) {
-                float ot = sm.eG[t] * r[t];
+            for (int tt = t0; tt < t0 + LPR && tt < KMAX; ++tt)
+                if (tt == t) rt = r[tt];
+            float ot = sm.tok[t].y * rt;
 #pragma unroll
-                for (int s = 0; s <= t; ++s) ot = __builtin_fmaf(sm.M[t][s], u[s], ot);
-                if ((t & 7) == sub) mine[t >> 3] = ot;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < (KMAX + 7) / 8; ++j) {
-            const int t = 8 * j + sub;
-            if (t < K) store1<O_BF16>(a.o, (((size_t)b * K + t) * Hv + h) * dv + i, mine[j]);
+            for (int s2 = 0; s2 < KMAX; ++s2) ot = __builtin_fmaf(sm.M[t][s2], u[s2], ot);  // M[t][s] = 0 for s > t
+            store1<O_BF16>(a.o, (((size_t)b * K + t) * Hv + h) * dv + i, ot);
         }
     }
 
-    // ---- 5. stream the states: H_t = gamma_t H_{t-1} + (u_t rk_t) k_t
+    // ---- 3c. stream the states: H_t = gamma_t H_{t-1} + (u_t / |k_t|) k_t
+    float* Hrow = a.H ? a.H + ((size_t)b * (K - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
+    const size_t Hstep = (size_t)Hv * SD;
 #pragma unroll
     for (int t = 0; t < KMAX; ++t) {
-        if (t < K) {
-            const float gm = sm.gam[t];
-            const float cu = u[t] * sm.rk[t];
-            float* dst;
+        const float gm = sm.gam[t];
+        const float cu = u[t] * sm.tok[t].z;
+        S[0] = __builtin_fmaf(cu, kr[t].x, gm * S[0]);
+        S[1] = __builtin_fmaf(cu, kr[t].y, gm * S[1]);
+        S[2] = __builtin_fmaf(cu, kr[t].z, gm * S[2]);
+        S[3] = __builtin_fmaf(cu, kr[t].w, gm * S[3]);
+        if (live) {
             if (t < K - 1) {
-                if (a.H == nullptr) dst = nullptr;
-                else dst = a.H + (((size_t)b * (K - 1) + t) * Hv + h) * SD + (size_t)i * DK;
-            } else {
-                dst = a.S_out + srow;
-            }
-#pragma unroll
-            for (int m = 0; m < NCH; ++m) {
-                const int c = 32 * m + 4 * sub;
-                float kx[4];
-                if constexpr (IN_BF16) {
-                    const uint2 ku = *reinterpret_cast<const uint2*>(&sm.k[t][c]);
-                    kx[0] = bf16_lo(ku.x); kx[1] = bf16_hi(ku.x); kx[2] = bf16_lo(ku.y); kx[3] = bf16_hi(ku.y);
-                } else {
-                    const float4 kf = *reinterpret_cast<const float4*>(&sm.k[t][c]);
-                    kx[0] = kf.x; kx[1] = kf.y; kx[2] = kf.z; kx[3] = kf.w;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) S[m][e] = __builtin_fmaf(cu, kx[e], gm * S[m][e]);
-                if (dst != nullptr) {
-                    if (t < K - 1) store_f4<NT>(dst + c, S[m]);
-                    else store_f4<false>(dst + c, S[m]);
-                }
+                if (Hrow) store_f4<NT>(Hrow + (size_t)t * Hstep, S);
+            } else if (t == K - 1) {
+                store_f4<false>(a.S_out + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S);
             }
         }
     }
@@ -316,8 +366,9 @@ __global__ __launch_bounds__(kLanes) void verify_kernel(VerifyArgs a)
 template <int DK, int KMAX, bool IN_BF16, bool O_BF16>
 hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
 {
-    dim3 grid(a.dv / 8, a.Hv, a.B);
-    verify_kernel<DK, KMAX, IN_BF16, O_BF16, false><<<grid, dim3(kLanes), 0, s>>>(a);
+    constexpr int RPG = 1024 / DK;
+    dim3 grid((a.dv + RPG - 1) / RPG, a.Hv, a.B);
+    verify_kernel<DK, KMAX, IN_BF16, O_BF16, true><<<grid, dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
