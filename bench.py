@@ -138,6 +138,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -150,11 +152,22 @@ def main():
 
     from speculative_verify_gdn_amd import gdn, synth
 
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    if args.copy_probe:
+        # a copy of known size: each launch reads and writes exactly n bytes
+        n = args.copy_probe * 2 ** 20
+        src = torch.ones(n // 4, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return
+
     wl = synth.WORKLOADS[args.workload]
     assert wl.chunk == 0, "the bench step is the verify path"
     gdn.load()
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
 
     # ---------------------------------------------------------------- buffers
     def make_set(seed):
