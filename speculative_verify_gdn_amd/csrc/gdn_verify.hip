@@ -23,19 +23,20 @@
 // rows of one head.  In the streaming phase a lane owns one float4 of one row
 // (a row is DK/4 lanes), so one store instruction of a wave writes whole rows
 // -- 1 KB contiguous at DK=128.
-//   1. the raw q, k of the key head and the workgroup's S_in rows go to LDS,
-//      the gates are computed; each lane also loads its own state float4, its
-//      k columns and its row's v for every token (branch-free, so the loads
-//      are in flight together);
-//   2. the contractions run on MFMA: wave 0 forms K K^T, Q K^T and diag(Q Q^T)
-//      (norms, decay sums, A and M follow in the same wave), waves 1 and 2
-//      form K S^T and Q S^T.  Operands: raw q, k in bf16 (products of bf16
+//   1. the raw q, k of the key head, the workgroup's S_in rows and their v
+//      values go to LDS with a few 16-byte loads per thread (branch-free, so
+//      they are in flight together), the gates are computed; each lane keeps
+//      its own state float4;
+//   2. the contractions run on MFMA, one job per wave: K K^T and then the
+//      norms of k, the decay sums and A (wave 0); Q K^T, diag(Q Q^T) and M
+//      (wave 3); K S^T (wave 1) and Q S^T (wave 2).  Operands: raw q, k in bf16 (products of bf16
 //      are exact, accumulation is fp32) against the state split into two bf16
 //      halves (hi + lo keeps about 16 bits), 16x16x32 bf16 instructions; for
 //      f32 inputs 16x16x4 f32 instructions on the unsplit values;
-//   3. per row: b_t, the forward substitution for u_t, o_t (one token per
-//      lane of the row), then H_t = gamma_t H_{t-1} + u_t k^_t streamed out
-//      with one 16-byte store per lane per token -- the bulk of the bytes of
+//   3. per row: the forward substitution for u_t is shared by the row's lanes
+//      (lane j owns token j, each finished u_t is broadcast with v_readlane),
+//      which also gives o_t; then every lane streams H_t = gamma_t H_{t-1} +
+//      u_t k^_t with one 16-byte store per token -- the bulk of the bytes of
 //      the whole step.
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -52,16 +53,20 @@ template <int DK, int KP, int RPG, bool IN_BF16>
 struct VerifySmem {
     using in_t = typename std::conditional<IN_BF16, uint16_t, float>::type;
     static constexpr int NP = RPG < 16 ? 16 : RPG;   // row tiles padded to 16
-    in_t q[KP][DK];                 // raw q of the key head, rows >= K zero
-    in_t k[KP][DK];                 // raw k
+    static constexpr int QW = DK + (IN_BF16 ? 8 : 4);   // padded row: rows start 4 banks apart
+    in_t q[KP][QW];                 // raw q of the key head, rows >= K zero
+    in_t k[KP][QW];                 // raw k
     float S[NP][DK + 4];            // S_in rows of the workgroup (rows >= RPG zero)
     float P[RPG][KP + 4];           // raw k_t . S_in[row]
     float R[RPG][KP + 4];           // raw q_t . S_in[row]
     float A[KP][KP + 4];            // beta_t e^{G_t-G_s} k^_t.k^_s, s < t
     float M[KP][KP + 4];            // e^{G_t-G_s} q^_t.k^_s, s <= t
+    float V[KP][RPG];               // v of the workgroup's rows, per token
     float4 tok[KP];                 // per token: beta, e^{G}, 1/|k|, 1/|q|
     float gam[KP];                  // e^{g}
     float g[KP];
+    float G[2][KP];                 // running sums of g (one copy per prologue wave)
+    float rk3[KP];                  // 1/|k| as the M wave computes it
 };
 
 // gates of one token for value head h
@@ -69,9 +74,9 @@ __device__ __forceinline__ void gate(float braw, float al, const float* dt_bias,
                                      float& beta, float& g)
 {
     if (dt_bias != nullptr) {
-        beta = 1.0f / (1.0f + __expf(-braw));
+        beta = __frcp_rn(1.0f + __expf(-braw));
         const float a = al + dt_bias[h];
-        const float sp = a > 20.0f ? a : log1pf(__expf(a));
+        const float sp = a > 20.0f ? a : __logf(1.0f + __expf(a));
         g = -sp * __expf(A_log[h]);
     } else {
         beta = braw;
@@ -97,8 +102,8 @@ __device__ __forceinline__ void split8(const float4& x0, const float4& x1, bf16x
 // X, Y raw q/k rows in LDS.  Lane l feeds row l%16 of both operands with the
 // same k-slice, so the product is the contraction whatever order the
 // instruction assigns to the k elements inside a lane.
-template <int DK, bool IN_BF16, typename in_t>
-__device__ __forceinline__ f32x4_t gram_tile(const in_t (*X)[DK], const in_t (*Y)[DK], int tm, int tn, int lane)
+template <int DK, int QW, bool IN_BF16, typename in_t>
+__device__ __forceinline__ f32x4_t gram_tile(const in_t (*X)[QW], const in_t (*Y)[QW], int tm, int tn, int lane)
 {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int r = lane & 15, ks = lane >> 4;
@@ -121,8 +126,8 @@ __device__ __forceinline__ f32x4_t gram_tile(const in_t (*X)[DK], const in_t (*Y
 }
 
 // D[m][n] = sum_c X[tm*16+m][c] S[tn*16+n][c]: raw q/k rows against fp32 state rows
-template <int DK, int SW, bool IN_BF16, typename in_t>
-__device__ __forceinline__ f32x4_t state_tile(const in_t (*X)[DK], const float (*S)[SW], int tm, int tn, int lane)
+template <int DK, int QW, int SW, bool IN_BF16, typename in_t>
+__device__ __forceinline__ f32x4_t state_tile(const in_t (*X)[QW], const float (*S)[SW], int tm, int tn, int lane)
 {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int r = lane & 15, ks = lane >> 4;
@@ -201,13 +206,13 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             *reinterpret_cast<uint4*>(&sm.q[t][cc]) = qv;
             *reinterpret_cast<uint4*>(&sm.k[t][cc]) = kv;
         }
-        if (tid < KP) {
-            const int tc = tid < K ? tid : K - 1;
+        if (wave == kWaves - 1 && lane < KP) {
+            const int tc = lane < K ? lane : K - 1;
             const size_t gi = ((size_t)b * K + tc) * Hv + h;
             float be, g;
             gate(load1<IN_BF16>(a.beta_raw, gi), load1<IN_BF16>(a.alpha, gi), a.dt_bias, a.A_log, h, be, g);
-            sm.g[tid] = tid < K ? g : 0.f;
-            sm.tok[tid].x = tid < K ? be : 0.f;
+            sm.g[lane] = lane < K ? g : 0.f;
+            sm.tok[lane].x = lane < K ? be : 0.f;
         }
     }
     f32x4_t S = load_f4(Sh + (size_t)ic * DK + c);
@@ -217,43 +222,28 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
         for (int idx = tid; idx < (16 - RPG) * LPR; idx += kThreads)
             *reinterpret_cast<f32x4_t*>(&sm.S[RPG + idx / LPR][4 * (idx % LPR)]) = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    float v[KMAX];
-    float4 kr[KMAX];
-#pragma unroll
-    for (int t = 0; t < KMAX; ++t) {
+    // v of the workgroup's RPG rows for every token: one element per thread
+    for (int idx = tid; idx < KMAX * RPG; idx += kThreads) {
+        const int t = idx / RPG, rr = idx % RPG;
+        const int gr = blockIdx.x * RPG + rr;
         const in_t* row = X + (size_t)(t < K ? t : K - 1) * C;
-        v[t] = load1<IN_BF16>(row, 2 * (size_t)Hk * DK + (size_t)h * dv + ic);
-        kr[t] = load4<IN_BF16>(row, koff + c);
+        sm.V[t][rr] = load1<IN_BF16>(row, 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1));
     }
     __syncthreads();
 
     // ---- 2. contractions on MFMA
+    // wave 0: K K^T -> 1/|k|, running decay sums, A
+    // wave 3: Q K^T, diag(Q Q^T), diag(K K^T) -> 1/|q|, M
+    // waves 1, 2: K S^T, Q S^T
     const int n16 = lane & 15, m0 = (lane >> 4) * 4;   // 16x16 result layout: row m0+e, column n16
-    if (wave == 0) {
-        // K K^T, Q K^T (lower blocks), diag(Q Q^T); then norms, decay sums, A, M
-        f32x4_t kk[TB][TB], qk[TB][TB];
-#pragma unroll
-        for (int tm = 0; tm < TB; ++tm)
-#pragma unroll
-            for (int tn = 0; tn <= tm; ++tn) {
-                kk[tm][tn] = gram_tile<DK, IN_BF16, in_t>(sm.k, sm.k, tm, tn, lane);
-                qk[tm][tn] = gram_tile<DK, IN_BF16, in_t>(sm.q, sm.k, tm, tn, lane);
-            }
-#pragma unroll
-        for (int tm = 0; tm < TB; ++tm) {
-            const f32x4_t qq = gram_tile<DK, IN_BF16, in_t>(sm.q, sm.q, tm, tm, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (m0 + e == n16) {
-                    const int t = tm * 16 + n16;
-                    // padded tokens keep k^ = q^ = 0 (never 0 * 1/sqrt(0))
-                    sm.tok[t].z = t < K ? 1.0f / sqrtf(kk[tm][tm][e] + a.eps) : 0.0f;
-                    sm.tok[t].w = t < K ? 1.0f / sqrtf(qq[e] + a.eps) : 0.0f;
-                }
-        }
-        float G = 0.f;
+    if (wave == 0 || wave == 3) {
+        const bool wa = wave == 0;
+        const int wi = wa ? 0 : 1;
+        float* Gw = sm.G[wi];
+        float* rkw = wa ? nullptr : sm.rk3;
         if (lane < KP) {
             // running sum of g: lane t adds g_0..g_t in order
+            float G = 0.f;
 #pragma unroll
             for (int s4 = 0; s4 < KP; s4 += 4) {
                 const float4 g4 = *reinterpret_cast<const float4*>(&sm.g[s4]);
@@ -262,48 +252,76 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
                 if (s4 + 2 <= lane) G += g4.z;
                 if (s4 + 3 <= lane) G += g4.w;
             }
-            sm.tok[lane].y = G;                 // G for now, e^{G} below
-            sm.gam[lane] = __expf(sm.g[lane]);
+            Gw[lane] = G;
+            if (wa) {
+                sm.tok[lane].y = __expf(G);
+                sm.gam[lane] = __expf(sm.g[lane]);
+            }
+        }
+        f32x4_t kk[TB][TB], qk[TB][TB];
+#pragma unroll
+        for (int tm = 0; tm < TB; ++tm)
+#pragma unroll
+            for (int tn = 0; tn <= tm; ++tn) {
+                if (wa || tn == tm) kk[tm][tn] = gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.k, sm.k, tm, tn, lane);
+                if (!wa) qk[tm][tn] = gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.q, sm.k, tm, tn, lane);
+            }
+#pragma unroll
+        for (int tm = 0; tm < TB; ++tm) {
+            f32x4_t qq = {0.f, 0.f, 0.f, 0.f};
+            if (!wa) qq = gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.q, sm.q, tm, tm, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (m0 + e == n16) {
+                    const int t = tm * 16 + n16;
+                    // padded tokens keep k^ = q^ = 0 (never 0 * 1/sqrt(0))
+                    const float rk = t < K ? __builtin_amdgcn_rsqf(kk[tm][tm][e] + a.eps) : 0.0f;
+                    if (wa) {
+                        sm.tok[t].z = rk;
+                    } else {
+                        rkw[t] = rk;
+                        sm.tok[t].w = t < K ? __builtin_amdgcn_rsqf(qq[e] + a.eps) : 0.0f;
+                    }
+                }
         }
         // LDS accesses of one wave complete in order: wait for this wave's
-        // writes before other lanes read them back
+        // writes, then read them back from other lanes
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
-        float Gs[TB];
-#pragma unroll
-        for (int tn = 0; tn < TB; ++tn) Gs[tn] = sm.tok[tn * 16 + n16].y;
+        const float* rkr = wa ? nullptr : rkw;
 #pragma unroll
         for (int tm = 0; tm < TB; ++tm)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = tm * 16 + m0 + e;
+                const float Gt = Gw[t];
                 const float4 tt = sm.tok[t];
+                const float rowf = wa ? tt.x * tt.z : tt.w;        // beta_t / |k_t|  or  1 / |q_t|
 #pragma unroll
                 for (int tn = 0; tn < TB; ++tn) {
                     const int s2 = tn * 16 + n16;
-                    float av = 0.f, mv = 0.f;
+                    float val = 0.f;
                     if (tn <= tm && s2 <= t) {
-                        const float dec = __expf(tt.y - Gs[tn]);
-                        const float rks = sm.tok[s2].z;
-                        mv = dec * qk[tm][tn][e] * tt.w * rks;
-                        if (s2 < t) av = tt.x * dec * kk[tm][tn][e] * tt.z * rks;
+                        const float dec = __expf(Gt - Gw[s2]);
+                        if (wa) {
+                            if (s2 < t) val = dec * kk[tm][tn][e] * rowf * sm.tok[s2].z;
+                        } else {
+                            val = dec * qk[tm][tn][e] * rowf * rkr[s2];
+                        }
                     }
-                    sm.A[t][s2] = av;
-                    sm.M[t][s2] = mv;
+                    if (wa) sm.A[t][s2] = val;
+                    else sm.M[t][s2] = val;
                 }
             }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        if (lane < KP) sm.tok[lane].y = __expf(G);
-    } else if (wave == 1 || wave == 2) {
+    } else {
         // raw K S^T (wave 1) or Q S^T (wave 2), stored per state row
-        const in_t(*Xs)[DK] = wave == 1 ? sm.k : sm.q;
+        const in_t(*Xs)[Smem::QW] = wave == 1 ? sm.k : sm.q;
         float(*D)[KP + 4] = wave == 1 ? sm.P : sm.R;
 #pragma unroll
         for (int tm = 0; tm < TB; ++tm)
 #pragma unroll
             for (int tn = 0; tn < NTL; ++tn) {
-                const f32x4_t d = state_tile<DK, DK + 4, IN_BF16, in_t>(Xs, sm.S, tm, tn, lane);
+                const f32x4_t d = state_tile<DK, Smem::QW, DK + 4, IN_BF16, in_t>(Xs, sm.S, tm, tn, lane);
                 const int row = tn * 16 + n16;
                 if (row < RPG) {
 #pragma unroll
@@ -313,46 +331,89 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     }
     __syncthreads();
 
-    // ---- 3a. b_t = beta_t (v_t - e^{G_t} S_in k^_t);  u = (I + A)^{-1} b
-    float u[KMAX], r[KMAX];
+    // ---- 3a. u = (I + A)^{-1} b with b_t = beta_t (v_t - e^{G_t} S_in k^_t), and o_t.
+    // Lane j of a row owns token j: it forms b_j, keeps row j of A and of M in
+    // registers, and at step t the owner of token t has its u_t final; every
+    // lane reads it with v_readlane (per row of the wave) and updates its own
+    // partial sum.  u_t ends up in scalar registers for the stream.
+    float us[RPW][KMAX];                         // u_t of each row of this wave (wave-uniform)
+    if constexpr (KMAX <= LPR) {
+        const int tj = j < KMAX ? j : KMAX - 1;  // this lane's token (clamped; lanes past K carry zeros)
+        const bool own = j < K;
+        const float4 tt = sm.tok[tj];            // beta, e^{G}, 1/|k|, 1/|q|
+        float part = own ? tt.x * (sm.V[tj][rloc] - tt.y * (sm.P[rloc][tj] * tt.z)) : 0.f;
+        float arow[KMAX], mrow[KMAX];
 #pragma unroll
-    for (int t = 0; t < KMAX; ++t) {
-        const float4 tt = sm.tok[t];            // beta, e^{G}, 1/|k|, 1/|q|
-        const float bt = tt.x * (v[t] - tt.y * (sm.P[rloc][t] * tt.z));
-        float acc = bt;
+        for (int s4 = 0; s4 < KMAX; s4 += 4) {
+            if (s4 + 4 <= KMAX) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&sm.A[tj][s4]);
+                const float4 m4 = *reinterpret_cast<const float4*>(&sm.M[tj][s4]);
+                arow[s4] = a4.x; arow[s4 + 1] = a4.y; arow[s4 + 2] = a4.z; arow[s4 + 3] = a4.w;
+                mrow[s4] = m4.x; mrow[s4 + 1] = m4.y; mrow[s4 + 2] = m4.z; mrow[s4 + 3] = m4.w;
+            } else {
 #pragma unroll
-        for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(-sm.A[t][s2], u[s2], acc);
-        u[t] = acc;
-        r[t] = sm.R[rloc][t] * tt.w;
-    }
-
-    // ---- 3b. o_t = e^{G_t} r_t + sum_{s<=t} M[t][s] u_s, one token per lane of the row
-#pragma unroll
-    for (int t0 = 0; t0 < KMAX; t0 += LPR) {
-        const int t = t0 + j;
-        if (t < K && live) {
-            float rt = 0.f;
-#pragma unroll
-            for (int tt = t0; tt < t0 + LPR && tt < KMAX; ++tt)
-                if (tt == t) rt = r[tt];
-            float ot = sm.tok[t].y * rt;
-#pragma unroll
-            for (int s2 = 0; s2 < KMAX; ++s2) ot = __builtin_fmaf(sm.M[t][s2], u[s2], ot);  // M[t][s] = 0 for s > t
-            store1<O_BF16>(a.o, (((size_t)b * K + t) * Hv + h) * dv + i, ot);
+                for (int e = 0; e < KMAX - s4; ++e) { arow[s4 + e] = sm.A[tj][s4 + e]; mrow[s4 + e] = sm.M[tj][s4 + e]; }
+            }
         }
+        const int wr = lane / LPR;               // row of this lane inside the wave
+        float ot = own ? tt.y * (sm.R[rloc][tj] * tt.w) : 0.f;
+#pragma unroll
+        for (int t = 0; t < KMAX; ++t) {
+            float mine = 0.f;
+#pragma unroll
+            for (int r2 = 0; r2 < RPW; ++r2) {
+                us[r2][t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), r2 * LPR + t));
+                if (r2 == wr) mine = us[r2][t];
+            }
+            // A[j][t] = 0 for t >= j, so finished lanes keep their value
+            part = __builtin_fmaf(-arow[t], mine, part);
+            ot = __builtin_fmaf(mrow[t], mine, ot);  // M[j][t] = 0 for t > j
+        }
+        if (own && live) store1<O_BF16>(a.o, (((size_t)b * K + j) * Hv + h) * dv + i, ot);
+    } else {
+        // more tokens than lanes per row: every lane solves its row's system
+        float u[KMAX];
+#pragma unroll
+        for (int t = 0; t < KMAX; ++t) {
+            const float4 tt = sm.tok[t];
+            float acc = tt.x * (sm.V[t][rloc] - tt.y * (sm.P[rloc][t] * tt.z));
+#pragma unroll
+            for (int s2 = 0; s2 < t; ++s2) acc = __builtin_fmaf(-sm.A[t][s2], u[s2], acc);
+            u[t] = acc;
+        }
+#pragma unroll
+        for (int t0 = 0; t0 < KMAX; t0 += LPR) {
+            const int t = t0 + j;
+            if (t < K && live) {
+                const float4 tt = sm.tok[t];
+                float ot = tt.y * (sm.R[rloc][t] * tt.w);
+#pragma unroll
+                for (int s2 = 0; s2 < KMAX; ++s2) ot = __builtin_fmaf(sm.M[t][s2], u[s2], ot);
+                store1<O_BF16>(a.o, (((size_t)b * K + t) * Hv + h) * dv + i, ot);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < KMAX; ++t)
+#pragma unroll
+            for (int r2 = 0; r2 < RPW; ++r2) us[r2][t] = u[t];
     }
 
-    // ---- 3c. stream the states: H_t = gamma_t H_{t-1} + (u_t / |k_t|) k_t
+    // ---- 3b. stream the states: H_t = gamma_t H_{t-1} + (u_t / |k_t|) k_t
     float* Hrow = a.H ? a.H + ((size_t)b * (K - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
     const size_t Hstep = (size_t)Hv * SD;
 #pragma unroll
     for (int t = 0; t < KMAX; ++t) {
         const float gm = sm.gam[t];
-        const float cu = u[t] * sm.tok[t].z;
-        S[0] = __builtin_fmaf(cu, kr[t].x, gm * S[0]);
-        S[1] = __builtin_fmaf(cu, kr[t].y, gm * S[1]);
-        S[2] = __builtin_fmaf(cu, kr[t].z, gm * S[2]);
-        S[3] = __builtin_fmaf(cu, kr[t].w, gm * S[3]);
+        float ut = us[0][t];
+#pragma unroll
+        for (int r2 = 1; r2 < RPW; ++r2)
+            if (lane / LPR == r2) ut = us[r2][t];
+        const float cu = ut * sm.tok[t].z;
+        const float4 kx = lds4<IN_BF16>(&sm.k[t][c]);
+        S[0] = __builtin_fmaf(cu, kx.x, gm * S[0]);
+        S[1] = __builtin_fmaf(cu, kx.y, gm * S[1]);
+        S[2] = __builtin_fmaf(cu, kx.z, gm * S[2]);
+        S[3] = __builtin_fmaf(cu, kx.w, gm * S[3]);
         if (live) {
             if (t < K - 1) {
                 if (Hrow) store_f4<NT>(Hrow + (size_t)t * Hstep, S);
