@@ -128,6 +128,70 @@ def cpu_baseline(wl, budget_s: float):
                       "one thread, %.1f s" % (steps, wl.name, el)}
 
 
+def other_workloads(torch, gdn, synth, dev):
+    """Kernel time of gdn_verify on the decode (K=1) and batched (B=32, K=8)
+    workloads, and of gdn_prefill_chunked on the prefill workload (B=4 x
+    T=4096, chunk 64): graph-replayed back-to-back launches over enough buffer
+    sets to exceed the Infinity Cache, HIP events on the launch stream."""
+    res = {}
+
+    def timed(fn, sets, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for d in sets:
+                fn(d)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
+
+    for name in ("decode", "batched"):
+        wl = synth.WORKLOADS[name]
+        per = wl.B * wl.Hv * wl.dv * wl.dk * 4 * (wl.T + 1)
+        R = max(2, math.ceil(2 * MALL_BYTES / per))
+        sets = []
+        for r in range(R):
+            inp = synth.make_inputs(wl, seed=r)
+            d = {k: v.to(dev) for k, v in inp.items()}
+            d["qkv"] = synth.make_qkv(wl, seed=r).to(dev)
+            d["S_out"] = torch.empty_like(d["S_in"])
+            d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev) if wl.T > 1 else None
+            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+            sets.append(d)
+
+        def ver(d, wl=wl):
+            gdn.verify(d["qkv"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"],
+                       d["H"], d["o"], wl.Hk)
+        us = timed(ver, sets, max(1, 200 // R))
+        b = verify_bytes(wl)
+        res[name] = {"verify_us": round(us, 3), "bytes_per_launch": b, "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                     "tokens_per_s": round(wl.B * wl.T / (us * 1e-6), 1)}
+        del sets
+    wl = synth.WORKLOADS["prefill"]
+    inp = synth.make_inputs(wl, seed=0)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    d["qkv"] = synth.make_qkv(wl, seed=0).to(dev)
+    d["S_out"] = torch.empty_like(d["S_in"])
+    d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev, dtype=torch.bfloat16)
+
+    def pre(d):
+        gdn.prefill_chunked(d["qkv"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"],
+                            d["o"], wl.Hk, chunk=wl.chunk)
+    us = timed(pre, [d], 5)
+    ie = 2
+    byts = wl.B * wl.T * (wl.C * ie + 2 * wl.Hv * ie + wl.Hv * wl.dv * 2) + 2 * wl.B * wl.Hv * wl.dv * wl.dk * 4
+    macs = 3 * wl.B * wl.T * wl.Hv * wl.dv * wl.dk
+    res["prefill"] = {"us": round(us, 1), "tokens_per_s": round(wl.B * wl.T / (us * 1e-6), 1),
+                      "bytes_per_launch": byts, "GBs": round(byts / (us * 1e-6) / 1e9, 1),
+                      "token_recurrence_TFLOPs": round(2 * macs / (us * 1e-6) / 1e12, 2)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +202,8 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of HIP graphs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the decode / batched / prefill kernel timings in the detail object")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -329,6 +395,8 @@ def main():
             "accept_lengths": accepts,
         },
     }
+    if not args.no_other_workloads:
+        out["detail"]["other_workloads"] = other_workloads(torch, gdn, synth, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)
