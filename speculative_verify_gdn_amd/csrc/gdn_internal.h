@@ -60,5 +60,6 @@ hipError_t launch_conv_step(const ConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
 hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
+hipError_t launch_prefill_wy(const PrefillArgs& a, bool o_bf16, hipStream_t s);
 
 }  // namespace gdn

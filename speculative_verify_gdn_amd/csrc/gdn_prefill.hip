@@ -1,4 +1,5 @@
-// gdn_prefill.hip -- the gated delta rule over a long prompt, final state only.
+// gdn_prefill.hip -- the gated delta rule over a long prompt, final state only
+// (fp32 q|k|v slabs; bf16 slabs go to the MFMA kernel of gdn_prefill_wy.hip).
 //
 // The same recurrence as the verify step (gates, L2-normalised q/k broadcast
 // from key heads, S_t = e^{g_t} S_{t-1}(I - beta k k^T) + beta v k^T,
@@ -205,7 +206,9 @@ hipError_t launch_io(const PrefillArgs& a, hipStream_t s)
 
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool o_bf16, hipStream_t s)
 {
-    if (in_bf16) return o_bf16 ? launch_io<true, true>(a, s) : launch_io<true, false>(a, s);
+    // bf16 slabs take the chunkwise WY form on MFMA (raw bf16 q, k, v are exact
+    // MFMA operands); fp32 slabs keep the fp32 token recurrence
+    if (in_bf16) return launch_prefill_wy(a, o_bf16, s);
     return o_bf16 ? launch_io<false, true>(a, s) : launch_io<false, false>(a, s);
 }
 

@@ -1,0 +1,655 @@
+// gdn_prefill_wy.hip -- chunked prefill in the chunkwise WY form on MFMA
+// (bf16 q|k|v slab).
+//
+// Per chunk of L tokens and value head (G_t = running sum of the gates g from
+// the chunk start, k^ = rk k and q^ = rq q the L2-normalised raw vectors,
+// S the state at the chunk start):
+//   A[t][s] = beta_t e^{G_t-G_s} k^_t.k^_s          (s < t)
+//   (I + A) U = beta (V - e^{G} (S K^^T)^T)          U, V: L x dv
+//   O[t]    = e^{G_t} S q^_t + sum_{s<=t} e^{G_t-G_s} (q^_t.k^_s) u_s
+//   S'      = e^{G_L} S + sum_s e^{G_L-G_s} u_s k^_s^T
+// This is the UT/WY evaluation of the gated delta rule: the same values as
+// the token recurrence up to rounding (Gated Delta Networks, Yang, Kautz and
+// Hatamizadeh, ICLR 2025: section 3.3, hardware-efficient chunkwise
+// training; atlas PR #297 "dflash scheduler/server verify-step glue": commit
+// message on the fused WY-chunkwise gated_delta_rule kernel).
+//
+// Workgroup: 8 waves, up to 128 state rows of one (sequence, value head) --
+// the whole head at d = 128, one workgroup per CU; each wave owns 16 rows for
+// the whole prompt, its state kept in registers as the MFMA accumulator tiles
+// of S^T (lane <-> state row, 4 key columns per tile).  Every chunk:
+//   stage   q, k (raw bf16) in MFMA operand order and K^T for the state
+//           update; norms by DPP row sums; gates, their running sum and the
+//           decay factors (wave 0).
+//   gram    K K^T and K Q^T tiles (raw bf16: exact products, fp32 sums),
+//           scaled to -A and M and stored as bf16 hi/lo pairs; wave 0 takes
+//           the diagonal blocks of A and inverts (I + A_ii) by forward
+//           substitution, one lane per column.  Every wave also forms
+//           P = K S^T and R = Q S^T with its state split into bf16 hi + lo,
+//           and from them the right-hand sides and the state part of O.
+//   solve   block forward substitution on the wave's 16 columns of U:
+//           U_i = T_ii (RHS_i - sum_{k<i} A_ik U_k); O from R, M and U;
+//           S^T <- e^{G_L} S^T + K^T diag(e^{G_L-G} rk) U folded in per 32
+//           tokens.  The next chunk's loads are in flight meanwhile.
+// fp32 operands enter the MFMA as a bf16 hi + lo pair (about 16 bits); a
+// product of two such operands keeps the three largest partial products.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4_t;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 16 * kWaves;        // state rows per workgroup
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: raw dword access on CDNA
+
+template <int DK, int L>
+struct WyShape {
+    static constexpr int NT = L / 16;             // 16-token tiles of a chunk
+    static constexpr int NS = (NT + 1) / 2;       // 32-token slices
+    static constexpr int NJ = DK / 32;            // 32-wide slices of the key dimension
+    static constexpr int JT = DK / 16;            // 16-wide tiles of the key dimension
+    static constexpr int NA = NT * (NT - 1) / 2;  // strictly lower 16x16 tiles
+    static constexpr int NM = NT * (NT + 1) / 2;  // lower 16x16 tiles with the diagonal
+    static constexpr int NO = NA + NM;            // gram tiles besides the diagonal of A
+    static constexpr int CPR = DK / 8;            // 16-byte pieces per q/k row
+    static constexpr int TPP = kThreads / CPR;    // tokens per staging pass
+    static constexpr int NP = (L + TPP - 1) / TPP;
+    static constexpr int VPP = kThreads / (kRows / 8);  // tokens per v staging pass
+    static constexpr int NPV = (L + VPP - 1) / VPP;
+};
+
+// LDS of one workgroup.  Operand order: element [tile][slice][lane] holds what
+// lane `lane` feeds to the MFMA for that tile, so every operand read is one
+// contiguous 16- or 8-byte access per lane.  Records are permuted inside a
+// tile (the swizzles below) so the staging writes spread over the banks.
+template <int DK, int L>
+struct WySmem {
+    using S = WyShape<DK, L>;
+    bf16x8_t qop[S::NT][S::NJ][64];  // raw q: lane (token r, group g), key dims pi(g, 0..7)
+    bf16x8_t kop[S::NT][S::NJ][64];  // raw k, same order
+    bf16x8_t ktop[S::JT][S::NS][64]; // raw k^T: lane (key dim r, group g), tokens pi(g, 0..7)
+    uint2 Ah[S::NA > 0 ? S::NA : 1][64];  // -A tiles (row block > column block), bf16 hi
+    uint2 Al[S::NA > 0 ? S::NA : 1][64];  //   and lo
+    uint2 Th[S::NT][64];             // (I + A_ii)^-1, hi
+    uint2 Tl[S::NT][64];             //   and lo
+    uint2 Mh[S::NM][64];             // M tiles, hi
+    uint2 Ml[S::NM][64];             //   and lo
+    float Ad[S::NT][16][16];         // fp32 diagonal blocks of A
+    // per token t of the chunk; padding tokens carry beta = 0, rk = rq = 0
+    float beta[L], eG[L], eGL[L], Gv[L];  // beta, e^{G_t}, e^{G_L - G_t}, G_t
+    float rk[L], rq[L];                   // 1/|k|, 1/|q|
+    float F[L];                           // e^{G_end(block of t) - G_t}
+    float E[S::NT][L];                    // e^{G_t - G_end(k)} for blocks k before t's block
+    uint16_t vs[L][kRows + 8];            // v of the workgroup's rows (raw bf16), padded rows
+};
+
+// A 32-wide slice of a contraction index is spread over the four lane groups
+// g of an MFMA operand as pi(g, s) = 4g + s (s < 4) and 16 + 4g + (s - 4)
+// (s >= 4): the order in which a 16x16 accumulator tile holds its rows, so
+// two accumulator tiles feed the next product directly.
+__device__ __forceinline__ int pi_group(int x) { return (x & 15) >> 2; }
+__device__ __forceinline__ int pi_slot(int x) { return ((x >> 4) << 2) | (x & 3); }
+
+// record swizzles (permutations of the 64 records of one operand tile)
+__device__ __forceinline__ int qk_rec(int lane, int m) { return lane ^ ((m & 3) << 2); }
+__device__ __forceinline__ int kt_rec(int lane, int jt) { return lane ^ (jt & 7); }
+
+// gates of one token for value head h
+__device__ __forceinline__ void wy_gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
+                                        float& beta, float& g)
+{
+    if (dt_bias != nullptr) {
+        beta = __frcp_rn(1.0f + __expf(-braw));
+        const float a = al + dt_bias[h];
+        const float sp = a > 20.0f ? a : __logf(1.0f + __expf(a));
+        g = -sp * __expf(A_log[h]);
+    } else {
+        beta = braw;
+        g = al;
+    }
+}
+
+// bf16 hi (round to nearest) and lo (the rounded remainder) of 2 floats, packed
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo)
+{
+    const bf16x2_t hb = {(__bf16)x0, (__bf16)x1};
+    const uint32_t hu = __builtin_bit_cast(uint32_t, hb);
+    const float r0 = x0 - __uint_as_float(hu << 16);
+    const float r1 = x1 - __uint_as_float(hu & 0xffff0000u);
+    const bf16x2_t lb = {(__bf16)r0, (__bf16)r1};
+    hi = hu;
+    lo = __builtin_bit_cast(uint32_t, lb);
+}
+
+__device__ __forceinline__ void split4(const f32x4_t x, uint2& hi, uint2& lo)
+{
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
+}
+
+__device__ __forceinline__ bf16x4_t as4(uint2 u) { return __builtin_bit_cast(bf16x4_t, u); }
+
+__device__ __forceinline__ bf16x8_t as8(uint2 a, uint2 b)
+{
+    return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
+}
+
+__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as4(a), as4(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float4 lds_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+// sum over each aligned group of N lanes (N = 4, 8 or 16), every lane gets it
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += dpp_mov<kDppQuadXor1>(v);
+    v += dpp_mov<kDppQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
+    return v;
+}
+
+__device__ __forceinline__ float sq8(const uint4 u)
+{
+    float s = 0.f;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float a = bf16_lo(w[e]), b = bf16_hi(w[e]);
+        s = __builtin_fmaf(a, a, s);
+        s = __builtin_fmaf(b, b, s);
+    }
+    return s;
+}
+
+// linear index of a gram tile other than the diagonal blocks of A ->
+// (M tile?, row block ib, column block kb): first the strictly lower A tiles
+// in row order, then the lower M tiles with the diagonal in row order
+template <int NT>
+__device__ __forceinline__ void other_tile(int i, bool& is_m, int& ib, int& kb)
+{
+    constexpr int NA = NT * (NT - 1) / 2;
+    is_m = i >= NA;
+    int r = is_m ? i - NA : i;
+    ib = is_m ? 0 : 1;
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+        const int n = is_m ? ib + 1 : ib;  // tiles in row ib
+        if (r >= n) {
+            r -= n;
+            ++ib;
+        }
+    }
+    kb = r;
+}
+
+template <int DK, int L, bool O_BF16>
+__global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
+{
+    using Sh = WyShape<DK, L>;
+    constexpr int NT = Sh::NT, NJ = Sh::NJ, JT = Sh::JT, NO = Sh::NO;
+    constexpr int CPR = Sh::CPR, TPP = Sh::TPP, NP = Sh::NP, VPP = Sh::VPP, NPV = Sh::NPV;
+    constexpr int SLOTS = (NO + kWaves - 2) / (kWaves - 1);  // gram tiles per wave 1..7
+    constexpr int OE = O_BF16 ? 2 : 4;
+    __shared__ WySmem<DK, L> sm;
+
+    const int tid = threadIdx.x;
+    const int lane0 = tid & 63, wave = tid >> 6;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int T = a.T, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
+    const int C = 2 * Hk * DK + Hv * dv;
+    const int hk = h / (Hv / Hk);
+    const uint16_t* qkv = reinterpret_cast<const uint16_t*>(a.qkv);
+
+    // this lane's state row; rows past dv carry zeros and store nothing
+    const int row = blockIdx.x * kRows + wave * 16 + (lane0 & 15);
+    const bool live = row < dv;
+    const int rowc = live ? row : dv - 1;
+
+    // ---- state S^T tiles: tile jt holds S[row][16 jt + 4 lg + e]
+    f32x4_t S[JT];
+    {
+        const float* sp = a.S_in + (((size_t)b * Hv + h) * dv + rowc) * DK + 4 * (lane0 >> 4);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+            const f32x4_t v = load_f4(sp + 16 * jt);
+            S[jt] = live ? v : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // ---- prefetch registers (one chunk ahead).  The loads go through buffer
+    // resources that cover exactly the chunk's valid tokens, so tokens past the
+    // end of the prompt read as zero.
+    uint4 qreg[NP], kreg[NP];
+    uint4 vreg[NPV];       // v: 8 rows of one token per thread
+    uint32_t graw = 0;     // wave 0, lane t: raw beta | raw alpha << 16
+    // lane offsets inside a chunk: q|k piece of the staging role, v of this
+    // lane's row at token 4 lg, the gates of token = lane
+    const int qoff = ((tid / CPR) * C + hk * DK + 8 * (tid % CPR)) * 2;
+    const int voff = ((tid / (kRows / 8)) * C + 2 * Hk * DK + h * dv + blockIdx.x * kRows + 8 * (tid % (kRows / 8))) * 2;
+    const int goff = (lane0 * Hv + h) * 2;
+    auto prefetch = [&](int c0) {
+        const int Lv = min(L, T - c0);
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(qkv + ((size_t)b * T + c0) * C), 0, Lv * C * 2, kBufferFlags);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int off = qoff + p * TPP * C * 2;
+            qreg[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+            kreg[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off + Hk * DK * 2, 0, 0));
+        }
+#pragma unroll
+        for (int p = 0; p < NPV; ++p)
+            vreg[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + p * VPP * C * 2, 0, 0));
+        if (wave == 0) {
+            const size_t g0 = ((size_t)b * T + c0) * Hv;
+            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.beta_raw) + g0), 0, Lv * Hv * 2,
+                kBufferFlags);
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.alpha) + g0), 0, Lv * Hv * 2,
+                kBufferFlags);
+            graw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, goff, 0, 0) |
+                   ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ra, goff, 0, 0) << 16);
+        }
+    };
+    prefetch(0);
+
+    for (int c0 = 0; c0 < T; c0 += L) {
+        const int Lv = min(L, T - c0);
+        __syncthreads();  // the previous chunk is done with the LDS
+        // lane indices re-materialised per chunk: keeps the compiler from holding
+        // every derived LDS address live across the loop
+        int lane = lane0, sr = tid % CPR, stp = tid / CPR;
+        asm volatile("" : "+v"(lane), "+v"(sr), "+v"(stp));
+        const int lr = lane & 15, lg = lane >> 4;
+
+        // ================= stage the chunk
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int t = p * TPP + stp;
+            const bool in_chunk = TPP * NP == L || t < L;
+            const uint4 q = qreg[p], k = kreg[p];  // zero past the prompt
+            if (in_chunk) {
+                // q, k in operand order: key dims 8 sr .. 8 sr + 7 of token t
+                const int tt = t >> 4, tr = t & 15;
+                const int m = sr >> 2, hf = (sr & 3) >> 1, g0 = (sr & 1) << 1;
+                char* qd = reinterpret_cast<char*>(&sm.qop[tt][m][0]) + 8 * hf;
+                char* kd = reinterpret_cast<char*>(&sm.kop[tt][m][0]) + 8 * hf;
+                const int r0 = qk_rec(tr + 16 * g0, m) * 16, r1 = qk_rec(tr + 16 * (g0 + 1), m) * 16;
+                *reinterpret_cast<uint2*>(qd + r0) = make_uint2(q.x, q.y);
+                *reinterpret_cast<uint2*>(qd + r1) = make_uint2(q.z, q.w);
+                *reinterpret_cast<uint2*>(kd + r0) = make_uint2(k.x, k.y);
+                *reinterpret_cast<uint2*>(kd + r1) = make_uint2(k.z, k.w);
+                // k^T in operand order: token t is group pi_group, slot pi_slot of its 32-token slice
+                const int ms = t >> 5, tg = pi_group(t & 31), ts = pi_slot(t & 31);
+                const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 8 * sr + e;
+                    uint16_t* dst =
+                        reinterpret_cast<uint16_t*>(&sm.ktop[j >> 4][ms][kt_rec((j & 15) + 16 * tg, j >> 4)]);
+                    dst[ts] = (uint16_t)((e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu));
+                }
+            }
+            // norms: every token row is CPR consecutive lanes
+            const float sq = group_sum<CPR>(sq8(q));
+            const float sk = group_sum<CPR>(sq8(k));
+            if (sr == 0 && in_chunk) {
+                const bool valid = t < Lv;
+                sm.rk[t] = valid ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.f;
+                sm.rq[t] = valid ? __builtin_amdgcn_rsqf(sq + a.eps) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < NPV; ++p) {
+            const int t = p * VPP + tid / (kRows / 8);
+            if (VPP * NPV == L || t < L)
+                *reinterpret_cast<uint4*>(&sm.vs[t][8 * (tid % (kRows / 8))]) = vreg[p];
+        }
+        if (wave == 0) {
+            // gates, their running sum and the decay factors; lane = token
+            float beta = 0.f, g = 0.f;
+            if (lane < Lv) wy_gate(bf16_lo(graw), bf16_hi(graw), a.dt_bias, a.A_log, h, beta, g);
+            float G = g;
+#pragma unroll
+            for (int d = 1; d < L; d <<= 1) {
+                const float o = __shfl_up(G, d, 64);
+                if (lane >= d) G += o;
+            }
+            const float GL = __shfl(G, L - 1, 64);
+            float Gend[NT];
+#pragma unroll
+            for (int k = 0; k < NT; ++k) Gend[k] = __shfl(G, 16 * k + 15, 64);
+            if (lane < L) {
+                const int blk = lane >> 4;
+                sm.beta[lane] = beta;
+                sm.eG[lane] = __expf(G);
+                sm.eGL[lane] = __expf(GL - G);
+                sm.Gv[lane] = G;
+                float ge = Gend[0];
+#pragma unroll
+                for (int k = 1; k < NT; ++k)
+                    if (blk == k) ge = Gend[k];
+                sm.F[lane] = __expf(fminf(ge - G, 0.f));
+#pragma unroll
+                for (int k = 0; k < NT; ++k) sm.E[k][lane] = k < blk ? __expf(fminf(G - Gend[k], 0.f)) : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ================= gram tiles
+        if (wave == 0) {
+            // diagonal blocks of A (fp32), then (I + A_ii)^-1
+            f32x4_t D[NT];
+#pragma unroll
+            for (int ib = 0; ib < NT; ++ib) {
+                D[ib] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < NJ; ++m) {
+                    const bf16x8_t kk = sm.kop[ib][m][qk_rec(lane, m)];
+                    D[ib] = mfma32(kk, kk, D[ib]);
+                }
+            }
+#pragma unroll
+            for (int ib = 0; ib < NT; ++ib) {
+                // lane: row t = 16 ib + lr, columns s = 16 ib + 4 lg + e
+                const int t = 16 * ib + lr;
+                const float bt = sm.beta[t] * sm.rk[t], Gt = sm.Gv[t];
+                const float4 rks = lds_f4(&sm.rk[16 * ib + 4 * lg]);
+                const float4 Gs = lds_f4(&sm.Gv[16 * ib + 4 * lg]);
+                const float rk4[4] = {rks.x, rks.y, rks.z, rks.w}, G4[4] = {Gs.x, Gs.y, Gs.z, Gs.w};
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 4 * lg + e;
+                    y[e] = s < lr ? bt * rk4[e] * __expf(fminf(Gt - G4[e], 0.f)) * D[ib][e] : 0.f;
+                }
+                *reinterpret_cast<float4*>(&sm.Ad[ib][lr][4 * lg]) = make_float4(y[0], y[1], y[2], y[3]);
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+            const int blk = lg, jc = lr;
+            if (blk < NT) {
+                // column jc of (I + A_blk)^-1: x_t = [t == jc] - sum_{s<t} A[t][s] x_s
+                float x[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    float acc0 = t == jc ? 1.f : 0.f, acc1 = 0.f;
+#pragma unroll
+                    for (int s4 = 0; s4 < (t + 3) / 4; ++s4) {
+                        const float4 ar = lds_f4(&sm.Ad[blk][t][4 * s4]);
+                        const float av[4] = {ar.x, ar.y, ar.z, ar.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (4 * s4 + e < t) {
+                                if (e & 1) acc1 = __builtin_fmaf(-av[e], x[4 * s4 + e], acc1);
+                                else acc0 = __builtin_fmaf(-av[e], x[4 * s4 + e], acc0);
+                            }
+                    }
+                    x[t] = acc0 + acc1;
+                }
+                // T[t][jc] -> operand lane t + 16 (jc / 4), slot jc % 4
+                uint16_t* th = reinterpret_cast<uint16_t*>(&sm.Th[blk][0]);
+                uint16_t* tl = reinterpret_cast<uint16_t*>(&sm.Tl[blk][0]);
+#pragma unroll
+                for (int t = 0; t < 16; t += 2) {
+                    uint32_t hi, lo;
+                    split2(x[t], x[t + 1], hi, lo);
+                    const int at = (t + 16 * (jc >> 2)) * 4 + (jc & 3);
+                    th[at] = (uint16_t)hi;
+                    tl[at] = (uint16_t)lo;
+                    th[at + 4] = (uint16_t)(hi >> 16);
+                    tl[at + 4] = (uint16_t)(lo >> 16);
+                }
+            }
+        } else {
+            // the other tiles, round robin over waves 1..7: -A below the diagonal, M
+            f32x4_t D[SLOTS];
+            bool ism[SLOTS];
+            int ibs[SLOTS], kbs[SLOTS];
+#pragma unroll
+            for (int sl = 0; sl < SLOTS; ++sl) {
+                const int i = sl * (kWaves - 1) + wave - 1;
+                other_tile<NT>(i < NO ? i : 0, ism[sl], ibs[sl], kbs[sl]);
+                D[sl] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int m = 0; m < NJ; ++m) {
+                    const int rec = qk_rec(lane, m);
+                    const bf16x8_t ka = sm.kop[kbs[sl]][m][rec];
+                    const bf16x8_t xb = ism[sl] ? sm.qop[ibs[sl]][m][rec] : sm.kop[ibs[sl]][m][rec];
+                    D[sl] = mfma32(ka, xb, D[sl]);
+                }
+            }
+#pragma unroll
+            for (int sl = 0; sl < SLOTS; ++sl) {
+                const int i = sl * (kWaves - 1) + wave - 1;
+                if (i < NO) {
+                    const int ib = ibs[sl], kb = kbs[sl];
+                    // lane: row t of the tile (ib, kb), columns s = 16 kb + 4 lg + e
+                    const int t = 16 * ib + lr, s0 = 16 * kb + 4 * lg;
+                    const float4 rks = lds_f4(&sm.rk[s0]);
+                    const float rk4[4] = {rks.x, rks.y, rks.z, rks.w};
+                    float y[4];
+                    if (kb < ib) {
+                        // e^{G_t - G_s} = E[kb][t] F[s]
+                        const float4 Fs = lds_f4(&sm.F[s0]);
+                        const float F4[4] = {Fs.x, Fs.y, Fs.z, Fs.w};
+                        const float ct = (ism[sl] ? sm.rq[t] : sm.beta[t] * sm.rk[t]) * sm.E[kb][t];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) y[e] = ct * F4[e] * rk4[e] * D[sl][e];
+                    } else {
+                        // diagonal tile of M: direct decay, s <= t
+                        const float Gt = sm.Gv[t], rqt = sm.rq[t];
+                        const float4 Gs = lds_f4(&sm.Gv[s0]);
+                        const float G4[4] = {Gs.x, Gs.y, Gs.z, Gs.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            y[e] = 4 * lg + e <= lr ? rqt * rk4[e] * __expf(fminf(Gt - G4[e], 0.f)) * D[sl][e] : 0.f;
+                    }
+                    uint2 hi, lo;
+                    if (ism[sl]) {
+                        split4(f32x4_t{y[0], y[1], y[2], y[3]}, hi, lo);
+                        const int im = ib * (ib + 1) / 2 + kb;
+                        sm.Mh[im][lane] = hi;
+                        sm.Ml[im][lane] = lo;
+                    } else {
+                        // stored negated: the solve accumulates -A U onto the right-hand side
+                        split4(f32x4_t{-y[0], -y[1], -y[2], -y[3]}, hi, lo);
+                        const int ia = ib * (ib - 1) / 2 + kb;
+                        sm.Ah[ia][lane] = hi;
+                        sm.Al[ia][lane] = lo;
+                    }
+                }
+            }
+        }
+
+        // ================= P = K S^T, R = Q S^T -> right-hand sides X and the state part of O
+        f32x4_t X[NT], O[NT];
+        {
+            f32x4_t P[NT], R[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                P[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                R[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int m = 0; m < NJ; ++m) {
+                uint2 h0, l0, h1, l1;
+                split4(S[2 * m], h0, l0);
+                split4(S[2 * m + 1], h1, l1);
+                const bf16x8_t shi = as8(h0, h1), slo = as8(l0, l1);
+                const int rec = qk_rec(lane, m);
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt) {
+                    const bf16x8_t ka = sm.kop[tt][m][rec];
+                    const bf16x8_t qa = sm.qop[tt][m][rec];
+                    P[tt] = mfma32(ka, shi, P[tt]);
+                    P[tt] = mfma32(ka, slo, P[tt]);
+                    R[tt] = mfma32(qa, shi, R[tt]);
+                    R[tt] = mfma32(qa, slo, R[tt]);
+                }
+            }
+            // X = beta (v - e^{G} rk P), O = e^{G} rq R (token t = 16 tt + 4 lg + e)
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt) {
+                const int t0 = 16 * tt + 4 * lg;
+                const float4 be = lds_f4(&sm.beta[t0]), eg = lds_f4(&sm.eG[t0]);
+                const float4 rk4 = lds_f4(&sm.rk[t0]), rq4 = lds_f4(&sm.rq[t0]);
+                const float bv[4] = {be.x, be.y, be.z, be.w}, gv[4] = {eg.x, eg.y, eg.z, eg.w};
+                const float kv[4] = {rk4.x, rk4.y, rk4.z, rk4.w}, qv[4] = {rq4.x, rq4.y, rq4.z, rq4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float v = live ? bf16_to_f32(sm.vs[t0 + e][wave * 16 + lr]) : 0.f;
+                    X[tt][e] = bv[e] * __builtin_fmaf(-gv[e] * kv[e], P[tt][e], v);
+                    O[tt][e] = gv[e] * qv[e] * R[tt][e];
+                }
+            }
+        }
+        __syncthreads();
+
+        // the next chunk's loads fly during the solve and the staging barrier
+        if (c0 + L < T) prefetch(c0 + L);
+
+        // ================= per wave (its 16 rows): U by block forward substitution, the
+        // outputs, and the state update per 32 tokens
+        {
+            const float eGL = sm.eG[L - 1];
+#pragma unroll
+            for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[jt][e] *= eGL;
+        }
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<char*>(a.o) + ((size_t)b * T + c0) * Hv * dv * OE, 0, Lv * Hv * dv * OE, kBufferFlags);
+        // rows past dv and tokens past the prompt fall outside the resource: dropped
+        const int ostride = __builtin_amdgcn_readfirstlane(Hv * dv * OE);
+        const int ooff = live ? ((4 * lg * Hv + h) * dv + row) * OE : 0x7ffffff0;
+        uint2 Uh[NT], Ul[NT];
+        uint2 ch0 = make_uint2(0, 0), cl0 = make_uint2(0, 0);
+#pragma unroll
+        for (int ib = 0; ib < NT; ++ib) {
+            f32x4_t x = X[ib];
+#pragma unroll
+            for (int kb = 0; kb < ib; ++kb) {
+                const int ia = ib * (ib - 1) / 2 + kb;
+                const uint2 ah = sm.Ah[ia][lane], al = sm.Al[ia][lane];
+                x = mfma16(ah, Uh[kb], x);
+                x = mfma16(ah, Ul[kb], x);
+                x = mfma16(al, Uh[kb], x);
+            }
+            uint2 xh, xl;
+            split4(x, xh, xl);
+            const uint2 th = sm.Th[ib][lane], tl = sm.Tl[ib][lane];
+            f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+            u = mfma16(th, xh, u);
+            u = mfma16(th, xl, u);
+            u = mfma16(tl, xh, u);
+            split4(u, Uh[ib], Ul[ib]);
+
+            f32x4_t o = O[ib];
+#pragma unroll
+            for (int kb = 0; kb <= ib; ++kb) {
+                const int im = ib * (ib + 1) / 2 + kb;
+                const uint2 mh = sm.Mh[im][lane], ml = sm.Ml[im][lane];
+                o = mfma16(mh, Uh[kb], o);
+                o = mfma16(mh, Ul[kb], o);
+                o = mfma16(ml, Uh[kb], o);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int off = ooff + (16 * ib + e) * ostride;
+                if constexpr (O_BF16)
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)o[e]), ro, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[e]), ro, off, 0, 0);
+            }
+
+            // c_t u_t with c_t = e^{G_L - G_t} rk_t: operand of the state update
+            const float4 el = lds_f4(&sm.eGL[16 * ib + 4 * lg]), rk4 = lds_f4(&sm.rk[16 * ib + 4 * lg]);
+            const f32x4_t cu = {el.x * rk4.x * u[0], el.y * rk4.y * u[1], el.z * rk4.z * u[2], el.w * rk4.w * u[3]};
+            uint2 ch, cl;
+            split4(cu, ch, cl);
+            if (ib & 1) {
+                // tiles ib-1, ib form the 32-token slice ib/2
+                const bf16x8_t chi = as8(ch0, ch), clo = as8(cl0, cl);
+#pragma unroll
+                for (int jt = 0; jt < JT; ++jt) {
+                    const bf16x8_t ka = sm.ktop[jt][ib >> 1][kt_rec(lane, jt)];
+                    S[jt] = mfma32(ka, chi, S[jt]);
+                    S[jt] = mfma32(ka, clo, S[jt]);
+                }
+            } else if (ib == NT - 1) {
+                // a lone 16-token tile: slots 0..3 of its slice
+#pragma unroll
+                for (int jt = 0; jt < JT; ++jt) {
+                    const uint4 kk = __builtin_bit_cast(uint4, sm.ktop[jt][ib >> 1][kt_rec(lane, jt)]);
+                    const uint2 ka = make_uint2(kk.x, kk.y);
+                    S[jt] = mfma16(ka, ch, S[jt]);
+                    S[jt] = mfma16(ka, cl, S[jt]);
+                }
+            } else {
+                ch0 = ch;
+                cl0 = cl;
+            }
+        }
+    }
+
+    if (live) {
+        float* sp = a.S_out + (((size_t)b * Hv + h) * dv + row) * DK + 4 * (lane0 >> 4);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) store_f4<false>(sp + 16 * jt, S[jt]);
+    }
+}
+
+template <int DK, int L, bool O_BF16>
+hipError_t launch_l(const PrefillArgs& a, hipStream_t s)
+{
+    dim3 grid((a.dv + kRows - 1) / kRows, a.Hv, a.B);
+    prefill_wy_kernel<DK, L, O_BF16><<<grid, dim3(kThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <int DK, bool O_BF16>
+hipError_t launch_d(const PrefillArgs& a, hipStream_t s)
+{
+    switch (a.chunk) {
+    case 16: return launch_l<DK, 16, O_BF16>(a, s);
+    case 32: return launch_l<DK, 32, O_BF16>(a, s);
+    case 64: return launch_l<DK, 64, O_BF16>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <bool O_BF16>
+hipError_t launch_o(const PrefillArgs& a, hipStream_t s)
+{
+    switch (a.dk) {
+    case 32: return launch_d<32, O_BF16>(a, s);
+    case 64: return launch_d<64, O_BF16>(a, s);
+    case 128: return launch_d<128, O_BF16>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_wy(const PrefillArgs& a, bool o_bf16, hipStream_t s)
+{
+    return o_bf16 ? launch_o<true>(a, s) : launch_o<false>(a, s);
+}
+
+}  // namespace gdn

@@ -328,6 +328,50 @@ def test_prefill_parity(name, over, chunk):
     assert np.all(err <= TOL * norms[..., None])
 
 
+# bf16 slabs run the chunkwise WY kernel on MFMA.  These cases cover its tiling:
+# every chunk length, exactly one chunk, T < chunk, ragged last chunks, dk of
+# 32/64/128, dv that leaves part of the 64-row workgroup empty, the state
+# updated in place, bf16 outputs, activated gates, and weak decay (the initial
+# state still matters after hundreds of tokens).
+WY_CASES = [
+    (dict(B=1, T=64, Hk=1, Hv=2), 64, dict()),
+    (dict(B=2, T=77, Hk=2, Hv=4, dk=32, dv=32), 16, dict(weak=True)),
+    (dict(B=1, T=100, Hk=1, Hv=3, dk=64, dv=40), 32, dict(weak=True, inplace=True, o_bf16=True)),
+    (dict(B=1, T=5, Hk=2, Hv=2), 64, dict(activated=True)),
+    (dict(B=1, T=300, Hk=1, Hv=1), 64, dict(weak=True)),
+    (dict(B=1, T=129, Hk=1, Hv=2), 32, dict(weak=True, o_bf16=True)),
+    (dict(B=1, T=47, Hk=1, Hv=2), 16, dict()),
+    (dict(B=3, T=96, Hk=2, Hv=2, dk=64, dv=64), 64, dict(activated=True, weak=True)),
+]
+
+
+@pytest.mark.parametrize("over,chunk,opt", WY_CASES)
+def test_prefill_wy_parity(over, chunk, opt):
+    wl = synth.small("prefill", **over)
+    say("prefill wy", over, chunk, opt)
+    inp = synth.make_inputs(wl, seed=11, weak_decay=opt.get("weak", False))
+    raw = not opt.get("activated")
+    if not raw:
+        inp["beta_raw"] = torch.sigmoid(inp["beta_raw"].float()).to(inp["beta_raw"].dtype)
+        inp["alpha"] = (-torch.nn.functional.softplus(inp["alpha"].float())).to(inp["alpha"].dtype)
+    qkv = synth.make_qkv(wl, seed=11)
+    S_in_ref = f64(inp["S_in"])
+    d = {k: dev(v) for k, v in inp.items()}
+    S_out = d["S_in"] if opt.get("inplace") else torch.empty_like(d["S_in"])
+    o_bf16 = opt.get("o_bf16", False)
+    o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda", dtype=torch.bfloat16 if o_bf16 else torch.float32)
+    dt, alog = (d["dt_bias"], d["A_log"]) if raw else (None, None)
+    gdn.prefill_chunked(dev(qkv), d["beta_raw"], d["alpha"], dt, alog, d["S_in"], S_out, o, wl.Hk, chunk=chunk)
+    torch.cuda.synchronize()
+    dt_r, alog_r = (f64(inp["dt_bias"]), f64(inp["A_log"])) if raw else (None, None)
+    S_ref, o_ref, norms = oracle_segments(f64(qkv), f64(inp["beta_raw"]), f64(inp["alpha"]), dt_r, alog_r,
+                                          S_in_ref, wl.Hk)
+    check_states(S_out.cpu().numpy(), S_ref, "prefill S_out")
+    err = np.abs(o.float().cpu().numpy() - o_ref)
+    bound = TOL * norms[..., None] + (np.abs(o_ref) * 2.0 ** -8 if o_bf16 else 0.0)
+    assert np.all(err <= bound), "o: worst err/bound = %.3g" % float(np.max(err / np.maximum(bound, 1e-30)))
+
+
 def test_prefill_full_size_sampled_heads():
     """B=4 x T=4096, 48 value heads, d=128: six (sequence, head) pairs re-run on the oracle."""
     wl = synth.WORKLOADS["prefill"]
