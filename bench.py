@@ -185,10 +185,16 @@ def other_workloads(torch, gdn, synth, dev):
     us = timed(pre, [d], 5)
     ie = 2
     byts = wl.B * wl.T * (wl.C * ie + 2 * wl.Hv * ie + wl.Hv * wl.dv * 2) + 2 * wl.B * wl.Hv * wl.dv * wl.dk * 4
-    macs = 3 * wl.B * wl.T * wl.Hv * wl.dv * wl.dk
+    # multiply-adds of the chunkwise form per (sequence, head, chunk of L tokens): S K^T, S Q^T and
+    # the state update (3 dv dk L), K K^T and Q K^T lower halves (L^2 dk), the triangular solve and
+    # M U lower halves (L^2 dv); the ragged last chunk counted whole
+    L = wl.chunk
+    chunks = -(-wl.T // L)
+    macs = wl.B * wl.Hv * chunks * (3 * wl.dv * wl.dk * L + L * L * (wl.dk + wl.dv))
     res["prefill"] = {"us": round(us, 1), "tokens_per_s": round(wl.B * wl.T / (us * 1e-6), 1),
                       "bytes_per_launch": byts, "GBs": round(byts / (us * 1e-6) / 1e9, 1),
-                      "token_recurrence_TFLOPs": round(2 * macs / (us * 1e-6) / 1e12, 2)}
+                      "chunkwise_flop_per_launch": 2 * macs,
+                      "chunkwise_TFLOPs": round(2 * macs / (us * 1e-6) / 1e12, 2)}
     return res
 
 

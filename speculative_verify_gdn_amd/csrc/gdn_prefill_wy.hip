@@ -72,7 +72,8 @@ struct WySmem {
     using S = WyShape<DK, L>;
     bf16x8_t qop[S::NT][S::NJ][64];  // raw q: lane (token r, group g), key dims pi(g, 0..7)
     bf16x8_t kop[S::NT][S::NJ][64];  // raw k, same order
-    bf16x8_t ktop[S::JT][S::NS][64]; // raw k^T: lane (key dim r, group g), tokens pi(g, 0..7)
+    bf16x8_t ktop[S::JT * (S::NS * 64 + 1)];  // raw k^T: per key tile jt, NS slices of 64 records
+                                              // (lane (key dim r, group g), tokens pi(g, 0..7)) + 1 pad
     uint2 Ah[S::NA > 0 ? S::NA : 1][64];  // -A tiles (row block > column block), bf16 hi
     uint2 Al[S::NA > 0 ? S::NA : 1][64];  //   and lo
     uint2 Th[S::NT][64];             // (I + A_ii)^-1, hi
@@ -95,9 +96,12 @@ struct WySmem {
 __device__ __forceinline__ int pi_group(int x) { return (x & 15) >> 2; }
 __device__ __forceinline__ int pi_slot(int x) { return ((x >> 4) << 2) | (x & 3); }
 
-// record swizzles (permutations of the 64 records of one operand tile)
+// record swizzle of q/k operand tiles (a permutation of the 64 records; it
+// spreads the staging writes over the banks), and the record of K^T operand
+// (jt, slice, lane): one pad record per key tile does the same for K^T
 __device__ __forceinline__ int qk_rec(int lane, int m) { return lane ^ ((m & 3) << 2); }
-__device__ __forceinline__ int kt_rec(int lane, int jt) { return lane ^ (jt & 7); }
+template <int NS>
+__device__ __forceinline__ int kt_rec(int jt, int ms, int lane) { return jt * (NS * 64 + 1) + ms * 64 + lane; }
 
 // gates of one token for value head h
 __device__ __forceinline__ void wy_gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
@@ -162,15 +166,15 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// sum of squares of 8 bf16 (exact products, fp32 sums)
 __device__ __forceinline__ float sq8(const uint4 u)
 {
     float s = 0.f;
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float a = bf16_lo(w[e]), b = bf16_hi(w[e]);
-        s = __builtin_fmaf(a, a, s);
-        s = __builtin_fmaf(b, b, s);
+        const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w[e]);
+        s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
     }
     return s;
 }
@@ -297,13 +301,11 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
                 // k^T in operand order: token t is group pi_group, slot pi_slot of its 32-token slice
                 const int ms = t >> 5, tg = pi_group(t & 31), ts = pi_slot(t & 31);
                 const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
+                uint16_t* dst = reinterpret_cast<uint16_t*>(
+                                    &sm.ktop[kt_rec<Sh::NS>(sr >> 1, ms, 8 * (sr & 1) + 16 * tg)]) + ts;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 8 * sr + e;
-                    uint16_t* dst =
-                        reinterpret_cast<uint16_t*>(&sm.ktop[j >> 4][ms][kt_rec((j & 15) + 16 * tg, j >> 4)]);
-                    dst[ts] = (uint16_t)((e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu));
-                }
+                for (int e = 0; e < 8; ++e)  // key dim 8 sr + e: record + e
+                    dst[8 * e] = (uint16_t)((e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu));
             }
             // norms: every token row is CPR consecutive lanes
             const float sq = group_sum<CPR>(sq8(q));
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
                 const bf16x8_t chi = as8(ch0, ch), clo = as8(cl0, cl);
 #pragma unroll
                 for (int jt = 0; jt < JT; ++jt) {
-                    const bf16x8_t ka = sm.ktop[jt][ib >> 1][kt_rec(lane, jt)];
+                    const bf16x8_t ka = sm.ktop[kt_rec<Sh::NS>(jt, ib >> 1, lane)];
                     S[jt] = mfma32(ka, chi, S[jt]);
                     S[jt] = mfma32(ka, clo, S[jt]);
                 }
@@ -596,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
                 // a lone 16-token tile: slots 0..3 of its slice
 #pragma unroll
                 for (int jt = 0; jt < JT; ++jt) {
-                    const uint4 kk = __builtin_bit_cast(uint4, sm.ktop[jt][ib >> 1][kt_rec(lane, jt)]);
+                    const uint4 kk = __builtin_bit_cast(uint4, sm.ktop[kt_rec<Sh::NS>(jt, ib >> 1, lane)]);
                     const uint2 ka = make_uint2(kk.x, kk.y);
                     S[jt] = mfma16(ka, ch, S[jt]);
                     S[jt] = mfma16(ka, cl, S[jt]);
