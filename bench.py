@@ -279,6 +279,7 @@ def main():
     torch.cuda.synchronize()
 
     graphs = None
+    per_graph = 1
     if not args.eager:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -287,11 +288,16 @@ def main():
                 step(d)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        # steps back to back as in a serving loop: one graph holds one step on
+        # each of the R buffer sets (when K is a multiple of R), else one graph
+        # per set
+        per_graph = R if args.steps % R == 0 else 1
         graphs = []
-        for d in sets:
+        for i in range(0, R, per_graph):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(d)
+                for d in sets[i:i + per_graph]:
+                    step(d)
             graphs.append(g)
         for g in graphs:
             g.replay()
@@ -304,8 +310,8 @@ def main():
     w0 = time.perf_counter()
     ev0.record()
     if graphs is not None:
-        for s in range(K):
-            graphs[s % R].replay()
+        for s in range(K // per_graph):
+            graphs[s % len(graphs)].replay()
     else:
         for s in range(K):
             step(sets[s % R])
@@ -377,7 +383,7 @@ def main():
             "workload": wl.name, "B": wl.B, "K": wl.T, "Hk": wl.Hk, "Hv": wl.Hv, "dk": wl.dk, "dv": wl.dv,
             "C": wl.C, "conv_width": wl.W, "io_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
             "step": "conv_step + verify(capture) + rollback", "buffer_sets": R,
-            "working_set_MB": round(R * set_bytes / 2 ** 20, 1), "launch": "eager" if args.eager else "hip_graph",
+            "working_set_MB": round(R * set_bytes / 2 ** 20, 1), "launch": "eager" if args.eager else ("hip_graph, %d steps per graph" % per_graph),
         },
         "roofline": {
             "bound": "hbm",
@@ -396,6 +402,8 @@ def main():
             "conv_GBs": round(conv_bytes(wl) / (t_conv * 1e-6) / 1e9, 1),
             "rollback_GBs": round(mean_rb_bytes / (t_rb * 1e-6) / 1e9, 1),
             "verify_only_tokens_per_s": round(tokens / (t_ver * 1e-6), 1),
+            # tokens per second per layer counting the conv step and the verify (rollback apart)
+            "conv_verify_tokens_per_s": round(tokens / ((t_conv + t_ver) * 1e-6), 1),
             "wall_ms_timed": round(wall_ms, 3),
             "source_sha": sha,
             "accept_lengths": accepts,
