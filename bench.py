@@ -128,7 +128,7 @@ def cpu_baseline(wl, budget_s: float):
                       "one thread, %.1f s" % (steps, wl.name, el)}
 
 
-def other_workloads(torch, gdn, synth, dev):
+def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "prefill")):
     """Kernel time of gdn_verify on the decode (K=1) and batched (B=32, K=8)
     workloads, and of gdn_prefill_chunked on the prefill workload (B=4 x
     T=4096, chunk 64): graph-replayed back-to-back launches over enough buffer
@@ -150,7 +150,7 @@ def other_workloads(torch, gdn, synth, dev):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / (reps * len(sets))
 
-    for name in ("decode", "batched"):
+    for name in [n for n in ("decode", "batched") if n in only]:
         wl = synth.WORKLOADS[name]
         per = wl.B * wl.Hv * wl.dv * wl.dk * 4 * (wl.T + 1)
         R = max(2, math.ceil(2 * MALL_BYTES / per))
@@ -172,6 +172,8 @@ def other_workloads(torch, gdn, synth, dev):
         res[name] = {"verify_us": round(us, 3), "bytes_per_launch": b, "GBs": round(b / (us * 1e-6) / 1e9, 1),
                      "tokens_per_s": round(wl.B * wl.T / (us * 1e-6), 1)}
         del sets
+    if "prefill" not in only:
+        return res
     wl = synth.WORKLOADS["prefill"]
     inp = synth.make_inputs(wl, seed=0)
     d = {k: v.to(dev) for k, v in inp.items()}
@@ -210,6 +212,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the decode / batched / prefill kernel timings in the detail object")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only time gdn_prefill_chunked on the prefill workload (B=4 x T=4096) and print its figures")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -237,9 +241,13 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
         return
 
+    gdn.load()
+    if args.prefill_only:
+        print(json.dumps({"prefill": other_workloads(torch, gdn, synth, dev, only=("prefill",))["prefill"]}))
+        return
+
     wl = synth.WORKLOADS[args.workload]
     assert wl.chunk == 0, "the bench step is the verify path"
-    gdn.load()
 
     # ---------------------------------------------------------------- buffers
     def make_set(seed):
