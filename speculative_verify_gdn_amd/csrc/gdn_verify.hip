@@ -25,14 +25,16 @@
 // -- 1 KB contiguous at DK=128.
 //   1. the raw q, k of the key head, the workgroup's S_in rows and their v
 //      values go to LDS with a few 16-byte loads per thread (branch-free, so
-//      they are in flight together), the gates are computed; each lane keeps
-//      its own state float4;
-//   2. the contractions run on MFMA, one job per wave: K K^T and then the
-//      norms of k, the decay sums and A (wave 0); Q K^T, diag(Q Q^T) and M
-//      (wave 3); K S^T (wave 1) and Q S^T (wave 2).  Operands: raw q, k in bf16 (products of bf16
-//      are exact, accumulation is fp32) against the state split into two bf16
-//      halves (hi + lo keeps about 16 bits), 16x16x32 bf16 instructions; for
-//      f32 inputs 16x16x4 f32 instructions on the unsplit values;
+//      they are in flight together); the q/k norms come from the staging
+//      threads (dot products and DPP row sums), the gates and their running
+//      sums from the last wave; each lane keeps its own state float4;
+//   2. the contractions run on MFMA, one job per wave: K K^T and A (wave 0);
+//      Q K^T and M (wave 3); K S^T (wave 1) and Q S^T (wave 2).  The norms,
+//      gates and running sums of g are already known from phase 1.  Operands:
+//      raw q, k in bf16 (products of bf16 are exact, accumulation is fp32)
+//      against the state split into two bf16 halves (hi + lo keeps about 16
+//      bits), 16x16x32 bf16 instructions; for f32 inputs 16x16x4 f32
+//      instructions on the unsplit values;
 //   3. per row: the forward substitution for u_t is shared by the row's lanes
 //      (lane j owns token j, each finished u_t is broadcast with v_readlane),
 //      which also gives o_t; then every lane streams H_t = gamma_t H_{t-1} +
@@ -64,10 +66,57 @@ struct VerifySmem {
     float V[KP][RPG];               // v of the workgroup's rows, per token
     float4 tok[KP];                 // per token: beta, e^{G}, 1/|k|, 1/|q|
     float gam[KP];                  // e^{g}
-    float g[KP];
-    float G[2][KP];                 // running sums of g (one copy per prologue wave)
-    float rk3[KP];                  // 1/|k| as the M wave computes it
+    float Gv[KP];                   // running sums of g
 };
+
+// sum over each aligned group of N lanes (N = 4, 8, 16 or 32), every lane gets it
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += dpp_mov<kDppQuadXor1>(v);
+    v += dpp_mov<kDppQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
+    if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+    return v;
+}
+
+// inclusive prefix sum over lanes 0..N-1 (N = 16 or 32; lanes past N get garbage):
+// Hillis-Steele inside each DPP row, then the last lane of row 0 carried into row 1
+template <int N>
+__device__ __forceinline__ float lane_scan(float v)
+{
+    static_assert(N == 16 || N == 32, "one or two DPP rows");
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));  // row_shr:1
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));  // row_shr:2
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xF, 0xF, true));  // row_shr:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xF, 0xF, true));  // row_shr:8
+    if constexpr (N == 32) {
+        const float c = __shfl(v, 15, 64);
+        v = (__lane_id() >> 4) == 1 ? v + c : v;
+    }
+    return v;
+}
+
+// sum of squares of the 16 bytes of a q/k row piece (exact products, fp32 sums)
+template <bool BF16>
+__device__ __forceinline__ float sumsq16(const uint4 u)
+{
+    float s = 0.f;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if constexpr (BF16) {
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w[e]);
+            s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+        } else {
+            const float f = __uint_as_float(w[e]);
+            s = __builtin_fmaf(f, f, s);
+        }
+    }
+    return s;
+}
 
 // gates of one token for value head h
 __device__ __forceinline__ void gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
@@ -192,125 +241,120 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     const in_t* X = reinterpret_cast<const in_t*>(a.qkv) + (size_t)b * K * C;   // this sequence's rows
     const size_t qoff = (size_t)hk * DK, koff = (size_t)(Hk + hk) * DK;
 
-    // ---- 1. stage q, k, the state rows; gates; loads for the streaming phase
-    // (addresses clamped into range instead of branching, so the loads issue together)
+    f32x4_t S;
+    // ---- 1. stage q, k and their norms, the state rows, v; gates and their running sums.
+    // Every global load of the phase is issued first (addresses clamped into
+    // range instead of branching), so they are in flight together.
     {
         constexpr int EPV = IN_BF16 ? 8 : 4;     // elements per 16-byte vector
-        constexpr int VPR = DK / EPV;
-        for (int idx = tid; idx < KP * VPR; idx += kThreads) {
-            const int t = idx / VPR, cc = (idx % VPR) * EPV;
-            const in_t* row = X + (size_t)(t < K ? t : K - 1) * C;
-            uint4 qv = *reinterpret_cast<const uint4*>(row + qoff + cc);
-            uint4 kv = *reinterpret_cast<const uint4*>(row + koff + cc);
-            if (t >= K) qv = kv = make_uint4(0, 0, 0, 0);
-            *reinterpret_cast<uint4*>(&sm.q[t][cc]) = qv;
-            *reinterpret_cast<uint4*>(&sm.k[t][cc]) = kv;
+        constexpr int VPR = DK / EPV;            // consecutive threads per token row
+        static_assert(64 % VPR == 0 && (KP * VPR) % 64 == 0, "a token row is a lane group of one wave");
+        constexpr int NQ = (KP * VPR + kThreads - 1) / kThreads;     // q/k pieces per thread
+        constexpr int NV = (KMAX * RPG + kThreads - 1) / kThreads;   // v elements per thread
+        uint4 qv[NQ], kv[NQ];
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int idx = tid + n * kThreads;
+            if (idx < KP * VPR) {
+                const int t = idx / VPR, cc = (idx % VPR) * EPV;
+                const in_t* row = X + (size_t)(t < K ? t : K - 1) * C;
+                qv[n] = *reinterpret_cast<const uint4*>(row + qoff + cc);
+                kv[n] = *reinterpret_cast<const uint4*>(row + koff + cc);
+            }
         }
-        if (wave == kWaves - 1 && lane < KP) {
-            const int tc = lane < K ? lane : K - 1;
-            const size_t gi = ((size_t)b * K + tc) * Hv + h;
-            float be, g;
-            gate(load1<IN_BF16>(a.beta_raw, gi), load1<IN_BF16>(a.alpha, gi), a.dt_bias, a.A_log, h, be, g);
-            sm.g[lane] = lane < K ? g : 0.f;
-            sm.tok[lane].x = lane < K ? be : 0.f;
+        f32x4_t S0 = load_f4(Sh + (size_t)ic * DK + c);
+        float vv[NV];
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            const int idx = tid + n * kThreads;
+            const int t = idx / RPG, rr = idx % RPG;
+            const int gr = blockIdx.x * RPG + rr;
+            const in_t* row = X + (size_t)(t < K ? t : (K - 1)) * C;
+            vv[n] = idx < KMAX * RPG ? load1<IN_BF16>(row, 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1))
+                                     : 0.f;
         }
-    }
-    f32x4_t S = load_f4(Sh + (size_t)ic * DK + c);
-    if (!live) S = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4_t*>(&sm.S[rloc][c]) = S;
-    if constexpr (RPG < 16) {
-        for (int idx = tid; idx < (16 - RPG) * LPR; idx += kThreads)
-            *reinterpret_cast<f32x4_t*>(&sm.S[RPG + idx / LPR][4 * (idx % LPR)]) = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    // v of the workgroup's RPG rows for every token: one element per thread
-    for (int idx = tid; idx < KMAX * RPG; idx += kThreads) {
-        const int t = idx / RPG, rr = idx % RPG;
-        const int gr = blockIdx.x * RPG + rr;
-        const in_t* row = X + (size_t)(t < K ? t : K - 1) * C;
-        sm.V[t][rr] = load1<IN_BF16>(row, 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1));
+        float braw = 0.f, bal = 0.f;
+        if (wave == kWaves - 1 && lane < K) {
+            const size_t gi = ((size_t)b * K + lane) * Hv + h;
+            braw = load1<IN_BF16>(a.beta_raw, gi);
+            bal = load1<IN_BF16>(a.alpha, gi);
+        }
+
+#pragma unroll
+        for (int n = 0; n < NQ; ++n) {
+            const int idx = tid + n * kThreads;
+            if (idx < KP * VPR) {
+                const int t = idx / VPR, cc = (idx % VPR) * EPV;
+                if (t >= K) qv[n] = kv[n] = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(&sm.q[t][cc]) = qv[n];
+                *reinterpret_cast<uint4*>(&sm.k[t][cc]) = kv[n];
+                // 1/|q_t|, 1/|k_t| (padded tokens keep q^ = k^ = 0, never 0 * 1/sqrt(0))
+                const float sq = group_sum<VPR>(sumsq16<IN_BF16>(qv[n]));
+                const float sk = group_sum<VPR>(sumsq16<IN_BF16>(kv[n]));
+                if (cc == 0) {
+                    sm.tok[t].z = t < K ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.0f;
+                    sm.tok[t].w = t < K ? __builtin_amdgcn_rsqf(sq + a.eps) : 0.0f;
+                }
+            }
+        }
+        if (!live) S0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        S = S0;
+        *reinterpret_cast<f32x4_t*>(&sm.S[rloc][c]) = S0;
+        if constexpr (RPG < 16) {
+            for (int idx = tid; idx < (16 - RPG) * LPR; idx += kThreads)
+                *reinterpret_cast<f32x4_t*>(&sm.S[RPG + idx / LPR][4 * (idx % LPR)]) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            const int idx = tid + n * kThreads;
+            if (idx < KMAX * RPG) sm.V[idx / RPG][idx % RPG] = vv[n];
+        }
+        if (wave == kWaves - 1) {
+            // lane t: gates of token t, then G_t = g_0 + ... + g_t by a scan over the lanes
+            float be = 0.f, g = 0.f;
+            if (lane < K) gate(braw, bal, a.dt_bias, a.A_log, h, be, g);
+            const float G = lane_scan<KP>(g);
+            if (lane < KP) {
+                sm.Gv[lane] = G;
+                sm.tok[lane].x = be;
+                sm.tok[lane].y = __expf(G);
+                sm.gam[lane] = __expf(g);
+            }
+        }
     }
     __syncthreads();
 
     // ---- 2. contractions on MFMA
-    // wave 0: K K^T -> 1/|k|, running decay sums, A
-    // wave 3: Q K^T, diag(Q Q^T), diag(K K^T) -> 1/|q|, M
+    // wave 0: K K^T -> A
+    // wave 3: Q K^T -> M
     // waves 1, 2: K S^T, Q S^T
     const int n16 = lane & 15, m0 = (lane >> 4) * 4;   // 16x16 result layout: row m0+e, column n16
     if (wave == 0 || wave == 3) {
         const bool wa = wave == 0;
-        const int wi = wa ? 0 : 1;
-        float* Gw = sm.G[wi];
-        float* rkw = wa ? nullptr : sm.rk3;
-        if (lane < KP) {
-            // running sum of g: lane t adds g_0..g_t in order
-            float G = 0.f;
-#pragma unroll
-            for (int s4 = 0; s4 < KP; s4 += 4) {
-                const float4 g4 = *reinterpret_cast<const float4*>(&sm.g[s4]);
-                if (s4 + 0 <= lane) G += g4.x;
-                if (s4 + 1 <= lane) G += g4.y;
-                if (s4 + 2 <= lane) G += g4.z;
-                if (s4 + 3 <= lane) G += g4.w;
-            }
-            Gw[lane] = G;
-            if (wa) {
-                sm.tok[lane].y = __expf(G);
-                sm.gam[lane] = __expf(sm.g[lane]);
-            }
-        }
-        f32x4_t kk[TB][TB], qk[TB][TB];
 #pragma unroll
         for (int tm = 0; tm < TB; ++tm)
 #pragma unroll
-            for (int tn = 0; tn <= tm; ++tn) {
-                if (wa || tn == tm) kk[tm][tn] = gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.k, sm.k, tm, tn, lane);
-                if (!wa) qk[tm][tn] = gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.q, sm.k, tm, tn, lane);
-            }
+            for (int tn = 0; tn < TB; ++tn) {
+                const int s2 = tn * 16 + n16;
+                if (tn > tm) {
+                    // tiles above the diagonal are zero
 #pragma unroll
-        for (int tm = 0; tm < TB; ++tm) {
-            f32x4_t qq = {0.f, 0.f, 0.f, 0.f};
-            if (!wa) qq = gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.q, sm.q, tm, tm, lane);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (m0 + e == n16) {
-                    const int t = tm * 16 + n16;
-                    // padded tokens keep k^ = q^ = 0 (never 0 * 1/sqrt(0))
-                    const float rk = t < K ? __builtin_amdgcn_rsqf(kk[tm][tm][e] + a.eps) : 0.0f;
-                    if (wa) {
-                        sm.tok[t].z = rk;
-                    } else {
-                        rkw[t] = rk;
-                        sm.tok[t].w = t < K ? __builtin_amdgcn_rsqf(qq[e] + a.eps) : 0.0f;
+                    for (int e = 0; e < 4; ++e) {
+                        if (wa) sm.A[tm * 16 + m0 + e][s2] = 0.f;
+                        else sm.M[tm * 16 + m0 + e][s2] = 0.f;
                     }
+                    continue;
                 }
-        }
-        // LDS accesses of one wave complete in order: wait for this wave's
-        // writes, then read them back from other lanes
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-        __builtin_amdgcn_wave_barrier();
-        const float* rkr = wa ? nullptr : rkw;
+                const f32x4_t d = wa ? gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.k, sm.k, tm, tn, lane)
+                                     : gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.q, sm.k, tm, tn, lane);
+                const float Gs = sm.Gv[s2], rks = sm.tok[s2].z;
 #pragma unroll
-        for (int tm = 0; tm < TB; ++tm)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = tm * 16 + m0 + e;
-                const float Gt = Gw[t];
-                const float4 tt = sm.tok[t];
-                const float rowf = wa ? tt.x * tt.z : tt.w;        // beta_t / |k_t|  or  1 / |q_t|
-#pragma unroll
-                for (int tn = 0; tn < TB; ++tn) {
-                    const int s2 = tn * 16 + n16;
-                    float val = 0.f;
-                    if (tn <= tm && s2 <= t) {
-                        const float dec = __expf(Gt - Gw[s2]);
-                        if (wa) {
-                            if (s2 < t) val = dec * kk[tm][tn][e] * rowf * sm.tok[s2].z;
-                        } else {
-                            val = dec * qk[tm][tn][e] * rowf * rkr[s2];
-                        }
-                    }
-                    if (wa) sm.A[t][s2] = val;
-                    else sm.M[t][s2] = val;
+                for (int e = 0; e < 4; ++e) {
+                    const int t = tm * 16 + m0 + e;
+                    const float4 tt = sm.tok[t];
+                    const float dec = __expf(fminf(sm.Gv[t] - Gs, 0.f));
+                    if (wa) sm.A[t][s2] = s2 < t ? tt.x * tt.z * rks * dec * d[e] : 0.f;
+                    else sm.M[t][s2] = s2 <= t ? tt.w * rks * dec * d[e] : 0.f;
                 }
             }
     } else {
