@@ -170,6 +170,34 @@ int gdn_rollback(const int32_t *accept, int K,
                  int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void *stream);
 
 /*
+ * gdn_rollback_conv_step -- gdn_rollback of the previous verify window
+ * followed by gdn_conv_step of the next tokens, in one launch: in a verify
+ * loop the rollback of step i and the conv step of step i+1 touch the same
+ * layer state back to back (the conv-state intermediates and snapshot
+ * rollback of the pages cited above), and one launch saves the fixed cost of
+ * the second.  The results are exactly those of the two calls
+ *   gdn_rollback(accept, K_prev, S_in, H, S_out, hist, win_prev, ...);
+ *   gdn_conv_step(x, w, hist, y, win, B, T, C, W, ...);
+ * (bit for bit): the conv history is taken from win_prev rows a..a+W-2,
+ * which is what the rollback writes into hist, and hist ends as the last W-1
+ * rows of the new window.
+ *
+ *   accept [B] int32 (device), K_prev, S_in, H, S_out: as gdn_rollback
+ *           (K_prev is the previous window length, H [B][K_prev-1][Hv][dv][dk])
+ *   win_prev [B][W-1+K_prev][C] io_dtype: the previous window (input)
+ *   x [B][T][C], w [C][W] float, y [B][T][C], win [B][W-1+T][C]: as
+ *           gdn_conv_step (win is required here)
+ *   hist [B][W-1][C]: output only
+ *   Every output (S_out, hist, y, win) must be disjoint from every input
+ *   and from the other outputs: keep two window buffers and alternate them.
+ */
+int gdn_rollback_conv_step(const int32_t *accept, int K_prev, const float *S_in,
+                           const float *H, float *S_out, const void *win_prev,
+                           const void *x, const float *w, void *hist, void *y, void *win,
+                           int B, int Hv, int dv, int dk, int T, int C, int W,
+                           int io_dtype, void *stream);
+
+/*
  * gdn_prefill_chunked -- the same recurrence over a long prompt, processed
  * in chunks of `chunk` tokens, writing only the final state and the outputs.
  *

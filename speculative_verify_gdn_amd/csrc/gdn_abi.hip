@@ -186,6 +186,47 @@ int gdn_rollback(const int32_t* accept, int K, const float* S_in, const float* H
     return launch_status(gdn::launch_rollback(a, (hipStream_t)stream), fn);
 }
 
+int gdn_rollback_conv_step(const int32_t* accept, int K_prev, const float* S_in, const float* H, float* S_out,
+                           const void* win_prev, const void* x, const float* w, void* hist, void* y, void* win,
+                           int B, int Hv, int dv, int dk, int T, int C, int W, int io_dtype, void* stream)
+{
+    const char* fn = "gdn_rollback_conv_step";
+    REQUIRE(B >= 0, GDN_EINVAL, "%s: B = %d < 0", fn, B);
+    REQUIRE(K_prev >= 1, GDN_EINVAL, "%s: K_prev = %d < 1", fn, K_prev);
+    REQUIRE(T >= 1, GDN_EINVAL, "%s: T = %d < 1", fn, T);
+    REQUIRE(C >= 1, GDN_EINVAL, "%s: C = %d < 1", fn, C);
+    REQUIRE(Hv >= 1 && dv >= 1 && dk >= 1, GDN_EINVAL, "%s: bad state shape", fn);
+    REQUIRE(((long long)Hv * dv * dk) % 4 == 0, GDN_EUNSUPPORTED, "%s: Hv*dv*dk must be a multiple of 4", fn);
+    REQUIRE(W >= 2 && W <= 8, GDN_EUNSUPPORTED, "%s: W = %d not in 2..8", fn, W);
+    REQUIRE(valid_dtype(io_dtype), GDN_EINVAL, "%s: bad dtype code %d", fn, io_dtype);
+    REQUIRE((long long)B * (T + K_prev) * C < (1LL << 40), GDN_EUNSUPPORTED, "%s: problem too large", fn);
+    REQUIRE(T <= 65535 * 16, GDN_EUNSUPPORTED, "%s: T = %d too large", fn, T);
+    REQUIRE(B <= 65535, GDN_EUNSUPPORTED, "%s: B = %d too large", fn, B);
+    if (B == 0) return ok();
+    REQUIRE(accept && S_in && S_out && win_prev && x && w && hist && y && win, GDN_EINVAL,
+            "%s: null pointer (only H may be NULL, and only when K_prev == 1)", fn);
+    REQUIRE(H || K_prev == 1, GDN_EINVAL, "%s: H is required when K_prev > 1", fn);
+    REQUIRE(S_in != S_out, GDN_EINVAL, "%s: S_out must not be S_in (the pre-window state is needed)", fn);
+    REQUIRE(aligned16(accept) && aligned16(S_in) && aligned16(S_out) && (!H || aligned16(H)) && aligned16(win_prev) &&
+                aligned16(x) && aligned16(w) && aligned16(hist) && aligned16(y) && aligned16(win),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    const size_t st = (size_t)Hv * dv * dk * 4, es = elem_size(io_dtype);
+    const Span ssi{S_in, B * st}, sso{S_out, B * st}, sH{H, H ? (size_t)B * (K_prev - 1) * st : 0},
+        swp{win_prev, (size_t)B * (W - 1 + K_prev) * C * es}, sx{x, (size_t)B * T * C * es},
+        sw{w, (size_t)C * W * 4}, sh{hist, (size_t)B * (W - 1) * C * es}, sy{y, (size_t)B * T * C * es},
+        swin{win, (size_t)B * (W - 1 + T) * C * es}, sacc{accept, (size_t)B * 4};
+    const Span ins[] = {ssi, sH, swp, sx, sw, sacc};
+    const Span outs[] = {sso, sh, sy, swin};
+    for (const Span& o : outs)
+        for (const Span& i : ins) REQUIRE(!overlap(o, i), GDN_EINVAL, "%s: an output overlaps an input", fn);
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            REQUIRE(!overlap(outs[i], outs[j]), GDN_EINVAL, "%s: two outputs overlap", fn);
+    gdn::RollConvArgs a{accept, K_prev, S_in, H, S_out, (long long)Hv * dv * dk, win_prev, x, w, hist, y, win,
+                        B, T, C, W};
+    return launch_status(gdn::launch_rollback_conv(a, io_dtype == GDN_BF16, (hipStream_t)stream), fn);
+}
+
 int gdn_prefill_chunked(const void* qkv, const void* beta_raw, const void* alpha, const float* dt_bias,
                         const float* A_log, const float* S_in, float* S_out, void* o, int B, int T, int chunk,
                         int Hk, int Hv, int dk, int dv, int in_dtype, int o_dtype, float l2_eps, void* stream)

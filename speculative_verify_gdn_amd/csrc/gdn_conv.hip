@@ -194,6 +194,121 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(ConvArgs a)
     if (hist_writer) store_row8<BF16>(a.hist, hb + (size_t)tl * C + c0, nch, vec, nh);
 }
 
+// The rollback of the previous window fused with the conv step of the next
+// tokens: exactly gdn_rollback followed by gdn_conv_step, in one launch.
+// x of the grid: first the state slabs of the rollback (one float4 per
+// thread), then the conv tiles (channel group tile, token tile); y: sequence.
+// The conv history is read from the previous window (rows a .. a+W-2, which is
+// what the rollback restores into hist) and hist is only written, so no
+// workgroup waits for another.
+template <bool BF16, int W>
+__global__ __launch_bounds__(kThreads) void rollback_conv_kernel(RollConvArgs a, int state_blocks, int cgx)
+{
+    const int b = blockIdx.y;
+    int acc = a.accept[b];
+    acc = acc < 0 ? 0 : (acc > a.Kp ? a.Kp : acc);
+
+    if ((int)blockIdx.x < state_blocks) {
+        if (acc == a.Kp) return;
+        const float* src = acc == 0 ? a.S_in + (size_t)b * a.state_elems
+                                    : a.H + ((size_t)b * (a.Kp - 1) + (acc - 1)) * a.state_elems;
+        float* dst = a.S_out + (size_t)b * a.state_elems;
+        const long long e = ((long long)blockIdx.x * kThreads + threadIdx.x) * 4;
+        if (e < a.state_elems)
+            __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + e)),
+                                        reinterpret_cast<f32x4_t*>(dst + e));
+        return;
+    }
+
+    const int bx = blockIdx.x - state_blocks;
+    const int g = threadIdx.x % kGroups, tl = threadIdx.x / kGroups;
+    const int c0 = ((bx % cgx) * kGroups + g) * kCh;
+    const int t = (bx / cgx) * kTok + tl;
+    const int T = a.T, C = a.C;
+    const bool active = c0 < C && t < T;
+    const int nch = c0 < C ? min(kCh, C - c0) : 0;
+    const bool vec = (nch == kCh) && ((C & 3) == 0);
+    const size_t xb = (size_t)b * T * C;
+    const size_t pb = ((size_t)b * (W - 1 + a.Kp) + acc) * C;   // previous window row acc
+
+    // new window row r is previous window row acc + r for r < W-1, else token r-(W-1)
+    float col[W][kCh];
+    float wt[kCh][W];
+    if (active) {
+#pragma unroll
+        for (int jj = 0; jj < W; ++jj) {
+            const int row = t + jj;
+            if (row < W - 1) load_row8<BF16>(a.win_prev, pb + (size_t)row * C + c0, nch, vec, col[jj]);
+            else load_row8<BF16>(a.x, xb + (size_t)(row - (W - 1)) * C + c0, nch, vec, col[jj]);
+        }
+        if (vec) {
+            const float4* wp = reinterpret_cast<const float4*>(a.w + (size_t)c0 * W);
+            float wl[kCh * W];
+#pragma unroll
+            for (int q4 = 0; q4 < kCh * W / 4; ++q4) {
+                const float4 f = wp[q4];
+                wl[4 * q4 + 0] = f.x; wl[4 * q4 + 1] = f.y; wl[4 * q4 + 2] = f.z; wl[4 * q4 + 3] = f.w;
+            }
+#pragma unroll
+            for (int e = 0; e < kCh; ++e)
+#pragma unroll
+                for (int jj = 0; jj < W; ++jj) wt[e][jj] = wl[e * W + jj];
+        } else {
+#pragma unroll
+            for (int e = 0; e < kCh; ++e) {
+                const int ce = c0 + e < C ? c0 + e : C - 1;
+#pragma unroll
+                for (int jj = 0; jj < W; ++jj) wt[e][jj] = a.w[(size_t)ce * W + jj];
+            }
+        }
+    }
+    // first token tile, threads tl < W-1: window row tl (the restored history)
+    // and the new history (window row T + tl)
+    if (bx / cgx == 0 && tl < W - 1 && c0 < C) {
+        float oh[kCh], nh[kCh];
+        load_row8<BF16>(a.win_prev, pb + (size_t)tl * C + c0, nch, vec, oh);
+        const int row = T + tl;
+        if (row < W - 1) load_row8<BF16>(a.win_prev, pb + (size_t)row * C + c0, nch, vec, nh);
+        else load_row8<BF16>(a.x, xb + (size_t)(row - (W - 1)) * C + c0, nch, vec, nh);
+        store_row8<BF16>(a.win, (size_t)b * (W - 1 + T) * C + (size_t)tl * C + c0, nch, vec, oh);
+        store_row8<BF16>(a.hist, (size_t)b * (W - 1) * C + (size_t)tl * C + c0, nch, vec, nh);
+    }
+    if (active) {
+        float out[kCh];
+#pragma unroll
+        for (int e = 0; e < kCh; ++e) {
+            float acc2 = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < W; ++jj) acc2 = __builtin_fmaf(wt[e][jj], col[jj][e], acc2);
+            out[e] = conv_silu(acc2);
+        }
+        store_row8<BF16>(a.y, xb + (size_t)t * C + c0, nch, vec, out);
+        store_row8<BF16>(a.win, (size_t)b * (W - 1 + T) * C + (size_t)(t + W - 1) * C + c0, nch, vec, col[W - 1]);
+    }
+}
+
+template <bool BF16>
+hipError_t launch_rc(const RollConvArgs& a, hipStream_t s)
+{
+    const int state_blocks = (int)((a.state_elems + (long long)kThreads * 4 - 1) / ((long long)kThreads * 4));
+    const int groups = (a.C + kCh - 1) / kCh;
+    const int cgx = (groups + kGroups - 1) / kGroups;
+    const int tiles = cgx * ((a.T + kTok - 1) / kTok);
+    dim3 grid(state_blocks + tiles, a.B);
+    dim3 block(kThreads);
+    switch (a.W) {
+    case 2: rollback_conv_kernel<BF16, 2><<<grid, block, 0, s>>>(a, state_blocks, cgx); break;
+    case 3: rollback_conv_kernel<BF16, 3><<<grid, block, 0, s>>>(a, state_blocks, cgx); break;
+    case 4: rollback_conv_kernel<BF16, 4><<<grid, block, 0, s>>>(a, state_blocks, cgx); break;
+    case 5: rollback_conv_kernel<BF16, 5><<<grid, block, 0, s>>>(a, state_blocks, cgx); break;
+    case 6: rollback_conv_kernel<BF16, 6><<<grid, block, 0, s>>>(a, state_blocks, cgx); break;
+    case 7: rollback_conv_kernel<BF16, 7><<<grid, block, 0, s>>>(a, state_blocks, cgx); break;
+    case 8: rollback_conv_kernel<BF16, 8><<<grid, block, 0, s>>>(a, state_blocks, cgx); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <bool BF16>
 hipError_t launch_w(const ConvArgs& a, hipStream_t s)
 {
@@ -218,6 +333,11 @@ hipError_t launch_w(const ConvArgs& a, hipStream_t s)
 hipError_t launch_conv_step(const ConvArgs& a, bool bf16, hipStream_t s)
 {
     return bf16 ? launch_w<true>(a, s) : launch_w<false>(a, s);
+}
+
+hipError_t launch_rollback_conv(const RollConvArgs& a, bool bf16, hipStream_t s)
+{
+    return bf16 ? launch_rc<true>(a, s) : launch_rc<false>(a, s);
 }
 
 }  // namespace gdn

@@ -43,6 +43,23 @@ struct RollbackArgs {
     int C, W, elem_bytes;
 };
 
+// rollback of the previous window fused with the conv step of the next tokens
+struct RollConvArgs {
+    const int32_t* accept;   // [B], accept lengths of the previous window
+    int Kp;                  // previous window length
+    const float* S_in;       // [B][Hv][dv][dk], state before the previous window
+    const float* H;          // [B][Kp-1][Hv][dv][dk]
+    float* S_out;            // [B][Hv][dv][dk]
+    long long state_elems;   // Hv*dv*dk
+    const void* win_prev;    // [B][W-1+Kp][C], previous conv window
+    const void* x;           // [B][T][C]
+    const float* w;          // [C][W]
+    void* hist;              // [B][W-1][C], written only
+    void* y;                 // [B][T][C]
+    void* win;               // [B][W-1+T][C]
+    int B, T, C, W;
+};
+
 struct PrefillArgs {
     const void* qkv;       // [B][T][C]
     const void* beta_raw;  // [B][T][Hv]
@@ -59,6 +76,7 @@ struct PrefillArgs {
 hipError_t launch_conv_step(const ConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
 hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
+hipError_t launch_rollback_conv(const RollConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
 hipError_t launch_prefill_wy(const PrefillArgs& a, bool o_bf16, hipStream_t s);
 

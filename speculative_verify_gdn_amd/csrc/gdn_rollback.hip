@@ -10,9 +10,11 @@
 //   hist[b][j] <- win[b][a+j],  j < W-1
 // The accept lengths are read on the device, so the copy needs no host sync.
 //
-// Grid: x covers one sequence's state in 16 KB slabs (256 threads x 4 float4)
-// followed by its conv rows; y is the sequence.  Workgroups of sequences with
-// a == K return at once.
+// Grid: x covers one sequence's state in 4 KB slabs (256 threads x 1 float4,
+// loaded and stored past the caches) followed by its conv rows; y is the
+// sequence.  State workgroups of sequences with a == K return at once; the conv
+// rows are copied for every a (for a == K they already hold win[K..] after an
+// in-place conv step, so the copy is a no-op there).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -20,8 +22,7 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;
-constexpr long long kSlab = (long long)kThreads * kVecPerThread * 4;  // floats per workgroup
+constexpr long long kSlab = (long long)kThreads * 4;  // floats per workgroup
 
 __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int state_blocks)
 {
@@ -29,25 +30,16 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int 
     const int K = a.K;
     int acc = a.accept[b];
     acc = acc < 0 ? 0 : (acc > K ? K : acc);
-    if (acc == K) return;
 
     if ((int)blockIdx.x < state_blocks) {
+        if (acc == K) return;
         const float* src = acc == 0 ? a.S_in + (size_t)b * a.state_elems
                                     : a.H + ((size_t)b * (K - 1) + (acc - 1)) * a.state_elems;
         float* dst = a.S_out + (size_t)b * a.state_elems;
-        const long long base = (long long)blockIdx.x * kSlab;
-        // loads clamped into range (branch-free, all in flight together), stores guarded
-        f32x4_t v[kVecPerThread];
-#pragma unroll
-        for (int j = 0; j < kVecPerThread; ++j) {
-            const long long e = base + ((long long)j * kThreads + threadIdx.x) * 4;
-            v[j] = load_f4(src + (e < a.state_elems ? e : a.state_elems - 4));
-        }
-#pragma unroll
-        for (int j = 0; j < kVecPerThread; ++j) {
-            const long long e = base + ((long long)j * kThreads + threadIdx.x) * 4;
-            if (e < a.state_elems) store_f4<false>(dst + e, v[j]);
-        }
+        const long long e = (long long)blockIdx.x * kSlab + (long long)threadIdx.x * 4;
+        if (e < a.state_elems)
+            __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + e)),
+                                        reinterpret_cast<f32x4_t*>(dst + e));
         return;
     }
 

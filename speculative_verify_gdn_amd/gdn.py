@@ -20,7 +20,8 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
 GDN_F32, GDN_BF16 = 0, 1
-EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked")
+EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked",
+           "gdn_rollback_conv_step")
 
 
 class GdnError(RuntimeError):
@@ -50,6 +51,7 @@ def load(path: str = LIB_PATH):
         lib.gdn_verify.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
         lib.gdn_rollback.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
         lib.gdn_prefill_chunked.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P]
+        lib.gdn_rollback_conv_step.argtypes = [P, I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
         for name in EXPORTS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "gdn_last_error" else I
         _lib = lib
@@ -123,6 +125,18 @@ def rollback(accept, K, S_in, H, S_out, hist=None, win=None, stream=None):
         W, C, io = 2, 1, GDN_F32
     _check(load().gdn_rollback(_p(accept), int(K), _p(S_in), _p(H), _p(S_out), _p(hist), _p(win),
                                B, Hv, dv, dk, C, W, io, _stream(stream)))
+
+
+def rollback_conv_step(accept, K_prev, S_in, H, S_out, win_prev, x, w, hist, y, win, stream=None):
+    """gdn_rollback_conv_step: gdn_rollback of the previous window (accept, K_prev, S_in, H, S_out, win_prev)
+    then gdn_conv_step of x [B][T][C] into y and win [B][W-1+T][C], in one launch; hist is written only."""
+    _dev(accept, S_in, H, S_out, win_prev, x, w, hist, y, win)
+    B, Hv, dv, dk = S_in.shape
+    _, T, C = x.shape
+    W = w.shape[1]
+    _check(load().gdn_rollback_conv_step(_p(accept), int(K_prev), _p(S_in), _p(H), _p(S_out), _p(win_prev), _p(x),
+                                         _p(w), _p(hist), _p(y), _p(win), B, Hv, dv, dk, T, C, W, _dtype(x),
+                                         _stream(stream)))
 
 
 def prefill_chunked(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, o, Hk, chunk=64, eps=1e-6, stream=None):

@@ -145,6 +145,37 @@ def test_rollback_k1_without_capture_and_empty_batch(lib):
     assert rollback_call(lib, B=0) == gdn.GDN_OK
 
 
+def rollconv_call(lib, **kw):
+    a = dict(acc=p(0), Kp=4, S_in=p(1), H=p(2), S_out=p(6), win_prev=p(9), x=p(10), w=p(11), hist=p(12), y=p(13),
+             win=p(14), B=1, Hv=2, dv=32, dk=32, T=4, C=192, W=4, io=gdn.GDN_BF16)
+    a.update(kw)
+    return lib.gdn_rollback_conv_step(a["acc"], a["Kp"], a["S_in"], a["H"], a["S_out"], a["win_prev"], a["x"],
+                                      a["w"], a["hist"], a["y"], a["win"], a["B"], a["Hv"], a["dv"], a["dk"],
+                                      a["T"], a["C"], a["W"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(acc=None), gdn.GDN_EINVAL),
+    (dict(Kp=0), gdn.GDN_EINVAL),
+    (dict(T=0), gdn.GDN_EINVAL),
+    (dict(H=None), gdn.GDN_EINVAL),              # needed for K_prev > 1
+    (dict(win=None), gdn.GDN_EINVAL),            # the new window is required
+    (dict(S_out=p(1)), gdn.GDN_EINVAL),          # the pre-window state is needed
+    (dict(win=p(9)), gdn.GDN_EINVAL),            # new window on the previous one
+    (dict(y=p(10)), gdn.GDN_EINVAL),             # y on x
+    (dict(hist=p(13)), gdn.GDN_EINVAL),          # two outputs on each other
+    (dict(W=9), gdn.GDN_EUNSUPPORTED),
+    (dict(io=7), gdn.GDN_EINVAL),
+    (dict(hist=ctypes.c_void_p(A + 12 * MB + 4)), gdn.GDN_EINVAL),  # misaligned
+])
+def test_rollback_conv_rejects(lib, kw, code):
+    assert rollconv_call(lib, **kw) == code
+
+
+def test_rollback_conv_empty_batch_is_ok(lib):
+    assert rollconv_call(lib, B=0) == gdn.GDN_OK
+
+
 def prefill_call(lib, **kw):
     a = dict(qkv=p(0), beta=p(1), alpha=p(2), dt=p(3), alog=p(4), S_in=p(5), S_out=p(6), o=p(8), B=1, T=100,
              chunk=64, Hk=2, Hv=2, dk=32, dv=32, ind=gdn.GDN_BF16, od=gdn.GDN_BF16, eps=1e-6)

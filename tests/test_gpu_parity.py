@@ -262,6 +262,65 @@ def test_rollback_bit_exact(name):
     assert np.array_equal(hg, hist_ref)
 
 
+# gdn_rollback_conv_step: the rollback of a previous window and the conv step of the
+# next tokens in one launch; against the oracle's byte-copy rollback followed by its
+# same-precision conv, bit for bit, and against the two separate GPU calls.
+# (name, sizes, previous window K_prev, new tokens T)
+ROLLCONV_CASES = [
+    ("verify16", dict(Hk=2, Hv=6, B=3), 16, 16),
+    ("tiny", dict(B=3), 4, 4),                                    # fp32
+    ("verify16", dict(Hk=2, Hv=6, B=3, W=2), 16, 1),              # decode-size new window
+    ("tiny", dict(Hk=1, Hv=3, dk=32, dv=40, B=3), 7, 2),          # C = 184 (ragged), T < W-1
+    ("verify16", dict(Hk=2, Hv=6, B=3, W=8), 16, 3),              # T < W-1
+]
+
+
+@pytest.mark.parametrize("name,over,Kp,Tn", ROLLCONV_CASES)
+def test_rollback_conv_step_bit_exact(name, over, Kp, Tn):
+    wl = synth.small(name, T=Kp, **over)
+    say("rollback+conv", name, over, "K_prev=%d T=%d C=%d" % (Kp, Tn, wl.C))
+    io = torch.bfloat16 if wl.bf16 else torch.float32
+    inp = synth.make_inputs(wl, seed=21)
+    B, C, W = wl.B, wl.C, wl.W
+    g = torch.Generator().manual_seed(22)
+    acc = torch.tensor([0, Kp, Kp // 2][:B], dtype=torch.int32)
+    win_prev = torch.randn(B, W - 1 + Kp, C, generator=g).to(io)
+    H = torch.randn(B, Kp - 1, wl.Hv, wl.dv, wl.dk, generator=g) * 0.1 if Kp > 1 else None
+    S_out0 = torch.randn(B, wl.Hv, wl.dv, wl.dk, generator=g)
+    x = torch.randn(B, Tn, C, generator=g).to(io)
+    hist0 = torch.randn(B, W - 1, C, generator=g).to(io)   # overwritten: only written by the call
+
+    def bits(t):
+        return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.numpy().view(np.int32)
+
+    # oracle: byte-copy rollback, then the same-precision conv from the restored history
+    S_ref = S_out0.numpy().copy()
+    hist_r = bits(hist0.clone()).copy()
+    oracle.rollback(acc.numpy(), Kp, inp["S_in"].numpy(), H.numpy() if H is not None else None, S_ref,
+                    win=bits(win_prev), hist=hist_r)
+    hist_restored = torch.from_numpy(hist_r).view(io) if wl.bf16 else torch.from_numpy(hist_r.view(np.float32))
+    y_ref, hist_ref, win_ref = oracle.conv_step_f32(x.float().numpy(), inp["w"].numpy(),
+                                                    hist_restored.float().numpy(), round_bf16=wl.bf16)
+
+    d_S_in, d_H, d_w = dev(inp["S_in"]), dev(H) if H is not None else None, dev(inp["w"])
+    S_out, hist = dev(S_out0), dev(hist0)
+    y = torch.empty(B, Tn, C, dtype=io, device="cuda")
+    win = torch.empty(B, W - 1 + Tn, C, dtype=io, device="cuda")
+    gdn.rollback_conv_step(dev(acc), Kp, d_S_in, d_H, S_out, dev(win_prev), dev(x), d_w, hist, y, win)
+    torch.cuda.synchronize()
+    assert np.array_equal(S_out.cpu().numpy(), S_ref)
+    for got, ref, what in ((y, y_ref, "y"), (hist, hist_ref, "hist"), (win, win_ref, "win")):
+        assert np.array_equal(got.float().cpu().numpy().view(np.uint32), ref.view(np.uint32)), what
+
+    # the two separate calls give the same bytes
+    S2, hist2 = dev(S_out0), dev(hist0)
+    y2, win2 = torch.empty_like(y), torch.empty_like(win)
+    gdn.rollback(dev(acc), Kp, d_S_in, d_H, S2, hist2, dev(win_prev))
+    gdn.conv_step(dev(x), d_w, hist2, y2, win2)
+    torch.cuda.synchronize()
+    assert torch.equal(S2, S_out) and torch.equal(y2, y) and torch.equal(win2, win) and torch.equal(hist2, hist)
+
+
 def test_rollback_equals_rerun_of_accepted_prefix():
     """State after rollback(a) matches a fresh verify of the first a tokens (oracle and GPU)."""
     wl = synth.WORKLOADS["verify16"]
