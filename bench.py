@@ -208,6 +208,9 @@ def main():
     ap.add_argument("--workload", default="verify16")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled (0: enough to exceed 2x the MALL)")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of HIP graphs")
+    ap.add_argument("--three-kernel", action="store_true",
+                    help="step as conv_step -> verify -> rollback (three launches) instead of "
+                         "rollback_conv_step -> verify")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
@@ -255,6 +258,7 @@ def main():
         d = {k: v.to(dev) for k, v in inp.items()}
         d["y"] = torch.empty_like(d["x"])
         d["win"] = torch.empty(wl.B, wl.W - 1 + wl.T, wl.C, dtype=d["x"].dtype, device=dev)
+        d["win_prev"] = torch.empty_like(d["win"])   # the previous step's window (fused step)
         d["S_out"] = torch.empty_like(d["S_in"])
         d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev) if wl.T > 1 else None
         d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
@@ -276,10 +280,24 @@ def main():
     def rollback(d):
         gdn.rollback(d["accept"], wl.T, d["S_in"], d["H"], d["S_out"], d["hist"], d["win"])
 
-    def step(d):
-        conv(d)
-        verify(d)
-        rollback(d)
+    def rollback_conv(d):
+        # the rollback of this set's previous window, then this step's conv, in one launch
+        gdn.rollback_conv_step(d["accept"], wl.T, d["S_in"], d["H"], d["S_out"], d["win_prev"], d["x"], d["w"],
+                               d["hist"], d["y"], d["win"])
+
+    if args.three_kernel:
+        def step(d):
+            conv(d)
+            verify(d)
+            rollback(d)
+    else:
+        def step(d):
+            rollback_conv(d)
+            verify(d)
+
+    # a valid previous window for the fused step: one conv step into win_prev
+    for d in sets:
+        gdn.conv_step(d["x"], d["w"], d["hist"], d["y"], d["win_prev"])
 
     # ---------------------------------------------------------------- warmup
     for s in range(args.warmup):
@@ -367,6 +385,7 @@ def main():
     t_ver = kernel_us(verify)
     t_conv = kernel_us(conv)
     t_rb = kernel_us(rollback)
+    t_rc = kernel_us(rollback_conv)
 
     vb = verify_bytes(wl)
     achieved = vb / (t_ver * 1e-6) / 1e9
@@ -390,7 +409,9 @@ def main():
         "config": {
             "workload": wl.name, "B": wl.B, "K": wl.T, "Hk": wl.Hk, "Hv": wl.Hv, "dk": wl.dk, "dv": wl.dv,
             "C": wl.C, "conv_width": wl.W, "io_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
-            "step": "conv_step + verify(capture) + rollback", "buffer_sets": R,
+            "step": ("conv_step + verify(capture) + rollback" if args.three_kernel else
+                     "rollback_conv_step (rollback of the previous window + conv_step, one launch) + verify(capture)"),
+            "buffer_sets": R,
             "working_set_MB": round(R * set_bytes / 2 ** 20, 1), "launch": "eager" if args.eager else ("hip_graph, %d steps per graph" % per_graph),
         },
         "roofline": {
@@ -407,6 +428,7 @@ def main():
             "verify_us": round(t_ver, 3),
             "conv_us": round(t_conv, 3),
             "rollback_us": round(t_rb, 3),
+            "rollback_conv_us": round(t_rc, 3),
             "conv_GBs": round(conv_bytes(wl) / (t_conv * 1e-6) / 1e9, 1),
             "rollback_GBs": round(mean_rb_bytes / (t_rb * 1e-6) / 1e9, 1),
             "verify_only_tokens_per_s": round(tokens / (t_ver * 1e-6), 1),
