@@ -37,9 +37,9 @@
 //      instructions on the unsplit values;
 //   3. per row: the forward substitution for u_t is shared by the row's lanes
 //      (lane j owns token j, each finished u_t is broadcast with v_readlane),
-//      which also gives o_t; then every lane streams H_t = gamma_t H_{t-1} +
-//      u_t k^_t with one 16-byte store per token -- the bulk of the bytes of
-//      the whole step.
+//      which also gives o_t; as soon as u_t is known every lane streams
+//      H_t = gamma_t H_{t-1} + u_t k^_t with one 16-byte store -- the bulk of
+//      the bytes of the whole step.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -375,13 +375,33 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     }
     __syncthreads();
 
-    // ---- 3a. u = (I + A)^{-1} b with b_t = beta_t (v_t - e^{G_t} S_in k^_t), and o_t.
-    // Lane j of a row owns token j: it forms b_j, keeps row j of A and of M in
-    // registers, and at step t the owner of token t has its u_t final; every
-    // lane reads it with v_readlane (per row of the wave) and updates its own
-    // partial sum.  u_t ends up in scalar registers for the stream.
-    float us[RPW][KMAX];                         // u_t of each row of this wave (wave-uniform)
+    // ---- 3. u = (I + A)^{-1} b with b_t = beta_t (v_t - e^{G_t} S_in k^_t), o_t, and the
+    // stream of the states H_t = gamma_t H_{t-1} + (u_t / |k_t|) k_t.  A state leaves as
+    // soon as its u_t is known, so the stores of the first tokens overlap the rest of
+    // the substitution.
+    float* Hrow = a.H ? a.H + ((size_t)b * (K - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
+    const size_t Hstep = (size_t)Hv * SD;
+    auto stream_token = [&](int t, float ut) {
+        const float gm = sm.gam[t];
+        const float cu = ut * sm.tok[t].z;
+        const float4 kx = lds4<IN_BF16>(&sm.k[t][c]);
+        S[0] = __builtin_fmaf(cu, kx.x, gm * S[0]);
+        S[1] = __builtin_fmaf(cu, kx.y, gm * S[1]);
+        S[2] = __builtin_fmaf(cu, kx.z, gm * S[2]);
+        S[3] = __builtin_fmaf(cu, kx.w, gm * S[3]);
+        if (live) {
+            if (t < K - 1) {
+                if (Hrow) store_f4<NT>(Hrow + (size_t)t * Hstep, S);
+            } else if (t == K - 1) {
+                store_f4<false>(a.S_out + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S);
+            }
+        }
+    };
     if constexpr (KMAX <= LPR) {
+        // Lane j of a row owns token j: it forms b_j, keeps row j of A and of M in
+        // registers, and at step t the owner of token t has its u_t final; every
+        // lane reads it with v_readlane (per row of the wave), updates its own
+        // partial sum and streams H_t.
         const int tj = j < KMAX ? j : KMAX - 1;  // this lane's token (clamped; lanes past K carry zeros)
         const bool own = j < K;
         const float4 tt = sm.tok[tj];            // beta, e^{G}, 1/|k|, 1/|q|
@@ -406,12 +426,13 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             float mine = 0.f;
 #pragma unroll
             for (int r2 = 0; r2 < RPW; ++r2) {
-                us[r2][t] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), r2 * LPR + t));
-                if (r2 == wr) mine = us[r2][t];
+                const float ur = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), r2 * LPR + t));
+                if (r2 == wr) mine = ur;
             }
             // A[j][t] = 0 for t >= j, so finished lanes keep their value
             part = __builtin_fmaf(-arow[t], mine, part);
             ot = __builtin_fmaf(mrow[t], mine, ot);  // M[j][t] = 0 for t > j
+            stream_token(t, mine);
         }
         if (own && live) store1<O_BF16>(a.o, (((size_t)b * K + j) * Hv + h) * dv + i, ot);
     } else {
@@ -437,34 +458,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             }
         }
 #pragma unroll
-        for (int t = 0; t < KMAX; ++t)
-#pragma unroll
-            for (int r2 = 0; r2 < RPW; ++r2) us[r2][t] = u[t];
-    }
-
-    // ---- 3b. stream the states: H_t = gamma_t H_{t-1} + (u_t / |k_t|) k_t
-    float* Hrow = a.H ? a.H + ((size_t)b * (K - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
-    const size_t Hstep = (size_t)Hv * SD;
-#pragma unroll
-    for (int t = 0; t < KMAX; ++t) {
-        const float gm = sm.gam[t];
-        float ut = us[0][t];
-#pragma unroll
-        for (int r2 = 1; r2 < RPW; ++r2)
-            if (lane / LPR == r2) ut = us[r2][t];
-        const float cu = ut * sm.tok[t].z;
-        const float4 kx = lds4<IN_BF16>(&sm.k[t][c]);
-        S[0] = __builtin_fmaf(cu, kx.x, gm * S[0]);
-        S[1] = __builtin_fmaf(cu, kx.y, gm * S[1]);
-        S[2] = __builtin_fmaf(cu, kx.z, gm * S[2]);
-        S[3] = __builtin_fmaf(cu, kx.w, gm * S[3]);
-        if (live) {
-            if (t < K - 1) {
-                if (Hrow) store_f4<NT>(Hrow + (size_t)t * Hstep, S);
-            } else if (t == K - 1) {
-                store_f4<false>(a.S_out + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S);
-            }
-        }
+        for (int t = 0; t < KMAX; ++t) stream_token(t, u[t]);
     }
 }
 
