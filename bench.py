@@ -55,6 +55,16 @@ def verify_bytes(wl, o_bytes=4) -> int:
     return wl.B * per_b + 2 * wl.Hv * 4
 
 
+def verify_bytes_ragged(wl, lens, o_bytes=4) -> int:
+    """verify_bytes for a ragged batch: sequence b reads and writes as a window of lens[b] tokens."""
+    ie = 2 if wl.bf16 else 4
+    st = wl.Hv * wl.dv * wl.dk * 4
+    tot = 2 * wl.Hv * 4
+    for L in lens:
+        tot += L * wl.C * ie + 2 * L * wl.Hv * ie + st + (L - 1) * st + st + L * wl.Hv * wl.dv * o_bytes
+    return tot
+
+
 def conv_bytes(wl) -> int:
     """x read, hist read + written, y written, window written, taps read."""
     ie = 2 if wl.bf16 else 4
@@ -171,6 +181,33 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "prefill"
         b = verify_bytes(wl)
         res[name] = {"verify_us": round(us, 3), "bytes_per_launch": b, "GBs": round(b / (us * 1e-6) / 1e9, 1),
                      "tokens_per_s": round(wl.B * wl.T / (us * 1e-6), 1)}
+        del sets
+    if "batched" in only:
+        # the same batch with per-sequence verify lengths drawn U{1..8} (one launch, lens on the device)
+        wl = synth.WORKLOADS["batched"]
+        g = torch.Generator().manual_seed(5)
+        lens = torch.randint(1, wl.T + 1, (wl.B,), generator=g, dtype=torch.int32)
+        per = sum((int(L) + 1) for L in lens) * wl.Hv * wl.dv * wl.dk * 4
+        R = max(2, math.ceil(2 * MALL_BYTES / per))
+        sets = []
+        for r in range(R):
+            inp = synth.make_inputs(wl, seed=r)
+            d = {k: v.to(dev) for k, v in inp.items()}
+            d["qkv"] = synth.make_qkv(wl, seed=r).to(dev)
+            d["S_out"] = torch.empty_like(d["S_in"])
+            d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev)
+            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+            d["lens"] = lens.to(dev)
+            sets.append(d)
+
+        def ver_r(d, wl=wl):
+            gdn.verify(d["qkv"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"],
+                       d["H"], d["o"], wl.Hk, lens=d["lens"])
+        us = timed(ver_r, sets, max(1, 200 // R))
+        b = verify_bytes_ragged(wl, [int(L) for L in lens])
+        res["batched_ragged"] = {"verify_us": round(us, 3), "lens_total": int(lens.sum()), "bytes_per_launch": b,
+                                 "GBs": round(b / (us * 1e-6) / 1e9, 1),
+                                 "tokens_per_s": round(int(lens.sum()) / (us * 1e-6), 1)}
         del sets
     if "prefill" not in only:
         return res

@@ -170,6 +170,49 @@ int gdn_rollback(const int32_t *accept, int K,
                  int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void *stream);
 
 /*
+ * Extended forms: per-sequence window lengths (a ragged batch in one launch)
+ * and gates read from a stacked projection output.
+ *
+ * A verify loop that truncates drafts by confidence gives every sequence its
+ * own verify length v_len <= K_max (lucebox PR #637: commit message on
+ * v_len <= q_len and the review note on the verify-length buffer), and the
+ * beta|alpha gates come from one stacked projection (commit message on the
+ * stacked ssm_ba projection).  The _ex forms take
+ *   lens         [B] int32 (device, nullable): tokens of sequence b; values
+ *                are clamped into 1..K (or 1..T).  NULL means every
+ *                sequence uses the whole window.  Sequence b then behaves
+ *                exactly as a call with K = lens[b] on its own: S_out[b] is
+ *                the state after lens[b] tokens, H[b][0..lens[b]-2] and
+ *                o[b][0..lens[b]-1] are written and the rest of its slots are
+ *                left untouched; the conv step keeps window rows
+ *                lens[b]..lens[b]+W-2 as the new history; the rollback keeps
+ *                the state for a == lens[b] and restores it for a < lens[b].
+ *                The buffers keep their K-sized (T-sized) layout.  4-byte
+ *                aligned.
+ *   gate_stride  elements between the gate rows of consecutive tokens
+ *                (>= Hv): Hv for separate [B][K][Hv] buffers, 2*Hv when
+ *                beta_raw points at a stacked [B][K][2*Hv] beta|alpha row
+ *                and alpha = beta_raw + Hv.  The gate pointers need only the
+ *                alignment of their element type.
+ * gdn_conv_step, gdn_verify and gdn_rollback are these with lens = NULL and
+ * gate_stride = Hv.
+ */
+int gdn_conv_step_ex(const void *x, const float *w, void *hist, void *y, void *win_out,
+                     const int32_t *lens, int B, int T, int C, int W, int io_dtype,
+                     void *stream);
+
+int gdn_verify_ex(const void *qkv, const void *beta_raw, const void *alpha, int gate_stride,
+                  const float *dt_bias, const float *A_log,
+                  const float *S_in, float *S_out, float *H, void *o, const int32_t *lens,
+                  int B, int K, int Hk, int Hv, int dk, int dv,
+                  int in_dtype, int o_dtype, float l2_eps, void *stream);
+
+int gdn_rollback_ex(const int32_t *accept, const int32_t *lens, int K,
+                    const float *S_in, const float *H, float *S_out,
+                    void *hist, const void *win,
+                    int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void *stream);
+
+/*
  * gdn_rollback_conv_step -- gdn_rollback of the previous verify window
  * followed by gdn_conv_step of the next tokens, in one launch: in a verify
  * loop the rollback of step i and the conv step of step i+1 touch the same

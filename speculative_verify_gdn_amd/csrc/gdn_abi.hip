@@ -90,6 +90,12 @@ const char* gdn_last_error(void) { return g_err; }
 int gdn_conv_step(const void* x, const float* w, void* hist, void* y, void* win_out, int B, int T, int C, int W,
                   int io_dtype, void* stream)
 {
+    return gdn_conv_step_ex(x, w, hist, y, win_out, nullptr, B, T, C, W, io_dtype, stream);
+}
+
+int gdn_conv_step_ex(const void* x, const float* w, void* hist, void* y, void* win_out, const int32_t* lens, int B,
+                     int T, int C, int W, int io_dtype, void* stream)
+{
     const char* fn = "gdn_conv_step";
     REQUIRE(B >= 0, GDN_EINVAL, "%s: B = %d < 0", fn, B);
     REQUIRE(T >= 1, GDN_EINVAL, "%s: T = %d < 1", fn, T);
@@ -101,6 +107,7 @@ int gdn_conv_step(const void* x, const float* w, void* hist, void* y, void* win_
     REQUIRE(x && w && hist && y, GDN_EINVAL, "%s: null pointer (x, w, hist and y are required)", fn);
     REQUIRE(aligned16(x) && aligned16(w) && aligned16(hist) && aligned16(y) && (!win_out || aligned16(win_out)),
             GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(!lens || ((uintptr_t)lens & 3) == 0, GDN_EINVAL, "%s: lens must be 4-byte aligned", fn);
     const size_t es = elem_size(io_dtype);
     const Span sx{x, (size_t)B * T * C * es}, sw{w, (size_t)C * W * 4}, sh{hist, (size_t)B * (W - 1) * C * es},
         sy{y, (size_t)B * T * C * es}, swin{win_out, win_out ? (size_t)B * (W - 1 + T) * C * es : 0};
@@ -110,13 +117,24 @@ int gdn_conv_step(const void* x, const float* w, void* hist, void* y, void* win_
     REQUIRE(!overlap(sh, sx) && !overlap(sh, sw), GDN_EINVAL, "%s: hist overlaps x or w", fn);
     REQUIRE(T <= 65535 * 16, GDN_EUNSUPPORTED, "%s: T = %d too large", fn, T);
     REQUIRE(B <= 65535, GDN_EUNSUPPORTED, "%s: B = %d too large", fn, B);
-    gdn::ConvArgs a{x, w, hist, y, win_out, B, T, C, W};
+    REQUIRE(!overlap(sh, Span{lens, lens ? (size_t)B * 4 : 0}) && !overlap(sy, Span{lens, lens ? (size_t)B * 4 : 0}) &&
+                !overlap(swin, Span{lens, lens ? (size_t)B * 4 : 0}),
+            GDN_EINVAL, "%s: an output overlaps lens", fn);
+    gdn::ConvArgs a{x, w, hist, y, win_out, B, T, C, W, lens};
     return launch_status(gdn::launch_conv_step(a, io_dtype == GDN_BF16, (hipStream_t)stream), fn);
 }
 
 int gdn_verify(const void* qkv, const void* beta_raw, const void* alpha, const float* dt_bias, const float* A_log,
                const float* S_in, float* S_out, float* H, void* o, int B, int K, int Hk, int Hv, int dk, int dv,
                int in_dtype, int o_dtype, float l2_eps, void* stream)
+{
+    return gdn_verify_ex(qkv, beta_raw, alpha, Hv, dt_bias, A_log, S_in, S_out, H, o, nullptr, B, K, Hk, Hv, dk, dv,
+                         in_dtype, o_dtype, l2_eps, stream);
+}
+
+int gdn_verify_ex(const void* qkv, const void* beta_raw, const void* alpha, int gate_stride, const float* dt_bias,
+                  const float* A_log, const float* S_in, float* S_out, float* H, void* o, const int32_t* lens, int B,
+                  int K, int Hk, int Hv, int dk, int dv, int in_dtype, int o_dtype, float l2_eps, void* stream)
 {
     const char* fn = "gdn_verify";
     int rc = check_gdn_shape(fn, B, K, Hk, Hv, dk, dv, in_dtype, o_dtype, l2_eps);
@@ -127,30 +145,43 @@ int gdn_verify(const void* qkv, const void* beta_raw, const void* alpha, const f
             "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
     if (B == 0) return ok();
     REQUIRE(qkv && beta_raw && alpha && S_in && S_out && o, GDN_EINVAL, "%s: null pointer", fn);
-    REQUIRE(aligned16(qkv) && aligned16(beta_raw) && aligned16(alpha) && aligned16(S_in) && aligned16(S_out) &&
-                aligned16(o) && (!H || aligned16(H)) && (!dt_bias || (aligned16(dt_bias) && aligned16(A_log))),
-            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(gate_stride >= Hv, GDN_EINVAL, "%s: gate_stride = %d < Hv = %d", fn, gate_stride, Hv);
     const size_t ie = elem_size(in_dtype), oe = elem_size(o_dtype);
+    REQUIRE(aligned16(qkv) && aligned16(S_in) && aligned16(S_out) && aligned16(o) && (!H || aligned16(H)) &&
+                (!dt_bias || (aligned16(dt_bias) && aligned16(A_log))),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(((uintptr_t)beta_raw % ie) == 0 && ((uintptr_t)alpha % ie) == 0 && (!lens || ((uintptr_t)lens & 3) == 0),
+            GDN_EINVAL, "%s: gate or lens pointers not aligned to their element size", fn);
     const size_t C = (size_t)2 * Hk * dk + (size_t)Hv * dv;
     const size_t SD = (size_t)B * Hv * dv * dk * 4;
-    const Span sq{qkv, (size_t)B * K * C * ie}, sb{beta_raw, (size_t)B * K * Hv * ie},
-        sa{alpha, (size_t)B * K * Hv * ie}, ssi{S_in, SD}, sso{S_out, SD},
+    const size_t gspan = ((size_t)B * K - 1) * gate_stride + Hv;   // elements from the first to the last gate
+    const Span sq{qkv, (size_t)B * K * C * ie}, sb{beta_raw, gspan * ie}, sa{alpha, gspan * ie},
+        ssi{S_in, SD}, sso{S_out, SD},
         sH{H, H ? (size_t)B * (K - 1) * Hv * dv * dk * 4 : 0}, so{o, (size_t)B * K * Hv * dv * oe},
         sdt{dt_bias, dt_bias ? (size_t)Hv * 4 : 0}, sal{A_log, A_log ? (size_t)Hv * 4 : 0};
     REQUIRE(!(overlap(sso, ssi) && S_out != S_in), GDN_EINVAL, "%s: S_out partially overlaps S_in", fn);
-    const Span ins[] = {sq, sb, sa, sdt, sal};
+    const Span sl{lens, lens ? (size_t)B * 4 : 0};
+    const Span ins[] = {sq, sb, sa, sdt, sal, sl};
     for (const Span& s : ins) {
         REQUIRE(!overlap(sso, s), GDN_EINVAL, "%s: S_out overlaps an input", fn);
         REQUIRE(!overlap(sH, s) && !overlap(so, s), GDN_EINVAL, "%s: H or o overlaps an input", fn);
     }
     REQUIRE(!overlap(sH, ssi) && !overlap(sH, sso) && !overlap(so, ssi) && !overlap(so, sso) && !overlap(so, sH),
             GDN_EINVAL, "%s: H, o and the state buffers must not overlap", fn);
-    gdn::VerifyArgs a{qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o, B, K, Hk, Hv, dk, dv, l2_eps};
+    gdn::VerifyArgs a{qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o, B, K, Hk, Hv, dk, dv, l2_eps, lens,
+                      gate_stride};
     return launch_status(gdn::launch_verify(a, in_dtype == GDN_BF16, o_dtype == GDN_BF16, (hipStream_t)stream), fn);
 }
 
 int gdn_rollback(const int32_t* accept, int K, const float* S_in, const float* H, float* S_out, void* hist,
                  const void* win, int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void* stream)
+{
+    return gdn_rollback_ex(accept, nullptr, K, S_in, H, S_out, hist, win, B, Hv, dv, dk, C, W, io_dtype, stream);
+}
+
+int gdn_rollback_ex(const int32_t* accept, const int32_t* lens, int K, const float* S_in, const float* H,
+                    float* S_out, void* hist, const void* win, int B, int Hv, int dv, int dk, int C, int W,
+                    int io_dtype, void* stream)
 {
     const char* fn = "gdn_rollback";
     REQUIRE(B >= 0, GDN_EINVAL, "%s: B = %d < 0", fn, B);
@@ -175,6 +206,8 @@ int gdn_rollback(const int32_t* accept, int K, const float* S_in, const float* H
     const size_t st = (size_t)Hv * dv * dk * 4;
     const Span ssi{S_in, B * st}, sso{S_out, B * st}, sH{H, H ? (size_t)B * (K - 1) * st : 0};
     REQUIRE(!overlap(sso, ssi) && !overlap(sso, sH), GDN_EINVAL, "%s: S_out overlaps S_in or H", fn);
+    REQUIRE(!lens || ((uintptr_t)lens & 3) == 0, GDN_EINVAL, "%s: lens must be 4-byte aligned", fn);
+    REQUIRE(!overlap(sso, Span{lens, lens ? (size_t)B * 4 : 0}), GDN_EINVAL, "%s: S_out overlaps lens", fn);
     if (hist) {
         const size_t es = elem_size(io_dtype);
         const Span sh{hist, (size_t)B * (W - 1) * C * es}, sw{win, (size_t)B * (W - 1 + K) * C * es};
@@ -182,7 +215,7 @@ int gdn_rollback(const int32_t* accept, int K, const float* S_in, const float* H
                 "%s: hist overlaps another buffer", fn);
     }
     gdn::RollbackArgs a{accept, S_in, H, S_out, hist, win, B, K, (long long)Hv * dv * dk, C, W,
-                        (int)elem_size(io_dtype)};
+                        (int)elem_size(io_dtype), lens};
     return launch_status(gdn::launch_rollback(a, (hipStream_t)stream), fn);
 }
 

@@ -164,12 +164,12 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(ConvArgs a)
         }
     }
     // first token tile, threads tl < W-1: history row tl of the window (old)
-    // and of the new history (window row T + tl)
+    // and of the new history (window row Tb + tl, Tb = this sequence's tokens)
     float nh[kCh], oh[kCh];
     const bool hist_writer = blockIdx.y == 0 && tl < W - 1 && c0 < C;
     if (hist_writer) {
         load_row8<BF16>(a.hist, hb + (size_t)tl * C + c0, nch, vec, oh);
-        const int row = T + tl;
+        const int row = (a.lens ? min(max(a.lens[b], 1), T) : T) + tl;
         if (row < W - 1) load_row8<BF16>(a.hist, hb + (size_t)row * C + c0, nch, vec, nh);
         else load_row8<BF16>(a.x, xb + (size_t)(row - (W - 1)) * C + c0, nch, vec, nh);
         if (a.win) store_row8<BF16>(a.win, (size_t)b * (W - 1 + T) * C + (size_t)tl * C + c0, nch, vec, oh);

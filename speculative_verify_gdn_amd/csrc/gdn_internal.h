@@ -15,6 +15,7 @@ struct ConvArgs {
     void* y;            // [B][T][C]
     void* win;          // [B][W-1+T][C] or nullptr
     int B, T, C, W;
+    const int32_t* lens = nullptr;  // [B] tokens per sequence (<= T), or nullptr: all T
 };
 
 struct VerifyArgs {
@@ -29,6 +30,8 @@ struct VerifyArgs {
     void* o;               // [B][K][Hv][dv]
     int B, K, Hk, Hv, dk, dv;
     float eps;
+    const int32_t* lens = nullptr;  // [B] tokens per sequence (<= K), or nullptr: all K
+    int gstride = 0;                // elements between the gate rows of consecutive tokens (0: Hv)
 };
 
 struct RollbackArgs {
@@ -41,6 +44,7 @@ struct RollbackArgs {
     int B, K;
     long long state_elems;  // Hv*dv*dk
     int C, W, elem_bytes;
+    const int32_t* lens = nullptr;  // [B] window length per sequence (<= K), or nullptr: all K
 };
 
 // rollback of the previous window fused with the conv step of the next tokens

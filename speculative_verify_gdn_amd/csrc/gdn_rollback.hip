@@ -27,14 +27,15 @@ constexpr long long kSlab = (long long)kThreads * 4;  // floats per workgroup
 __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int state_blocks)
 {
     const int b = blockIdx.y;
-    const int K = a.K;
+    const int Kb = a.K;                                        // window of the buffers
+    const int K = a.lens ? min(max(a.lens[b], 1), Kb) : Kb;   // this sequence's window
     int acc = a.accept[b];
     acc = acc < 0 ? 0 : (acc > K ? K : acc);
 
     if ((int)blockIdx.x < state_blocks) {
         if (acc == K) return;
         const float* src = acc == 0 ? a.S_in + (size_t)b * a.state_elems
-                                    : a.H + ((size_t)b * (K - 1) + (acc - 1)) * a.state_elems;
+                                    : a.H + ((size_t)b * (Kb - 1) + (acc - 1)) * a.state_elems;
         float* dst = a.S_out + (size_t)b * a.state_elems;
         const long long e = (long long)blockIdx.x * kSlab + (long long)threadIdx.x * 4;
         if (e < a.state_elems)
@@ -47,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int 
     if (a.hist == nullptr) return;
     const long long n = (long long)(a.W - 1) * a.C;
     const long long e = ((long long)(blockIdx.x - state_blocks) * kThreads + threadIdx.x) * 8;
-    const size_t src0 = ((size_t)b * (a.W - 1 + K) + acc) * a.C;
+    const size_t src0 = ((size_t)b * (a.W - 1 + Kb) + acc) * a.C;
     const size_t dst0 = (size_t)b * (a.W - 1) * a.C;
     if (a.elem_bytes == 2) {
         const uint16_t* s = reinterpret_cast<const uint16_t*>(a.win) + src0;

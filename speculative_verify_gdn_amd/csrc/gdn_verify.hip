@@ -231,14 +231,17 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     const int rloc = wave * RPW + lane / LPR;    // row inside the workgroup
     const int h = blockIdx.y, b = blockIdx.z;
     const int i = blockIdx.x * RPG + rloc;
-    const int K = a.K, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
+    // Kb: the window of the buffers (strides); K: this sequence's tokens (masks)
+    const int Kb = a.K, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
+    const int K = a.lens ? min(max(a.lens[b], 1), Kb) : Kb;
+    const int gs = a.gstride > 0 ? a.gstride : Hv;
     const bool live = i < dv;
     const int ic = live ? i : dv - 1;            // clamped row for loads
     const int C = 2 * Hk * DK + Hv * dv;
     const int hk = h / (Hv / Hk);
     const size_t SD = (size_t)dv * DK;
     const float* Sh = a.S_in + ((size_t)b * Hv + h) * SD;
-    const in_t* X = reinterpret_cast<const in_t*>(a.qkv) + (size_t)b * K * C;   // this sequence's rows
+    const in_t* X = reinterpret_cast<const in_t*>(a.qkv) + (size_t)b * Kb * C;   // this sequence's rows
     const size_t qoff = (size_t)hk * DK, koff = (size_t)(Hk + hk) * DK;
 
     f32x4_t S;
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
         }
         float braw = 0.f, bal = 0.f;
         if (wave == kWaves - 1 && lane < K) {
-            const size_t gi = ((size_t)b * K + lane) * Hv + h;
+            const size_t gi = ((size_t)b * Kb + lane) * gs + h;
             braw = load1<IN_BF16>(a.beta_raw, gi);
             bal = load1<IN_BF16>(a.alpha, gi);
         }
@@ -379,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     // stream of the states H_t = gamma_t H_{t-1} + (u_t / |k_t|) k_t.  A state leaves as
     // soon as its u_t is known, so the stores of the first tokens overlap the rest of
     // the substitution.
-    float* Hrow = a.H ? a.H + ((size_t)b * (K - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
+    float* Hrow = a.H ? a.H + ((size_t)b * (Kb - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
     const size_t Hstep = (size_t)Hv * SD;
     auto stream_token = [&](int t, float ut) {
         const float gm = sm.gam[t];
@@ -434,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             ot = __builtin_fmaf(mrow[t], mine, ot);  // M[j][t] = 0 for t > j
             stream_token(t, mine);
         }
-        if (own && live) store1<O_BF16>(a.o, (((size_t)b * K + j) * Hv + h) * dv + i, ot);
+        if (own && live) store1<O_BF16>(a.o, (((size_t)b * Kb + j) * Hv + h) * dv + i, ot);
     } else {
         // more tokens than lanes per row: every lane solves its row's system
         float u[KMAX];
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
                 float ot = tt.y * (sm.R[rloc][t] * tt.w);
 #pragma unroll
                 for (int s2 = 0; s2 < KMAX; ++s2) ot = __builtin_fmaf(sm.M[t][s2], u[s2], ot);
-                store1<O_BF16>(a.o, (((size_t)b * K + t) * Hv + h) * dv + i, ot);
+                store1<O_BF16>(a.o, (((size_t)b * Kb + t) * Hv + h) * dv + i, ot);
             }
         }
 #pragma unroll

@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked",
-           "gdn_rollback_conv_step")
+           "gdn_rollback_conv_step", "gdn_conv_step_ex", "gdn_verify_ex", "gdn_rollback_ex")
 
 
 class GdnError(RuntimeError):
@@ -52,6 +52,9 @@ def load(path: str = LIB_PATH):
         lib.gdn_rollback.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
         lib.gdn_prefill_chunked.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P]
         lib.gdn_rollback_conv_step.argtypes = [P, I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+        lib.gdn_conv_step_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
+        lib.gdn_verify_ex.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+        lib.gdn_rollback_ex.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
         for name in EXPORTS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "gdn_last_error" else I
         _lib = lib
@@ -94,28 +97,38 @@ def version() -> int:
     return load().gdn_version()
 
 
-def conv_step(x, w, hist, y, win=None, stream=None):
-    """gdn_conv_step: x [B][T][C], w [C][W] f32, hist [B][W-1][C] (updated), y, win [B][W-1+T][C]."""
-    _dev(x, w, hist, y, win)
+def conv_step(x, w, hist, y, win=None, lens=None, stream=None):
+    """gdn_conv_step(_ex): x [B][T][C], w [C][W] f32, hist [B][W-1][C] (updated), y, win [B][W-1+T][C];
+    lens [B] int32 (device) for a ragged batch."""
+    _dev(x, w, hist, y, win, lens)
     B, T, C = x.shape
     W = w.shape[1]
-    _check(load().gdn_conv_step(_p(x), _p(w), _p(hist), _p(y), _p(win), B, T, C, W, _dtype(x), _stream(stream)))
+    _check(load().gdn_conv_step_ex(_p(x), _p(w), _p(hist), _p(y), _p(win), _p(lens), B, T, C, W, _dtype(x),
+                                   _stream(stream)))
 
 
-def verify(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o, Hk, eps=1e-6, stream=None):
-    """gdn_verify: qkv [B][K][C], gates [B][K][Hv], S [B][Hv][dv][dk] f32, H [B][K-1][Hv][dv][dk] or None,
-    o [B][K][Hv][dv]."""
-    _dev(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o)
+def verify(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o, Hk, eps=1e-6, lens=None, gate_stride=None,
+           stream=None):
+    """gdn_verify(_ex): qkv [B][K][C], gates [B][K][Hv], S [B][Hv][dv][dk] f32, H [B][K-1][Hv][dv][dk] or None,
+    o [B][K][Hv][dv]; lens [B] int32 (device) for a ragged batch; gate_stride for gates read out of a
+    stacked beta|alpha buffer (beta_raw and alpha are then views of it: their data pointers are used)."""
+    _dev(qkv, S_in, S_out, H, o, lens, dt_bias, A_log)
+    if gate_stride is None:
+        _dev(beta_raw, alpha)
+    elif not (beta_raw.is_cuda and alpha.is_cuda):
+        raise ValueError("libgdn takes device tensors")
     B, K, _ = qkv.shape
     _, Hv, dv, dk = S_in.shape
-    _check(load().gdn_verify(_p(qkv), _p(beta_raw), _p(alpha), _p(dt_bias), _p(A_log), _p(S_in), _p(S_out),
-                             _p(H), _p(o), B, K, Hk, Hv, dk, dv, _dtype(qkv), _dtype(o), float(eps),
-                             _stream(stream)))
+    gs = Hv if gate_stride is None else int(gate_stride)
+    _check(load().gdn_verify_ex(_p(qkv), _p(beta_raw), _p(alpha), gs, _p(dt_bias), _p(A_log), _p(S_in),
+                                _p(S_out), _p(H), _p(o), _p(lens), B, K, Hk, Hv, dk, dv, _dtype(qkv), _dtype(o),
+                                float(eps), _stream(stream)))
 
 
-def rollback(accept, K, S_in, H, S_out, hist=None, win=None, stream=None):
-    """gdn_rollback: accept [B] int32 (device), S_in/S_out [B][Hv][dv][dk], H [B][K-1][...] or None."""
-    _dev(accept, S_in, H, S_out, hist, win)
+def rollback(accept, K, S_in, H, S_out, hist=None, win=None, lens=None, stream=None):
+    """gdn_rollback(_ex): accept [B] int32 (device), S_in/S_out [B][Hv][dv][dk], H [B][K-1][...] or None;
+    lens [B] int32 (device) for a ragged batch."""
+    _dev(accept, S_in, H, S_out, hist, win, lens)
     B, Hv, dv, dk = S_in.shape
     if hist is not None:
         W = hist.shape[1] + 1
@@ -123,8 +136,8 @@ def rollback(accept, K, S_in, H, S_out, hist=None, win=None, stream=None):
         io = _dtype(hist)
     else:
         W, C, io = 2, 1, GDN_F32
-    _check(load().gdn_rollback(_p(accept), int(K), _p(S_in), _p(H), _p(S_out), _p(hist), _p(win),
-                               B, Hv, dv, dk, C, W, io, _stream(stream)))
+    _check(load().gdn_rollback_ex(_p(accept), _p(lens), int(K), _p(S_in), _p(H), _p(S_out), _p(hist), _p(win),
+                                  B, Hv, dv, dk, C, W, io, _stream(stream)))
 
 
 def rollback_conv_step(accept, K_prev, S_in, H, S_out, win_prev, x, w, hist, y, win, stream=None):

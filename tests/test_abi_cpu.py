@@ -176,6 +176,41 @@ def test_rollback_conv_empty_batch_is_ok(lib):
     assert rollconv_call(lib, B=0) == gdn.GDN_OK
 
 
+def verify_ex_call(lib, **kw):
+    a = dict(qkv=p(0), beta=p(1), alpha=p(2), gs=2, dt=p(3), alog=p(4), S_in=p(5), S_out=p(6), H=p(7), o=p(8),
+             lens=p(9), B=1, K=4, Hk=2, Hv=2, dk=32, dv=32, ind=gdn.GDN_BF16, od=gdn.GDN_F32, eps=1e-6)
+    a.update(kw)
+    return lib.gdn_verify_ex(a["qkv"], a["beta"], a["alpha"], a["gs"], a["dt"], a["alog"], a["S_in"], a["S_out"],
+                             a["H"], a["o"], a["lens"], a["B"], a["K"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["ind"],
+                             a["od"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(gs=1), gdn.GDN_EINVAL),                                  # gate rows narrower than Hv
+    (dict(lens=ctypes.c_void_p(A + 9 * MB + 2)), gdn.GDN_EINVAL),  # lens misaligned
+    (dict(beta=ctypes.c_void_p(A + MB + 1)), gdn.GDN_EINVAL),      # bf16 gate misaligned
+    (dict(lens=p(6)), gdn.GDN_EINVAL),                             # S_out over lens
+    (dict(o=p(1)), gdn.GDN_EINVAL),                                # o over the gates
+])
+def test_verify_ex_rejects(lib, kw, code):
+    assert verify_ex_call(lib, **kw) == code
+
+
+def test_ex_forms_empty_batch_is_ok(lib):
+    assert verify_ex_call(lib, B=0) == gdn.GDN_OK
+    assert lib.gdn_conv_step_ex(p(0), p(1), p(2), p(3), p(4), p(5), 0, 4, 192, 4, gdn.GDN_BF16, None) == gdn.GDN_OK
+    assert lib.gdn_rollback_ex(p(0), p(1), 4, p(2), p(3), p(6), None, None, 0, 2, 32, 32, 1, 2, gdn.GDN_F32,
+                               None) == gdn.GDN_OK
+
+
+def test_ex_forms_reject_misaligned_lens(lib):
+    bad = ctypes.c_void_p(A + 5 * MB + 2)
+    assert lib.gdn_conv_step_ex(p(0), p(1), p(2), p(3), p(4), bad, 1, 4, 192, 4, gdn.GDN_BF16,
+                                None) == gdn.GDN_EINVAL
+    assert lib.gdn_rollback_ex(p(0), bad, 4, p(2), p(3), p(6), None, None, 1, 2, 32, 32, 1, 2, gdn.GDN_F32,
+                               None) == gdn.GDN_EINVAL
+
+
 def prefill_call(lib, **kw):
     a = dict(qkv=p(0), beta=p(1), alpha=p(2), dt=p(3), alog=p(4), S_in=p(5), S_out=p(6), o=p(8), B=1, T=100,
              chunk=64, Hk=2, Hv=2, dk=32, dv=32, ind=gdn.GDN_BF16, od=gdn.GDN_BF16, eps=1e-6)

@@ -341,6 +341,103 @@ def test_rollback_equals_rerun_of_accepted_prefix():
         check_states(S.cpu().numpy(), ref, "rollback a=%d" % a)
 
 
+# ------------------------------------------------------------------ ragged batches, stacked gates
+SENT = 7.25  # sentinel for slots a ragged sequence must leave untouched
+
+
+def test_verify_ragged_matches_per_sequence_oracle():
+    """lens = [16, 1, 5, 11]: sequence b is a verify of lens[b] tokens on its own; its other slots stay."""
+    wl = synth.small("verify16", Hk=2, Hv=6, B=4)
+    lens = torch.tensor([16, 1, 5, 11], dtype=torch.int32)
+    say("verify ragged", lens.tolist())
+    inp = synth.make_inputs(wl, seed=31, weak_decay=True)
+    qkv = synth.make_qkv(wl, seed=31)
+    d = {k: dev(v) for k, v in inp.items()}
+    B, K = wl.B, wl.T
+    S_out = torch.full_like(d["S_in"], SENT)
+    H = torch.full((B, K - 1, wl.Hv, wl.dv, wl.dk), SENT, device="cuda")
+    o = torch.full((B, K, wl.Hv, wl.dv), SENT, device="cuda")
+    gdn.verify(dev(qkv), d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, H, o, wl.Hk,
+               lens=dev(lens))
+    torch.cuda.synchronize()
+    S_out, H, o = S_out.cpu().numpy(), H.cpu().numpy(), o.cpu().numpy()
+    for b, L in enumerate(lens.tolist()):
+        S_ref, H_ref, o_ref = oracle.gdn_recurrent_f64(f64(qkv[b:b + 1, :L]), f64(inp["beta_raw"][b:b + 1, :L]),
+                                                       f64(inp["alpha"][b:b + 1, :L]), f64(inp["dt_bias"]),
+                                                       f64(inp["A_log"]), f64(inp["S_in"][b:b + 1]), wl.Hk)
+        check_states(S_out[b:b + 1], S_ref, "ragged S_out b=%d" % b)
+        if L > 1:
+            check_states(H[b:b + 1, :L - 1], H_ref, "ragged H b=%d" % b)
+        assert np.all(H[b, max(L - 1, 0):] == SENT), "b=%d: H slots past the window were written" % b
+        states = all_states(S_ref, H_ref)
+        check_outputs(o[b:b + 1, :L], o_ref, states, False)
+        assert np.all(o[b, L:] == SENT), "b=%d: o slots past the window were written" % b
+
+
+def test_verify_stacked_gates_equal_separate_buffers():
+    """beta|alpha read out of one [B][K][2Hv] row (gate_stride = 2 Hv): same bytes as separate buffers."""
+    wl = synth.small("verify16", Hk=2, Hv=6, B=2)
+    say("verify stacked gates")
+    inp = synth.make_inputs(wl, seed=32)
+    qkv = dev(synth.make_qkv(wl, seed=32))
+    d = {k: dev(v) for k, v in inp.items()}
+    stacked = torch.cat([d["beta_raw"], d["alpha"]], dim=-1).contiguous()   # [B][K][2 Hv]
+    outs = []
+    for gates in ((d["beta_raw"], d["alpha"], None), (stacked[..., :wl.Hv], stacked[..., wl.Hv:], 2 * wl.Hv)):
+        S_out = torch.empty_like(d["S_in"])
+        H = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device="cuda")
+        o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda")
+        gdn.verify(qkv, gates[0], gates[1], d["dt_bias"], d["A_log"], d["S_in"], S_out, H, o, wl.Hk,
+                   gate_stride=gates[2])
+        outs.append((S_out, H, o))
+    torch.cuda.synchronize()
+    for a_, b_ in zip(outs[0], outs[1]):
+        assert torch.equal(a_, b_)
+    S_ref, H_ref, o_ref = oracle_verify(wl, inp, qkv.cpu())
+    check_states(outs[1][0].cpu().numpy(), S_ref, "stacked S_out")
+
+
+def test_conv_and_rollback_ragged_match_oracle():
+    """Ragged conv step (history = window rows lens[b]..) and ragged rollback (a == lens[b] keeps the state)."""
+    wl = synth.small("verify16", Hk=2, Hv=6, B=4)
+    lens = torch.tensor([16, 1, 5, 11], dtype=torch.int32)
+    acc = torch.tensor([3, 1, 0, 11], dtype=torch.int32)     # a < len, a == len, a == 0, a == len
+    say("conv + rollback ragged", lens.tolist(), acc.tolist())
+    inp = synth.make_inputs(wl, seed=33)
+    B, K, C, W = wl.B, wl.T, wl.C, wl.W
+    x, w, hist = dev(inp["x"]), dev(inp["w"]), dev(inp["hist"])
+    y = torch.empty_like(x)
+    win = torch.empty(B, W - 1 + K, C, dtype=x.dtype, device="cuda")
+    gdn.conv_step(x, w, hist, y, win, lens=dev(lens))
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens.tolist()):
+        y_ref, hist_ref, win_ref = oracle.conv_step_f32(inp["x"][b:b + 1, :L].float().numpy(), inp["w"].numpy(),
+                                                        inp["hist"][b:b + 1].float().numpy(), round_bf16=True)
+        assert np.array_equal(y[b:b + 1, :L].float().cpu().numpy(), y_ref)
+        assert np.array_equal(hist[b:b + 1].float().cpu().numpy(), hist_ref)
+        assert np.array_equal(win[b:b + 1, :W - 1 + L].float().cpu().numpy(), win_ref)
+    # verify on the conv output, then roll back
+    d = {k: dev(v) for k, v in inp.items()}
+    S_out = torch.empty_like(d["S_in"])
+    H = torch.empty(B, K - 1, wl.Hv, wl.dv, wl.dk, device="cuda")
+    o = torch.empty(B, K, wl.Hv, wl.dv, device="cuda")
+    gdn.verify(y, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, H, o, wl.Hk,
+               lens=dev(lens))
+    torch.cuda.synchronize()
+    S_before, H_np, win_np = S_out.cpu().numpy().copy(), H.cpu().numpy(), win.cpu().view(torch.int16).numpy()
+    hist_before = hist.cpu().view(torch.int16).numpy().copy()
+    gdn.rollback(dev(acc), K, d["S_in"], H, S_out, hist, win, lens=dev(lens))
+    torch.cuda.synchronize()
+    S_in_np = inp["S_in"].numpy()
+    for b, L in enumerate(lens.tolist()):
+        S_ref = S_before[b:b + 1].copy()
+        hist_ref = hist_before[b:b + 1].copy()
+        oracle.rollback(acc[b:b + 1].numpy(), L, S_in_np[b:b + 1], np.ascontiguousarray(H_np[b:b + 1, :max(L - 1, 0)]),
+                        S_ref, win=np.ascontiguousarray(win_np[b:b + 1, :W - 1 + L]), hist=hist_ref)
+        assert np.array_equal(S_out[b:b + 1].cpu().numpy(), S_ref), "rollback b=%d" % b
+        assert np.array_equal(hist[b:b + 1].cpu().view(torch.int16).numpy(), hist_ref), "hist b=%d" % b
+
+
 # ------------------------------------------------------------------ prefill
 PREFILL_CASES = [
     ("tiny", dict(T=100), 64),
