@@ -424,6 +424,25 @@ def main():
     t_rb = kernel_us(rollback)
     t_rc = kernel_us(rollback_conv)
 
+    # rollback by checkpoint and replay instead of capture: verify without H, then replay the accepted
+    # prefix from the checkpoint S_in (the same step, timed the same way, on the same sets)
+    def verify_nocap(d):
+        gdn.verify(d["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"], None,
+                   d["o"], wl.Hk)
+
+    def replay(d):
+        gdn.replay(d["accept"], d["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"],
+                   wl.Hk, hist=d["hist"], win=d["win"])
+
+    def replay_step(d):
+        conv(d)
+        verify_nocap(d)
+        replay(d)
+
+    t_ver_nocap = kernel_us(verify_nocap)
+    t_replay = kernel_us(replay)
+    t_replay_step = kernel_us(replay_step)
+
     vb = verify_bytes(wl)
     achieved = vb / (t_ver * 1e-6) / 1e9
     sha = source_sha("gdn_verify.hip", "gdn_device.h")
@@ -466,6 +485,10 @@ def main():
             "conv_us": round(t_conv, 3),
             "rollback_us": round(t_rb, 3),
             "rollback_conv_us": round(t_rc, 3),
+            "checkpoint_replay": {"step_us": round(t_replay_step, 3), "verify_no_capture_us": round(t_ver_nocap, 3),
+                                  "replay_us": round(t_replay, 3),
+                                  "tokens_per_s": round(tokens / (t_replay_step * 1e-6), 1),
+                                  "step": "conv_step + verify(no capture) + replay(accepted prefix) + conv rows"},
             "conv_GBs": round(conv_bytes(wl) / (t_conv * 1e-6) / 1e9, 1),
             "rollback_GBs": round(mean_rb_bytes / (t_rb * 1e-6) / 1e9, 1),
             "verify_only_tokens_per_s": round(tokens / (t_ver * 1e-6), 1),

@@ -213,6 +213,33 @@ int gdn_rollback_ex(const int32_t *accept, const int32_t *lens, int K,
                     int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void *stream);
 
 /*
+ * gdn_replay -- rollback by checkpoint and replay instead of capture.
+ *
+ * A verify without capture (gdn_verify with H = NULL) reads and writes one
+ * state per head instead of K+1; the state before the window is kept as the
+ * checkpoint.  On a partial accept the accepted prefix is replayed from the
+ * checkpoint without verifying again (strix-llama.cpp PR #14: commit messages
+ * on device-resident rolling checkpoints and replay of the accepted tokens).
+ * For each sequence b, a = accept[b] (clamped into 0..K):
+ *   a == K:      S_out[b] untouched (the verify wrote the final state)
+ *   a == 0:      S_out[b] <- S_ckpt[b]
+ *   0 < a < K:   S_out[b] <- the state after the first a window tokens from
+ *                S_ckpt[b] (the same recurrence and arithmetic as gdn_verify
+ *                over a tokens; no outputs, no intermediate states)
+ *   conv (if hist/win given): hist[b][j] <- win[b][a+j], j < W-1
+ *
+ *   accept [B] int32 (device); qkv, beta_raw, alpha, gate_stride, dt_bias,
+ *   A_log: the verify window's inputs as gdn_verify_ex; S_ckpt, S_out
+ *   [B][Hv][dv][dk] float, distinct; hist [B][W-1][C], win [B][W-1+K][C]
+ *   in_dtype, or both NULL.
+ */
+int gdn_replay(const int32_t *accept, const void *qkv, const void *beta_raw, const void *alpha,
+               int gate_stride, const float *dt_bias, const float *A_log,
+               const float *S_ckpt, float *S_out, void *hist, const void *win,
+               int B, int K, int Hk, int Hv, int dk, int dv, int W, int in_dtype,
+               float l2_eps, void *stream);
+
+/*
  * gdn_rollback_conv_step -- gdn_rollback of the previous verify window
  * followed by gdn_conv_step of the next tokens, in one launch: in a verify
  * loop the rollback of step i and the conv step of step i+1 touch the same

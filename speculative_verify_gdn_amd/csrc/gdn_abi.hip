@@ -219,6 +219,51 @@ int gdn_rollback_ex(const int32_t* accept, const int32_t* lens, int K, const flo
     return launch_status(gdn::launch_rollback(a, (hipStream_t)stream), fn);
 }
 
+int gdn_replay(const int32_t* accept, const void* qkv, const void* beta_raw, const void* alpha, int gate_stride,
+               const float* dt_bias, const float* A_log, const float* S_ckpt, float* S_out, void* hist,
+               const void* win, int B, int K, int Hk, int Hv, int dk, int dv, int W, int in_dtype, float l2_eps,
+               void* stream)
+{
+    const char* fn = "gdn_replay";
+    int rc = check_gdn_shape(fn, B, K, Hk, Hv, dk, dv, in_dtype, GDN_F32, l2_eps);
+    if (rc) return rc;
+    REQUIRE(K <= 32, GDN_EUNSUPPORTED, "%s: K = %d > 32", fn, K);
+    REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
+    REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
+            "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
+    REQUIRE((hist == nullptr) == (win == nullptr), GDN_EINVAL, "%s: hist and win must be both given or both NULL",
+            fn);
+    if (hist) REQUIRE(W >= 2 && W <= 8, GDN_EUNSUPPORTED, "%s: W = %d not in 2..8", fn, W);
+    if (B == 0) return ok();
+    REQUIRE(accept && qkv && beta_raw && alpha && S_ckpt && S_out, GDN_EINVAL, "%s: null pointer", fn);
+    REQUIRE(S_ckpt != S_out, GDN_EINVAL, "%s: S_out must not be the checkpoint", fn);
+    REQUIRE(gate_stride >= Hv, GDN_EINVAL, "%s: gate_stride = %d < Hv = %d", fn, gate_stride, Hv);
+    const size_t ie = elem_size(in_dtype);
+    REQUIRE(aligned16(accept) && aligned16(qkv) && aligned16(S_ckpt) && aligned16(S_out) &&
+                (!dt_bias || (aligned16(dt_bias) && aligned16(A_log))) && (!hist || (aligned16(hist) && aligned16(win))),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(((uintptr_t)beta_raw % ie) == 0 && ((uintptr_t)alpha % ie) == 0, GDN_EINVAL,
+            "%s: gate pointers not aligned to their element size", fn);
+    const size_t C = (size_t)2 * Hk * dk + (size_t)Hv * dv;
+    const size_t SD = (size_t)B * Hv * dv * dk * 4;
+    const size_t gspan = ((size_t)B * K - 1) * gate_stride + Hv;
+    const Span sq{qkv, (size_t)B * K * C * ie}, sb{beta_raw, gspan * ie}, sa{alpha, gspan * ie}, sc{S_ckpt, SD},
+        sso{S_out, SD}, sacc{accept, (size_t)B * 4}, sdt{dt_bias, dt_bias ? (size_t)Hv * 4 : 0},
+        sal{A_log, A_log ? (size_t)Hv * 4 : 0}, sh{hist, hist ? (size_t)B * (W - 1) * C * ie : 0},
+        sw{win, win ? (size_t)B * (W - 1 + K) * C * ie : 0};
+    const Span ins[] = {sq, sb, sa, sc, sacc, sdt, sal, sw};
+    for (const Span& s : ins)
+        REQUIRE(!overlap(sso, s) && !overlap(sh, s), GDN_EINVAL, "%s: an output overlaps an input", fn);
+    REQUIRE(!overlap(sso, sh), GDN_EINVAL, "%s: S_out overlaps hist", fn);
+    gdn::VerifyArgs a{qkv, beta_raw, alpha, dt_bias, A_log, S_ckpt, S_out, nullptr, nullptr, B, K, Hk, Hv, dk, dv,
+                      l2_eps, nullptr, gate_stride, accept};
+    rc = launch_status(gdn::launch_verify(a, in_dtype == GDN_BF16, false, (hipStream_t)stream), fn);
+    if (rc || !hist) return rc;
+    // the conv history of the accepted prefix: the rollback's conv rows only
+    gdn::RollbackArgs r{accept, S_ckpt, nullptr, S_out, hist, win, B, K, 0, (int)C, W, (int)ie};
+    return launch_status(gdn::launch_rollback(r, (hipStream_t)stream), fn);
+}
+
 int gdn_rollback_conv_step(const int32_t* accept, int K_prev, const float* S_in, const float* H, float* S_out,
                            const void* win_prev, const void* x, const float* w, void* hist, void* y, void* win,
                            int B, int Hv, int dv, int dk, int T, int C, int W, int io_dtype, void* stream)

@@ -32,6 +32,7 @@ struct VerifyArgs {
     float eps;
     const int32_t* lens = nullptr;  // [B] tokens per sequence (<= K), or nullptr: all K
     int gstride = 0;                // elements between the gate rows of consecutive tokens (0: Hv)
+    const int32_t* replay = nullptr;  // [B] accept lengths: rebuild S_out from S_in over that many tokens
 };
 
 struct RollbackArgs {

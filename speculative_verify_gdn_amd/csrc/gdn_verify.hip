@@ -233,8 +233,23 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     const int i = blockIdx.x * RPG + rloc;
     // Kb: the window of the buffers (strides); K: this sequence's tokens (masks)
     const int Kb = a.K, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
-    const int K = a.lens ? min(max(a.lens[b], 1), Kb) : Kb;
+    int K = a.lens ? min(max(a.lens[b], 1), Kb) : Kb;
     const int gs = a.gstride > 0 ? a.gstride : Hv;
+    if (a.replay) {
+        // replay of the accepted prefix from the checkpoint S_in: nothing to do when the
+        // whole window was kept (S_out holds its final state), a copy when none was
+        const int acc = min(max(a.replay[b], 0), Kb);
+        if (acc >= Kb) return;
+        if (acc == 0) {
+            const int rl = blockIdx.x * RPG + wave * RPW + lane / LPR;
+            if (rl < a.dv) {
+                const size_t off = (((size_t)b * Hv + h) * a.dv + rl) * DK + 4 * (lane % LPR);
+                store_f4<false>(a.S_out + off, load_f4(a.S_in + off));
+            }
+            return;
+        }
+        K = acc;
+    }
     const bool live = i < dv;
     const int ic = live ? i : dv - 1;            // clamped row for loads
     const int C = 2 * Hk * DK + Hv * dv;
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             ot = __builtin_fmaf(mrow[t], mine, ot);  // M[j][t] = 0 for t > j
             stream_token(t, mine);
         }
-        if (own && live) store1<O_BF16>(a.o, (((size_t)b * Kb + j) * Hv + h) * dv + i, ot);
+        if (own && live && a.o) store1<O_BF16>(a.o, (((size_t)b * Kb + j) * Hv + h) * dv + i, ot);
     } else {
         // more tokens than lanes per row: every lane solves its row's system
         float u[KMAX];
@@ -452,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
 #pragma unroll
         for (int t0 = 0; t0 < KMAX; t0 += LPR) {
             const int t = t0 + j;
-            if (t < K && live) {
+            if (t < K && live && a.o) {
                 const float4 tt = sm.tok[t];
                 float ot = tt.y * (sm.R[rloc][t] * tt.w);
 #pragma unroll

@@ -21,7 +21,7 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked",
-           "gdn_rollback_conv_step", "gdn_conv_step_ex", "gdn_verify_ex", "gdn_rollback_ex")
+           "gdn_rollback_conv_step", "gdn_conv_step_ex", "gdn_verify_ex", "gdn_rollback_ex", "gdn_replay")
 
 
 class GdnError(RuntimeError):
@@ -55,6 +55,7 @@ def load(path: str = LIB_PATH):
         lib.gdn_conv_step_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
         lib.gdn_verify_ex.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
         lib.gdn_rollback_ex.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
+        lib.gdn_replay.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
         for name in EXPORTS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "gdn_last_error" else I
         _lib = lib
@@ -150,6 +151,19 @@ def rollback_conv_step(accept, K_prev, S_in, H, S_out, win_prev, x, w, hist, y, 
     _check(load().gdn_rollback_conv_step(_p(accept), int(K_prev), _p(S_in), _p(H), _p(S_out), _p(win_prev), _p(x),
                                          _p(w), _p(hist), _p(y), _p(win), B, Hv, dv, dk, T, C, W, _dtype(x),
                                          _stream(stream)))
+
+
+def replay(accept, qkv, beta_raw, alpha, dt_bias, A_log, S_ckpt, S_out, Hk, hist=None, win=None, eps=1e-6,
+           stream=None):
+    """gdn_replay: S_out <- state after accept[b] tokens of the window from the checkpoint S_ckpt (untouched when
+    accept[b] == K); hist <- win rows accept[b].. when given."""
+    _dev(accept, qkv, beta_raw, alpha, dt_bias, A_log, S_ckpt, S_out, hist, win)
+    B, K, _ = qkv.shape
+    _, Hv, dv, dk = S_ckpt.shape
+    W = hist.shape[1] + 1 if hist is not None else 2
+    _check(load().gdn_replay(_p(accept), _p(qkv), _p(beta_raw), _p(alpha), Hv, _p(dt_bias), _p(A_log), _p(S_ckpt),
+                             _p(S_out), _p(hist), _p(win), B, K, Hk, Hv, dk, dv, W, _dtype(qkv), float(eps),
+                             _stream(stream)))
 
 
 def prefill_chunked(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, o, Hk, chunk=64, eps=1e-6, stream=None):

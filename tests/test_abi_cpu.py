@@ -211,6 +211,32 @@ def test_ex_forms_reject_misaligned_lens(lib):
                                None) == gdn.GDN_EINVAL
 
 
+def replay_call(lib, **kw):
+    a = dict(acc=p(0), qkv=p(1), beta=p(2), alpha=p(3), gs=2, dt=p(4), alog=p(5), S_c=p(6), S_out=p(7), hist=p(8),
+             win=p(9), B=1, K=4, Hk=2, Hv=2, dk=32, dv=32, W=4, ind=gdn.GDN_BF16, eps=1e-6)
+    a.update(kw)
+    return lib.gdn_replay(a["acc"], a["qkv"], a["beta"], a["alpha"], a["gs"], a["dt"], a["alog"], a["S_c"],
+                          a["S_out"], a["hist"], a["win"], a["B"], a["K"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["W"],
+                          a["ind"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(acc=None), gdn.GDN_EINVAL),
+    (dict(S_out=p(6)), gdn.GDN_EINVAL),        # the checkpoint must survive
+    (dict(hist=None), gdn.GDN_EINVAL),         # hist without win
+    (dict(gs=1), gdn.GDN_EINVAL),
+    (dict(K=33), gdn.GDN_EUNSUPPORTED),
+    (dict(S_out=p(1)), gdn.GDN_EINVAL),        # over qkv
+    (dict(W=9), gdn.GDN_EUNSUPPORTED),
+])
+def test_replay_rejects(lib, kw, code):
+    assert replay_call(lib, **kw) == code
+
+
+def test_replay_empty_batch_is_ok(lib):
+    assert replay_call(lib, B=0) == gdn.GDN_OK
+
+
 def prefill_call(lib, **kw):
     a = dict(qkv=p(0), beta=p(1), alpha=p(2), dt=p(3), alog=p(4), S_in=p(5), S_out=p(6), o=p(8), B=1, T=100,
              chunk=64, Hk=2, Hv=2, dk=32, dv=32, ind=gdn.GDN_BF16, od=gdn.GDN_BF16, eps=1e-6)

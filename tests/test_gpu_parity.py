@@ -438,6 +438,48 @@ def test_conv_and_rollback_ragged_match_oracle():
         assert np.array_equal(hist[b:b + 1].cpu().view(torch.int16).numpy(), hist_ref), "hist b=%d" % b
 
 
+def test_replay_matches_oracle_and_capture_rollback():
+    """Checkpoint + replay: verify without capture, then rebuild the accepted prefix from the checkpoint."""
+    wl = synth.small("verify16", Hk=2, Hv=6, B=4)
+    acc = torch.tensor([0, 16, 5, 11], dtype=torch.int32)
+    say("replay", acc.tolist())
+    inp = synth.make_inputs(wl, seed=34, weak_decay=True)
+    B, K, C, W = wl.B, wl.T, wl.C, wl.W
+    d = {k: dev(v) for k, v in inp.items()}
+    x, w = d["x"], d["w"]
+    y = torch.empty_like(x)
+    win = torch.empty(B, W - 1 + K, C, dtype=x.dtype, device="cuda")
+    hist_c = d["hist"].clone()
+    gdn.conv_step(x, w, hist_c, y, win)
+    # capture path
+    S_cap = torch.empty_like(d["S_in"])
+    H = torch.empty(B, K - 1, wl.Hv, wl.dv, wl.dk, device="cuda")
+    o = torch.empty(B, K, wl.Hv, wl.dv, device="cuda")
+    gdn.verify(y, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_cap, H, o, wl.Hk)
+    hist_cap = hist_c.clone()
+    gdn.rollback(dev(acc), K, d["S_in"], H, S_cap, hist_cap, win)
+    # checkpoint + replay path
+    S_rep = torch.empty_like(d["S_in"])
+    gdn.verify(y, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_rep, None, o, wl.Hk)
+    torch.cuda.synchronize()
+    S_final = S_rep.clone()
+    hist_rep = hist_c.clone()
+    gdn.replay(dev(acc), y, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_rep, wl.Hk,
+               hist=hist_rep, win=win)
+    torch.cuda.synchronize()
+    assert torch.equal(hist_rep, hist_cap)
+    assert torch.equal(S_rep[0], d["S_in"][0])          # a = 0: the checkpoint
+    assert torch.equal(S_rep[1], S_final[1])            # a = K: untouched
+    yc = y.cpu()
+    for b, a in enumerate(acc.tolist()):
+        if 0 < a < K:
+            S_ref, _, _ = oracle.gdn_recurrent_f64(f64(yc[b:b + 1, :a]), f64(inp["beta_raw"][b:b + 1, :a]),
+                                                   f64(inp["alpha"][b:b + 1, :a]), f64(inp["dt_bias"]),
+                                                   f64(inp["A_log"]), f64(inp["S_in"][b:b + 1]), wl.Hk, capture=False)
+            check_states(S_rep[b:b + 1].cpu().numpy(), S_ref, "replay b=%d" % b)
+            check_states(S_cap[b:b + 1].cpu().numpy(), S_ref, "capture b=%d" % b)
+
+
 # ------------------------------------------------------------------ prefill
 PREFILL_CASES = [
     ("tiny", dict(T=100), 64),
