@@ -209,6 +209,41 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "prefill"
                                  "GBs": round(b / (us * 1e-6) / 1e9, 1),
                                  "tokens_per_s": round(int(lens.sum()) / (us * 1e-6), 1)}
         del sets
+    if "batched" in only:
+        # rollback by capture (verify writes every H_t, rollback copies H_{a-1}) against checkpoint + replay
+        # (verify writes the final state only, replay re-runs the accepted prefix from S_in), state only,
+        # accept lengths drawn U{0..K} (seed 6)
+        wl = synth.WORKLOADS["batched"]
+        g = torch.Generator().manual_seed(6)
+        acc = torch.randint(0, wl.T + 1, (wl.B,), generator=g, dtype=torch.int32)
+        per = wl.B * wl.Hv * wl.dv * wl.dk * 4 * (wl.T + 1)
+        R = max(2, math.ceil(2 * MALL_BYTES / per))
+        sets = []
+        for r in range(R):
+            inp = synth.make_inputs(wl, seed=r)
+            d = {k: v.to(dev) for k, v in inp.items()}
+            d["qkv"] = synth.make_qkv(wl, seed=r).to(dev)
+            d["S_out"] = torch.empty_like(d["S_in"])
+            d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev)
+            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+            d["acc"] = acc.to(dev)
+            sets.append(d)
+
+        def cap(d, wl=wl):
+            gdn.verify(d["qkv"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"],
+                       d["H"], d["o"], wl.Hk)
+            gdn.rollback(d["acc"], wl.T, d["S_in"], d["H"], d["S_out"])
+
+        def rep(d, wl=wl):
+            gdn.verify(d["qkv"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"],
+                       None, d["o"], wl.Hk)
+            gdn.replay(d["acc"], d["qkv"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"],
+                       d["S_out"], wl.Hk)
+        reps = max(1, 200 // R)
+        res["batched_rollback"] = {"accept_total": int(acc.sum()), "capture_step_us": round(timed(cap, sets, reps), 3),
+                                   "replay_step_us": round(timed(rep, sets, reps), 3),
+                                   "steps": "verify(H) + rollback vs verify(no H) + replay, state only"}
+        del sets
     if "prefill" not in only:
         return res
     wl = synth.WORKLOADS["prefill"]

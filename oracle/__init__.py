@@ -66,6 +66,9 @@ class Oracle:
         lib.oracle_gdn_recurrent_f64.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D]
         lib.oracle_gdn_chunked_f64.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D, I]
         lib.oracle_rollback.argtypes = [P, I, I, P, P, P, L, P, P, L, I]
+        lib.oracle_conv_tree_f32.argtypes = [P, P, P, P, P, I, I, I, I, I]
+        lib.oracle_gdn_tree_f64.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, D]
+        lib.oracle_tree_rollback.argtypes = [P, P, I, I, P, P, P, L, P, P, I, I, I]
         self.lib = lib
         self.path = path
 
@@ -203,6 +206,65 @@ class Oracle:
                                  _ptr(S_out), state_bytes, _ptr(win) if win is not None else None,
                                  _ptr(hist) if hist is not None else None, row_bytes, W)
 
+    # ------------------------------------------------------------------
+    # tree verify
+    # ------------------------------------------------------------------
+    @staticmethod
+    def _parent(parent, B, N):
+        p = np.ascontiguousarray(np.asarray(parent, dtype=np.int32))
+        assert p.shape == (B, N), "parent must be [B][N]"
+        return p
+
+    def conv_tree_f32(self, x, w, hist, parent, round_bf16: bool):
+        """Conv of every node of a draft tree, same precision as conv_step_f32.
+
+        x [B][N][C], w [C][W], hist [B][W-1][C] (not modified), parent [B][N]
+        (an entry outside [0, i) marks a root).  Returns y [B][N][C].
+        """
+        x, w, hist = _f32(x), _f32(w), _f32(hist)
+        B, N, C = x.shape
+        W = w.shape[1]
+        par = self._parent(parent, B, N)
+        y = np.empty((B, N, C), np.float32)
+        self.lib.oracle_conv_tree_f32(_ptr(x), _ptr(w), _ptr(hist), _ptr(par), _ptr(y), B, N, C, W,
+                                      int(bool(round_bf16)))
+        return y
+
+    def gdn_tree_f64(self, qkv, beta_raw, alpha, dt_bias, A_log, parent, S_in, Hk, eps=1e-6):
+        """GDN over a draft tree, one step per node from its parent's state.
+
+        Returns (H [B][N][Hv][dv][dk], o [B][N][Hv][dv]).
+        """
+        qkv, br, al, dt, alog, S_in, B, N, Hv, dv, dk = self._gdn_args(qkv, beta_raw, alpha, dt_bias,
+                                                                       A_log, S_in, Hk)
+        par = self._parent(parent, B, N)
+        H = np.empty((B, N, Hv, dv, dk))
+        o = np.empty((B, N, Hv, dv))
+        self.lib.oracle_gdn_tree_f64(_ptr(qkv), _ptr(br), _ptr(al), _ptr(dt), _ptr(alog), _ptr(par), _ptr(S_in),
+                                     _ptr(H), _ptr(o), B, N, Hk, Hv, dk, dv, float(eps))
+        return H, o
+
+    def tree_rollback(self, node, parent, S_in, H, S_out, x=None, hist=None):
+        """Byte-copy rollback to a tree node on numpy arrays of any element type.
+
+        node [B] (outside [0, N): nothing accepted), parent [B][N],
+        S_in, S_out [B][...state...], H [B][N][...state...], x [B][N][C],
+        hist [B][W-1][C].  S_out and hist are modified in place.
+        """
+        B, N = H.shape[0], H.shape[1]
+        nd = np.ascontiguousarray(np.asarray(node, dtype=np.int32))
+        par = self._parent(parent, B, N)
+        assert S_out.flags.c_contiguous and S_in.flags.c_contiguous and H.flags.c_contiguous
+        state_bytes = S_out.nbytes // B
+        if hist is not None:
+            assert hist.flags.c_contiguous and x.flags.c_contiguous and hist.dtype == x.dtype
+            W, C, eb = hist.shape[1] + 1, hist.shape[2], hist.itemsize
+        else:
+            W, C, eb = 1, 0, 1
+        self.lib.oracle_tree_rollback(_ptr(nd), _ptr(par), int(N), int(B), _ptr(S_in), _ptr(H), _ptr(S_out),
+                                      state_bytes, _ptr(x) if hist is not None else None,
+                                      _ptr(hist) if hist is not None else None, C, W, eb)
+
 
 _lock = threading.Lock()
 _default = None
@@ -219,7 +281,8 @@ def default() -> Oracle:
 def __getattr__(name):
     # module-level access to the default build: oracle.gdn_recurrent_f64(...)
     if name in ("exp32", "silu32", "bf16_rne_bits", "exp32_constants", "conv_step_f32", "conv_step_f64",
-                "gates_f64", "gdn_recurrent_f64", "gdn_chunked_f64", "rollback"):
+                "gates_f64", "gdn_recurrent_f64", "gdn_chunked_f64", "rollback", "conv_tree_f32", "gdn_tree_f64",
+                "tree_rollback"):
         return getattr(default(), name)
     raise AttributeError(name)
 

@@ -495,4 +495,143 @@ void oracle_rollback(const int32_t *accept, int K, int B,
     }
 }
 
-int oracle_version(void) { return 1; }
+/* ------------------------------------------------------------------------- */
+/* Tree verify: the drafted tokens form a tree instead of a chain             */
+/* (lucebox PR #637: DDTree drafting and the tree variant of the conv,        */
+/* ggml_ssm_conv_tree, in the commit messages and the review excerpt of       */
+/* ggml.c).  The pages give the op's name and that the drafter proposes a     */
+/* tree; what it computes is read here as the chain step applied along every  */
+/* root path: a node continues the state its parent left, exactly as token t  */
+/* continues token t-1 in a chain.                                            */
+/*                                                                           */
+/* parent [B][N]: node i continues node parent[b][i].  An entry outside      */
+/* [0, i) marks a root, which continues the committed state (S_in, hist).     */
+/* So the nodes are numbered parents-first and parent[i] = i-1 is the chain.  */
+/* ------------------------------------------------------------------------- */
+static int orc_parent(const int32_t *parent, int b, int N, int i)
+{
+    const int p = parent[(size_t)b * N + i];
+    return (p >= 0 && p < i) ? p : -1;
+}
+
+/* The conv window of node i, oldest first: the W newest rows of             */
+/* [hist ; x along the path root .. i].  col[W-1] = x_i, col[W-2] = x of its */
+/* parent, ..., and once the path ends the history rows from the newest.     */
+static void orc_tree_window(const float *x, const float *hist, const int32_t *parent,
+                            int b, int N, int C, int W, int c, int i, float *col)
+{
+    int m = 0, n = i;
+    while (m < W && n >= 0) {
+        col[W - 1 - m] = x[((size_t)b * N + n) * C + c];
+        n = orc_parent(parent, b, N, n);
+        ++m;
+    }
+    for (int h = W - 2; m < W; --h, ++m) col[W - 1 - m] = hist[((size_t)b * (W - 1) + h) * C + c];
+}
+
+/* Conv of every tree node, same precision and rounding order as             */
+/* oracle_conv_step_f32 (fmaf chain over the taps, oldest first).            */
+/*   x [B][N][C], hist [B][W-1][C] (read only), y [B][N][C].                  */
+void oracle_conv_tree_f32(const float *x, const float *w, const float *hist, const int32_t *parent,
+                          float *y, int B, int N, int C, int W, int round_bf16)
+{
+    float *col = (float *)malloc(sizeof(float) * (size_t)W);
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < N; ++i)
+            for (int c = 0; c < C; ++c) {
+                orc_tree_window(x, hist, parent, b, N, C, W, c, i, col);
+                float acc = 0.0f;
+                for (int j = 0; j < W; ++j) acc = fmaf(w[(size_t)c * W + j], col[j], acc);
+                float out = oracle_silu32(acc);
+                if (round_bf16) out = oracle_bf16_to_f32(oracle_bf16_rne(out));
+                y[((size_t)b * N + i) * C + c] = out;
+            }
+    free(col);
+}
+
+/* GDN over a tree of N nodes, one token step per node from its parent's     */
+/* state (S_in for a root), the same step as oracle_gdn_recurrent_f64.        */
+/*   qkv [B][N][C], beta_raw, alpha [B][N][Hv]                                */
+/*   H [B][N][Hv][dv][dk]   the state after every node                        */
+/*   o [B][N][Hv][dv]       o_i = S_i q_i                                     */
+void oracle_gdn_tree_f64(const double *qkv, const double *beta_raw, const double *alpha,
+                         const double *dt_bias, const double *A_log, const int32_t *parent,
+                         const double *S_in, double *H, double *o,
+                         int B, int N, int Hk, int Hv, int dk, int dv, double eps)
+{
+    const int C = 2 * Hk * dk + Hv * dv;
+    const int grp = Hv / Hk;
+    const size_t SD = (size_t)dv * dk;
+    double *qn = (double *)malloc(sizeof(double) * (size_t)dk);
+    double *kn = (double *)malloc(sizeof(double) * (size_t)dk);
+    for (int b = 0; b < B; ++b) {
+        for (int h = 0; h < Hv; ++h) {
+            const int hk = h / grp;
+            for (int t = 0; t < N; ++t) {
+                const int p = orc_parent(parent, b, N, t);
+                double *S = H + (((size_t)b * N + t) * Hv + h) * SD;
+                const double *from = p < 0 ? S_in + ((size_t)b * Hv + h) * SD
+                                           : H + (((size_t)b * N + p) * Hv + h) * SD;
+                memcpy(S, from, sizeof(double) * SD);
+                const double *row = qkv + ((size_t)b * N + t) * C;
+                orc_l2norm(row + (size_t)hk * dk, qn, dk, eps);
+                orc_l2norm(row + (size_t)Hk * dk + (size_t)hk * dk, kn, dk, eps);
+                const double *v = row + 2 * (size_t)Hk * dk + (size_t)h * dv;
+                double beta, g;
+                const size_t gi = ((size_t)b * N + t) * Hv + h;
+                orc_gate(beta_raw[gi], alpha[gi], dt_bias, A_log, h, &beta, &g);
+                const double gam = exp(g);
+                for (size_t e = 0; e < SD; ++e) S[e] *= gam;
+                for (int i = 0; i < dv; ++i) {
+                    double *Si = S + (size_t)i * dk;
+                    double sk = 0.0;
+                    for (int j = 0; j < dk; ++j) sk += Si[j] * kn[j];
+                    const double u = beta * (v[i] - sk);
+                    for (int j = 0; j < dk; ++j) Si[j] += u * kn[j];
+                    double sq = 0.0;
+                    for (int j = 0; j < dk; ++j) sq += Si[j] * qn[j];
+                    o[(((size_t)b * N + t) * Hv + h) * dv + i] = sq;
+                }
+            }
+        }
+    }
+    free(qn);
+    free(kn);
+}
+
+/* Rollback after a tree verify: sequence b keeps the path root .. node[b]    */
+/* (node[b] outside [0, N): nothing accepted).                                */
+/*   state: S_out[b] <- H[b][node] (S_in[b] when nothing is accepted)         */
+/*   conv:  hist[b] <- the W-1 newest rows of [hist ; x along the path]       */
+/* x, hist hold elements of elem_bytes bytes (a byte copy).                   */
+void oracle_tree_rollback(const int32_t *node, const int32_t *parent, int N, int B,
+                          const void *S_in, const void *H, void *S_out, long state_bytes,
+                          const void *x, void *hist, int C, int W, int elem_bytes)
+{
+    const size_t rb = (size_t)C * elem_bytes;
+    unsigned char *rows = (unsigned char *)malloc(rb * (size_t)(W > 1 ? W - 1 : 1));
+    for (int b = 0; b < B; ++b) {
+        int n = node[b];
+        if (n < 0 || n >= N) n = -1;
+        unsigned char *dst = (unsigned char *)S_out + (size_t)b * state_bytes;
+        if (n < 0)
+            memcpy(dst, (const unsigned char *)S_in + (size_t)b * state_bytes, (size_t)state_bytes);
+        else
+            memcpy(dst, (const unsigned char *)H + ((size_t)b * N + n) * state_bytes, (size_t)state_bytes);
+        if (!hist || !x || W < 2 || n < 0) continue;
+        unsigned char *hb = (unsigned char *)hist + (size_t)b * (W - 1) * rb;
+        /* newest first: x of the path from node n upward, then the old history */
+        int m = 0;
+        while (m < W - 1 && n >= 0) {
+            memcpy(rows + (size_t)(W - 2 - m) * rb, (const unsigned char *)x + ((size_t)b * N + n) * rb, rb);
+            n = orc_parent(parent, b, N, n);
+            ++m;
+        }
+        for (int h = W - 2; m < W - 1; --h, ++m)
+            memcpy(rows + (size_t)(W - 2 - m) * rb, hb + (size_t)h * rb, rb);
+        memcpy(hb, rows, rb * (size_t)(W - 1));
+    }
+    free(rows);
+}
+
+int oracle_version(void) { return 2; }

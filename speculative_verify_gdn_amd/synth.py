@@ -104,3 +104,36 @@ def small(name: str, **over) -> Workload:
     base = asdict(WORKLOADS[name])
     base.update(over)
     return Workload(**base)
+
+
+def make_tree(B: int, N: int, seed: int = 0, shape: str = "random", fan: int = 4):
+    """Parent indices [B][N] int32 of a draft tree, numbered parents first.
+
+    chain:  parent[i] = i - 1 (node 0 a root) -- the plain verify window;
+    star:   every node a root (N one-token continuations of the committed state);
+    random: node 0 a root, node i >= 1 picks its parent uniformly among the
+            `fan` nodes before it (depth about N / (fan/2 + 1));
+    forest: like random, with the committed state (-1) as one more choice.
+    """
+    g = torch.Generator().manual_seed(seed + 104729)
+    par = torch.empty(B, N, dtype=torch.int32)
+    for b in range(B):
+        for i in range(N):
+            if shape == "chain":
+                p = i - 1
+            elif shape == "star":
+                p = -1
+            elif shape in ("random", "forest"):
+                lo = max(0, i - fan)
+                choices = list(range(lo, i)) + ([-1] if (shape == "forest" or i == 0) else [])
+                p = choices[int(torch.randint(0, len(choices), (1,), generator=g))]
+            else:
+                raise ValueError("unknown tree shape %r" % shape)
+            par[b, i] = p
+    return par
+
+
+def make_tree_accept(B: int, N: int, seed: int = 0):
+    """The accepted node per sequence [B] int32, uniform over {-1 (none), 0..N-1}."""
+    g = torch.Generator().manual_seed(seed + 15485863)
+    return torch.randint(-1, N, (B,), generator=g, dtype=torch.int64).to(torch.int32)

@@ -16,6 +16,7 @@ import oracle
 from tests import test_oracle_conv as tc
 from tests import test_oracle_gdn as tg
 from tests import test_oracle_primitives as tp
+from tests import test_oracle_tree as tt
 
 # (name, text in gdn_oracle.c, replacement, occurrence to replace (1-based, 0 = all))
 MUTANTS = [
@@ -61,6 +62,14 @@ MUTANTS = [
     ("wy_final_state_drops_decay", "acc += exp(G[L - 1] - G[s]) * U", "acc += U", 1),
     ("rollback_off_by_one", "+ (a - 1)) * state_bytes", "+ (a > 1 ? a - 2 : 0)) * state_bytes", 1),
     ("rollback_conv_window_row", "+ a) * row_bytes,", "+ (a > 0 ? a - 1 : 0)) * row_bytes,", 1),
+    ("tree_follows_index_not_parent", "const int p = orc_parent(parent, b, N, t);", "const int p = t - 1;", 1),
+    ("tree_parent_may_be_itself", "return (p >= 0 && p < i) ? p : -1;", "return (p >= 0 && p <= i) ? p : -1;", 1),
+    ("tree_window_history_reversed", "for (int h = W - 2; m < W; --h, ++m) col[W - 1 - m]",
+     "for (int h = 0; m < W; ++h, ++m) col[W - 1 - m]", 1),
+    ("tree_rollback_rows_reversed", "memcpy(rows + (size_t)(W - 2 - m) * rb, (const unsigned char *)x",
+     "memcpy(rows + (size_t)m * rb, (const unsigned char *)x", 1),
+    ("tree_rollback_keeps_parent_state", "memcpy(dst, (const unsigned char *)H + ((size_t)b * N + n) * state_bytes",
+     "memcpy(dst, (const unsigned char *)H + ((size_t)b * N + (n > 0 ? n - 1 : 0)) * state_bytes", 1),
 ]
 
 
@@ -93,6 +102,13 @@ def _pin_suite(o):
     yield "wy_strong", lambda: tg.test_chunked_wy_strong_decay_no_ratio_overflow(o)
     yield "head_map", lambda: tg.test_head_map_value_head_reads_key_head_h_div_group(o)
     yield "slab_order", lambda: tg.test_slab_order_q_then_k_then_v(o)
+    yield "tree_chain", lambda: tt.test_chain_tree_equals_chain_verify(o, 5)
+    yield "tree_paths", lambda: tt.test_every_node_equals_chain_over_its_root_path(o, "forest", 12, 4)
+    yield "tree_roots", lambda: tt.test_out_of_range_parents_are_roots(o)
+    yield "tree_conv_chain", lambda: tt.test_chain_tree_conv_equals_conv_step_bitwise(o, 3, 4)
+    yield "tree_conv_paths", lambda: tt.test_tree_conv_node_equals_conv_step_over_its_path(o, "forest")
+    yield "tree_rollback", lambda: tt.test_tree_rollback_equals_path_rerun(o, 4)
+    yield "tree_rollback_bytes", lambda: tt.test_tree_rollback_bf16_bytes(o)
 
 
 def _plant(src: str, old: str, new: str, occ: int) -> str:
