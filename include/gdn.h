@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 1
+#define GDN_VERSION 2
 
 enum gdn_status {
     GDN_OK = 0,
@@ -282,6 +282,60 @@ int gdn_prefill_chunked(const void *qkv, const void *beta_raw, const void *alpha
                         const float *S_in, float *S_out, void *o,
                         int B, int T, int chunk, int Hk, int Hv, int dk, int dv,
                         int in_dtype, int o_dtype, float l2_eps, void *stream);
+
+/*
+ * Tree verify -- the drafter proposes a tree of candidate tokens instead of a
+ * chain (lucebox PR #637: DDTree drafting in the commit messages, and the tree
+ * variant of the conv, ggml_ssm_conv_tree, in the review excerpt of ggml.c).
+ * Node i of sequence b continues node parent[b][i]: its conv window and its
+ * GDN state are those its parent left, exactly as token t continues token
+ * t-1 in a chain.  An entry outside [0, i) marks a root, which continues the
+ * committed state (hist, S_in); nodes are therefore numbered parents first,
+ * and parent[i] = i-1 is the plain chain.  N = nodes per sequence, 1..32.
+ *   parent [B][N] int32 (device), 4-byte aligned, read only.
+ *
+ * gdn_conv_tree -- the conv step of every node: y[b][i] = silu(conv over the
+ * W newest rows of [hist ; x along the path from the root to i]); the same
+ * rounding as gdn_conv_step (a chain-shaped tree gives its y bit for bit).
+ * hist is only read: the history changes once a node is accepted
+ * (gdn_rollback_tree).
+ *   x [B][N][C], hist [B][W-1][C], y [B][N][C] io_dtype; w [C][W] float;
+ *   16-byte aligned; y disjoint from the inputs.
+ */
+int gdn_conv_tree(const void *x, const float *w, const void *hist, const int32_t *parent, void *y,
+                  int B, int N, int C, int W, int io_dtype, void *stream);
+
+/*
+ * gdn_verify_tree -- the GDN recurrence over every node of the tree, each
+ * node one step from its parent's state (S_in for a root):
+ *   H [B][N][Hv][dv][dk] float   the state after every node (N planes: a tree
+ *                                has no single final state)
+ *   o [B][N][Hv][dv]     o_dtype o_i = S_i q^_i
+ * The other arguments, their layouts, alignment and the gate forms are those
+ * of gdn_verify_ex (with K -> N and no lens).  Computed in WY form with the
+ * pairs (node, ancestor) only; every node's state is formed directly from
+ * S_in and the corrections along its path.
+ */
+int gdn_verify_tree(const void *qkv, const void *beta_raw, const void *alpha, int gate_stride,
+                    const float *dt_bias, const float *A_log, const int32_t *parent,
+                    const float *S_in, float *H, void *o,
+                    int B, int N, int Hk, int Hv, int dk, int dv,
+                    int in_dtype, int o_dtype, float l2_eps, void *stream);
+
+/*
+ * gdn_rollback_tree -- sequence b keeps the path from its root to node
+ * n = node[b] (device int32 [B]; outside [0, N): nothing kept):
+ *   S_out[b] <- H[b][n]      (S_in[b] when nothing is kept)
+ *   hist[b]  <- the W-1 newest rows of [hist ; x along the path]
+ *               (unchanged when nothing is kept), a byte copy
+ *   S_in, S_out [B][Hv][dv][dk] float, distinct; H as gdn_verify_tree;
+ *   x [B][N][C] (the conv inputs of the tree) and hist [B][W-1][C] io_dtype,
+ *   both given or both NULL (state only).
+ */
+int gdn_rollback_tree(const int32_t *node, const int32_t *parent, int N,
+                      const float *S_in, const float *H, float *S_out,
+                      const void *x, void *hist,
+                      int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -337,4 +337,102 @@ int gdn_prefill_chunked(const void* qkv, const void* beta_raw, const void* alpha
                          fn);
 }
 
+int gdn_conv_tree(const void* x, const float* w, const void* hist, const int32_t* parent, void* y, int B, int N,
+                  int C, int W, int io_dtype, void* stream)
+{
+    const char* fn = "gdn_conv_tree";
+    REQUIRE(B >= 0, GDN_EINVAL, "%s: B = %d < 0", fn, B);
+    REQUIRE(N >= 1, GDN_EINVAL, "%s: N = %d < 1", fn, N);
+    REQUIRE(N <= gdn::kTreeMax, GDN_EUNSUPPORTED, "%s: N = %d > %d", fn, N, gdn::kTreeMax);
+    REQUIRE(C >= 1, GDN_EINVAL, "%s: C = %d < 1", fn, C);
+    REQUIRE(W >= 2 && W <= 8, GDN_EUNSUPPORTED, "%s: W = %d not in 2..8", fn, W);
+    REQUIRE(valid_dtype(io_dtype), GDN_EINVAL, "%s: bad dtype code %d", fn, io_dtype);
+    REQUIRE((long long)B * N * C < (1LL << 40), GDN_EUNSUPPORTED, "%s: problem too large", fn);
+    REQUIRE(B <= 65535, GDN_EUNSUPPORTED, "%s: B = %d too large", fn, B);
+    if (B == 0) return ok();
+    REQUIRE(x && w && hist && parent && y, GDN_EINVAL, "%s: null pointer", fn);
+    REQUIRE(aligned16(x) && aligned16(w) && aligned16(hist) && aligned16(y), GDN_EINVAL,
+            "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(((uintptr_t)parent & 3) == 0, GDN_EINVAL, "%s: parent must be 4-byte aligned", fn);
+    const size_t es = elem_size(io_dtype);
+    const Span sy{y, (size_t)B * N * C * es};
+    const Span ins[] = {Span{x, (size_t)B * N * C * es}, Span{w, (size_t)C * W * 4},
+                        Span{hist, (size_t)B * (W - 1) * C * es}, Span{parent, (size_t)B * N * 4}};
+    for (const Span& s : ins) REQUIRE(!overlap(sy, s), GDN_EINVAL, "%s: y overlaps an input", fn);
+    gdn::ConvTreeArgs a{x, w, hist, parent, y, B, N, C, W};
+    return launch_status(gdn::launch_conv_tree(a, io_dtype == GDN_BF16, (hipStream_t)stream), fn);
+}
+
+int gdn_verify_tree(const void* qkv, const void* beta_raw, const void* alpha, int gate_stride, const float* dt_bias,
+                    const float* A_log, const int32_t* parent, const float* S_in, float* H, void* o, int B, int N,
+                    int Hk, int Hv, int dk, int dv, int in_dtype, int o_dtype, float l2_eps, void* stream)
+{
+    const char* fn = "gdn_verify_tree";
+    int rc = check_gdn_shape(fn, B, N, Hk, Hv, dk, dv, in_dtype, o_dtype, l2_eps);
+    if (rc) return rc;
+    REQUIRE(N <= gdn::kTreeMax, GDN_EUNSUPPORTED, "%s: N = %d > %d", fn, N, gdn::kTreeMax);
+    REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
+    REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
+            "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
+    if (B == 0) return ok();
+    REQUIRE(qkv && beta_raw && alpha && parent && S_in && H && o, GDN_EINVAL, "%s: null pointer", fn);
+    REQUIRE(gate_stride >= Hv, GDN_EINVAL, "%s: gate_stride = %d < Hv = %d", fn, gate_stride, Hv);
+    const size_t ie = elem_size(in_dtype), oe = elem_size(o_dtype);
+    REQUIRE(aligned16(qkv) && aligned16(S_in) && aligned16(H) && aligned16(o) &&
+                (!dt_bias || (aligned16(dt_bias) && aligned16(A_log))),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(((uintptr_t)beta_raw % ie) == 0 && ((uintptr_t)alpha % ie) == 0 && ((uintptr_t)parent & 3) == 0,
+            GDN_EINVAL, "%s: gate or parent pointers not aligned to their element size", fn);
+    const size_t C = (size_t)2 * Hk * dk + (size_t)Hv * dv;
+    const size_t st = (size_t)Hv * dv * dk * 4;
+    const size_t gspan = ((size_t)B * N - 1) * gate_stride + Hv;
+    const Span sH{H, (size_t)B * N * st}, so{o, (size_t)B * N * Hv * dv * oe};
+    const Span ins[] = {Span{qkv, (size_t)B * N * C * ie}, Span{beta_raw, gspan * ie}, Span{alpha, gspan * ie},
+                        Span{dt_bias, dt_bias ? (size_t)Hv * 4 : 0}, Span{A_log, A_log ? (size_t)Hv * 4 : 0},
+                        Span{parent, (size_t)B * N * 4}, Span{S_in, B * st}};
+    for (const Span& s : ins)
+        REQUIRE(!overlap(sH, s) && !overlap(so, s), GDN_EINVAL, "%s: H or o overlaps an input", fn);
+    REQUIRE(!overlap(sH, so), GDN_EINVAL, "%s: H and o overlap", fn);
+    gdn::VerifyArgs a{qkv, beta_raw, alpha, dt_bias, A_log, S_in, nullptr, H, o, B, N, Hk, Hv, dk, dv, l2_eps,
+                      nullptr, gate_stride, nullptr, parent};
+    return launch_status(gdn::launch_verify(a, in_dtype == GDN_BF16, o_dtype == GDN_BF16, (hipStream_t)stream), fn);
+}
+
+int gdn_rollback_tree(const int32_t* node, const int32_t* parent, int N, const float* S_in, const float* H,
+                      float* S_out, const void* x, void* hist, int B, int Hv, int dv, int dk, int C, int W,
+                      int io_dtype, void* stream)
+{
+    const char* fn = "gdn_rollback_tree";
+    REQUIRE(B >= 0, GDN_EINVAL, "%s: B = %d < 0", fn, B);
+    REQUIRE(N >= 1, GDN_EINVAL, "%s: N = %d < 1", fn, N);
+    REQUIRE(N <= gdn::kTreeMax, GDN_EUNSUPPORTED, "%s: N = %d > %d", fn, N, gdn::kTreeMax);
+    REQUIRE(Hv >= 1 && dv >= 1 && dk >= 1, GDN_EINVAL, "%s: bad state shape", fn);
+    REQUIRE(((long long)Hv * dv * dk) % 4 == 0, GDN_EUNSUPPORTED, "%s: Hv*dv*dk must be a multiple of 4", fn);
+    REQUIRE((hist == nullptr) == (x == nullptr), GDN_EINVAL, "%s: x and hist must be both given or both NULL", fn);
+    if (hist) {
+        REQUIRE(C >= 1, GDN_EINVAL, "%s: C = %d < 1", fn, C);
+        REQUIRE(W >= 2 && W <= 8, GDN_EUNSUPPORTED, "%s: W = %d not in 2..8", fn, W);
+        REQUIRE(valid_dtype(io_dtype), GDN_EINVAL, "%s: bad dtype code %d", fn, io_dtype);
+    }
+    REQUIRE(B <= 65535, GDN_EUNSUPPORTED, "%s: B = %d too large", fn, B);
+    if (B == 0) return ok();
+    REQUIRE(node && parent && S_in && H && S_out, GDN_EINVAL, "%s: null pointer", fn);
+    REQUIRE(S_in != S_out, GDN_EINVAL, "%s: S_out must not be S_in", fn);
+    REQUIRE(aligned16(S_in) && aligned16(S_out) && aligned16(H) && (!hist || (aligned16(hist) && aligned16(x))),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(((uintptr_t)node & 3) == 0 && ((uintptr_t)parent & 3) == 0, GDN_EINVAL,
+            "%s: node and parent must be 4-byte aligned", fn);
+    const size_t st = (size_t)Hv * dv * dk * 4;
+    const Span sso{S_out, B * st}, sh{hist, hist ? (size_t)B * (W - 1) * C * elem_size(io_dtype) : 0};
+    const Span ins[] = {Span{S_in, B * st}, Span{H, (size_t)B * N * st}, Span{node, (size_t)B * 4},
+                        Span{parent, (size_t)B * N * 4},
+                        Span{x, x ? (size_t)B * N * C * elem_size(io_dtype) : 0}};
+    for (const Span& s : ins)
+        REQUIRE(!overlap(sso, s) && !overlap(sh, s), GDN_EINVAL, "%s: an output overlaps an input", fn);
+    REQUIRE(!overlap(sso, sh), GDN_EINVAL, "%s: S_out overlaps hist", fn);
+    gdn::TreeRollbackArgs a{node, parent, S_in, H, S_out, (long long)Hv * dv * dk, x, hist, B, N, C, W,
+                            (int)elem_size(io_dtype)};
+    return launch_status(gdn::launch_tree_rollback(a, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

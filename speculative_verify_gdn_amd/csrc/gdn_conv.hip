@@ -287,6 +287,82 @@ __global__ __launch_bounds__(kThreads) void rollback_conv_kernel(RollConvArgs a,
     }
 }
 
+// Conv of every node of a draft tree (the tree variant of the conv step,
+// ggml_ssm_conv_tree in lucebox PR #637): node i's window is the W newest rows
+// of [hist ; x along its root path], i.e. x_i, x of its parent, ... and then
+// the history from its newest row.  Same thread mapping and rounding as the
+// chain step (a chain-shaped tree gives its y bit for bit); the history is
+// only read -- the tree rollback writes it once a node is accepted.
+template <bool BF16, int W>
+__global__ __launch_bounds__(kThreads) void conv_tree_kernel(ConvTreeArgs a)
+{
+    __shared__ int spar[kTreeMax];
+    const int b = blockIdx.z, N = a.N, C = a.C;
+    if ((int)threadIdx.x < N) {
+        const int i = threadIdx.x;
+        const int p = a.parent[(size_t)b * N + i];
+        spar[i] = (p >= 0 && p < i) ? p : -1;
+    }
+    __syncthreads();
+    const int g = threadIdx.x % kGroups, tl = threadIdx.x / kGroups;
+    const int c0 = (blockIdx.x * kGroups + g) * kCh;
+    const int t = blockIdx.y * kTok + tl;
+    if (c0 >= C || t >= N) return;
+    const int nch = min(kCh, C - c0);
+    const bool vec = (nch == kCh) && ((C & 3) == 0);
+    const size_t xb = (size_t)b * N * C;
+    const size_t hb = (size_t)b * (W - 1) * C;
+
+    // col[W-1] = x_t, then up the path; past a root the history rows, newest first
+    float col[W][kCh];
+    int n = t, hr = W - 2;
+#pragma unroll
+    for (int jj = W - 1; jj >= 0; --jj) {
+        if (n >= 0) {
+            load_row8<BF16>(a.x, xb + (size_t)n * C + c0, nch, vec, col[jj]);
+            n = spar[n];
+        } else {
+            load_row8<BF16>(a.hist, hb + (size_t)hr * C + c0, nch, vec, col[jj]);
+            --hr;
+        }
+    }
+    float wt[kCh][W];
+#pragma unroll
+    for (int e = 0; e < kCh; ++e) {
+        const int ce = c0 + e < C ? c0 + e : C - 1;
+#pragma unroll
+        for (int jj = 0; jj < W; ++jj) wt[e][jj] = a.w[(size_t)ce * W + jj];
+    }
+    float out[kCh];
+#pragma unroll
+    for (int e = 0; e < kCh; ++e) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < W; ++jj) acc = __builtin_fmaf(wt[e][jj], col[jj][e], acc);
+        out[e] = conv_silu(acc);
+    }
+    store_row8<BF16>(a.y, xb + (size_t)t * C + c0, nch, vec, out);
+}
+
+template <bool BF16>
+hipError_t launch_ct(const ConvTreeArgs& a, hipStream_t s)
+{
+    const int groups = (a.C + kCh - 1) / kCh;
+    dim3 grid((groups + kGroups - 1) / kGroups, (a.N + kTok - 1) / kTok, a.B);
+    dim3 block(kThreads);
+    switch (a.W) {
+    case 2: conv_tree_kernel<BF16, 2><<<grid, block, 0, s>>>(a); break;
+    case 3: conv_tree_kernel<BF16, 3><<<grid, block, 0, s>>>(a); break;
+    case 4: conv_tree_kernel<BF16, 4><<<grid, block, 0, s>>>(a); break;
+    case 5: conv_tree_kernel<BF16, 5><<<grid, block, 0, s>>>(a); break;
+    case 6: conv_tree_kernel<BF16, 6><<<grid, block, 0, s>>>(a); break;
+    case 7: conv_tree_kernel<BF16, 7><<<grid, block, 0, s>>>(a); break;
+    case 8: conv_tree_kernel<BF16, 8><<<grid, block, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <bool BF16>
 hipError_t launch_rc(const RollConvArgs& a, hipStream_t s)
 {
@@ -338,6 +414,11 @@ hipError_t launch_conv_step(const ConvArgs& a, bool bf16, hipStream_t s)
 hipError_t launch_rollback_conv(const RollConvArgs& a, bool bf16, hipStream_t s)
 {
     return bf16 ? launch_rc<true>(a, s) : launch_rc<false>(a, s);
+}
+
+hipError_t launch_conv_tree(const ConvTreeArgs& a, bool bf16, hipStream_t s)
+{
+    return bf16 ? launch_ct<true>(a, s) : launch_ct<false>(a, s);
 }
 
 }  // namespace gdn

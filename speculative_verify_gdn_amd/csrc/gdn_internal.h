@@ -33,6 +33,31 @@ struct VerifyArgs {
     const int32_t* lens = nullptr;  // [B] tokens per sequence (<= K), or nullptr: all K
     int gstride = 0;                // elements between the gate rows of consecutive tokens (0: Hv)
     const int32_t* replay = nullptr;  // [B] accept lengths: rebuild S_out from S_in over that many tokens
+    const int32_t* parent = nullptr;  // [B][K] tree verify: parent node per node (H then holds K states)
+};
+
+// largest draft tree (nodes per sequence) of the tree calls
+constexpr int kTreeMax = 32;
+
+struct ConvTreeArgs {
+    const void* x;           // [B][N][C]
+    const float* w;          // [C][W]
+    const void* hist;        // [B][W-1][C], read only
+    const int32_t* parent;   // [B][N]
+    void* y;                 // [B][N][C]
+    int B, N, C, W;
+};
+
+struct TreeRollbackArgs {
+    const int32_t* node;     // [B] accepted node (outside [0, N): none)
+    const int32_t* parent;   // [B][N]
+    const float* S_in;       // [B][Hv][dv][dk]
+    const float* H;          // [B][N][Hv][dv][dk]
+    float* S_out;            // [B][Hv][dv][dk]
+    long long state_elems;   // Hv*dv*dk
+    const void* x;           // [B][N][C] conv inputs of the tree, or nullptr
+    void* hist;              // [B][W-1][C], updated in place, or nullptr
+    int B, N, C, W, elem_bytes;
 };
 
 struct RollbackArgs {
@@ -84,5 +109,7 @@ hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
 hipError_t launch_rollback_conv(const RollConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
 hipError_t launch_prefill_wy(const PrefillArgs& a, bool o_bf16, hipStream_t s);
+hipError_t launch_conv_tree(const ConvTreeArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_tree_rollback(const TreeRollbackArgs& a, hipStream_t s);
 
 }  // namespace gdn

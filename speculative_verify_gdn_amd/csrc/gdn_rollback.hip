@@ -65,7 +65,98 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int 
     }
 }
 
+// Rollback after a tree verify: sequence b keeps the path from its root to node
+// n = node[b] (none when n is outside [0, N)).
+//   S_out[b] <- H[b][n]  (S_in[b] when nothing is kept)
+//   hist[b]  <- the W-1 newest rows of [hist ; x along the path]  (unchanged when nothing is kept)
+// Grid as above: the state slabs, then the conv columns.  A conv thread owns 8
+// columns of one sequence for all W-1 rows: it reads every source row (the old
+// history included) before it writes, so the in-place update needs no barrier.
+template <typename E, int R>
+__device__ __forceinline__ void tree_rows(const E* xs, E* hs, const size_t (&src)[R], const bool (&from_x)[R],
+                                          size_t hb, int C, long long e, int cnt)
+{
+    E v[R][8];
+#pragma unroll
+    for (int m = 0; m < R; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < cnt) v[m][j] = (from_x[m] ? xs : hs)[src[m] + e + j];
+#pragma unroll
+    for (int m = 0; m < R; ++m)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (j < cnt) hs[hb + (size_t)(R - 1 - m) * C + e + j] = v[m][j];
+}
+
+template <int W>
+__global__ __launch_bounds__(kThreads) void tree_rollback_kernel(TreeRollbackArgs a, int state_blocks)
+{
+    const int b = blockIdx.y, N = a.N;
+    int n = a.node[b];
+    n = (n >= 0 && n < N) ? n : -1;
+
+    if ((int)blockIdx.x < state_blocks) {
+        const float* src = n < 0 ? a.S_in + (size_t)b * a.state_elems
+                                 : a.H + ((size_t)b * N + n) * a.state_elems;
+        float* dst = a.S_out + (size_t)b * a.state_elems;
+        const long long e = (long long)blockIdx.x * kSlab + (long long)threadIdx.x * 4;
+        if (e < a.state_elems)
+            __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(src + e)),
+                                        reinterpret_cast<f32x4_t*>(dst + e));
+        return;
+    }
+    if (a.hist == nullptr || n < 0) return;
+    constexpr int R = W - 1;
+    const long long e = ((long long)(blockIdx.x - state_blocks) * kThreads + threadIdx.x) * 8;
+    if (e >= a.C) return;
+    const int cnt = (int)min((long long)8, a.C - e);
+    // source of new history row R-1-m (the m-th newest): x of the m-th node up the
+    // path, then the old history from its newest row
+    size_t src[R];
+    bool from_x[R];
+    int hr = R - 1;
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+        from_x[m] = n >= 0;
+        if (n >= 0) {
+            src[m] = ((size_t)b * N + n) * a.C;
+            const int p = a.parent[(size_t)b * N + n];
+            n = (p >= 0 && p < n) ? p : -1;
+        } else {
+            src[m] = ((size_t)b * R + hr) * a.C;
+            --hr;
+        }
+    }
+    const size_t hb = (size_t)b * R * a.C;
+    if (a.elem_bytes == 2)
+        tree_rows<uint16_t, R>(reinterpret_cast<const uint16_t*>(a.x), reinterpret_cast<uint16_t*>(a.hist), src,
+                               from_x, hb, a.C, e, cnt);
+    else
+        tree_rows<uint32_t, R>(reinterpret_cast<const uint32_t*>(a.x), reinterpret_cast<uint32_t*>(a.hist), src,
+                               from_x, hb, a.C, e, cnt);
+}
+
 }  // namespace
+
+hipError_t launch_tree_rollback(const TreeRollbackArgs& a, hipStream_t s)
+{
+    const int state_blocks = (int)((a.state_elems + kSlab - 1) / kSlab);
+    const int conv_blocks = a.hist != nullptr ? (a.C + kThreads * 8 - 1) / (kThreads * 8) : 0;
+    dim3 grid(state_blocks + conv_blocks, a.B);
+    dim3 block(kThreads);
+    switch (a.hist != nullptr ? a.W : 2) {
+    case 2: tree_rollback_kernel<2><<<grid, block, 0, s>>>(a, state_blocks); break;
+    case 3: tree_rollback_kernel<3><<<grid, block, 0, s>>>(a, state_blocks); break;
+    case 4: tree_rollback_kernel<4><<<grid, block, 0, s>>>(a, state_blocks); break;
+    case 5: tree_rollback_kernel<5><<<grid, block, 0, s>>>(a, state_blocks); break;
+    case 6: tree_rollback_kernel<6><<<grid, block, 0, s>>>(a, state_blocks); break;
+    case 7: tree_rollback_kernel<7><<<grid, block, 0, s>>>(a, state_blocks); break;
+    case 8: tree_rollback_kernel<8><<<grid, block, 0, s>>>(a, state_blocks); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s)
 {

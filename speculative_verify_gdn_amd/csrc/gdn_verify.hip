@@ -14,6 +14,12 @@
 //   (I + A) u = beta (v - e^{G} S_in k^)            (one column per state row)
 //   o_t = e^{G_t} S_in q^_t + sum_{s<=t} M[t][s] u_s
 //   H_t = e^{g_t} H_{t-1} + u_t k^_t^T,  H_{-1} = S_in
+// Tree verify (the drafted tokens form a tree; lucebox PR #637, DDTree drafting
+// in the commit messages): node t continues its parent's state, so G_t sums g
+// along the root path, A and M keep only the pairs (t, s) with s an ancestor of t
+// (or t itself, for M), and H_t = e^{G_t} S_in + sum over the path of
+// e^{G_t-G_s} u_s k^_s^T is formed directly for every node (no state leaves a
+// register chain, since nodes of different branches interleave).
 // (I + A)^{-1} is the WY / UT transform of the window: it turns the K delta
 // corrections into one triangular solve that needs S_in only through the
 // contractions S_in K^T and S_in Q^T.  Only exponentials of G_t - G_s with
@@ -51,7 +57,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
-template <int DK, int KP, int RPG, bool IN_BF16>
+template <int DK, int KP, int RPG, bool IN_BF16, bool TREE>
 struct VerifySmem {
     using in_t = typename std::conditional<IN_BF16, uint16_t, float>::type;
     static constexpr int NP = RPG < 16 ? 16 : RPG;   // row tiles padded to 16
@@ -66,7 +72,12 @@ struct VerifySmem {
     float V[KP][RPG];               // v of the workgroup's rows, per token
     float4 tok[KP];                 // per token: beta, e^{G}, 1/|k|, 1/|q|
     float gam[KP];                  // e^{g}
-    float Gv[KP];                   // running sums of g
+    float Gv[KP];                   // running sums of g (along the root path for a tree)
+    // tree only (one element otherwise)
+    static constexpr int TK = TREE ? KP : 1, TR = TREE ? RPG : 1;
+    uint32_t anc[TK];               // strict ancestors of node t, one bit per node
+    float Cm[TK][KP + 4];           // e^{G_t-G_s}/|k_s| for s an ancestor of t or t itself, else 0
+    float U[TR][KP + 4];            // u_s of each row, for the direct state sums
 };
 
 // sum over each aligned group of N lanes (N = 4, 8, 16 or 32), every lane gets it
@@ -212,7 +223,7 @@ __device__ __forceinline__ float4 lds4(const void* p)
     }
 }
 
-template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT>
+template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT, bool TREE>
 __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
 {
     constexpr int LPR = DK / 4;                  // lanes per state row (one float4 each)
@@ -221,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     constexpr int TB = (KMAX + 15) / 16;         // 16-token MFMA blocks
     constexpr int KP = TB * 16;
     constexpr int NTL = (RPG + 15) / 16;         // 16-row MFMA blocks
-    using Smem = VerifySmem<DK, KP, RPG, IN_BF16>;
+    using Smem = VerifySmem<DK, KP, RPG, IN_BF16, TREE>;
     using in_t = typename Smem::in_t;
     __shared__ Smem sm;
 
@@ -292,10 +303,12 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
                                      : 0.f;
         }
         float braw = 0.f, bal = 0.f;
+        int par = -1;
         if (wave == kWaves - 1 && lane < K) {
             const size_t gi = ((size_t)b * Kb + lane) * gs + h;
             braw = load1<IN_BF16>(a.beta_raw, gi);
             bal = load1<IN_BF16>(a.alpha, gi);
+            if constexpr (TREE) par = a.parent[(size_t)b * Kb + lane];
         }
 
 #pragma unroll
@@ -331,7 +344,30 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             // lane t: gates of token t, then G_t = g_0 + ... + g_t by a scan over the lanes
             float be = 0.f, g = 0.f;
             if (lane < K) gate(braw, bal, a.dt_bias, a.A_log, h, be, g);
-            const float G = lane_scan<KP>(g);
+            float G;
+            if constexpr (TREE) {
+                // G_t = sum of g over the root path of node t, and its strict ancestors, by
+                // pointer jumping: after round r, G covers the 2^r nearest nodes of the path
+                // (t included) and nxt is the next node above them (-1 past the root)
+                int nxt = (lane < K && par >= 0 && par < lane) ? par : -1;
+                uint32_t anc = nxt >= 0 ? 1u << nxt : 0u;
+                G = g;
+#pragma unroll
+                for (int r = 1; r < KP; r *= 2) {
+                    const int src = nxt >= 0 ? nxt : lane;
+                    const float Gn = __shfl(G, src, 64);
+                    const uint32_t an = (uint32_t)__shfl((int)anc, src, 64);
+                    const int nn = __shfl(nxt, src, 64);
+                    if (nxt >= 0) {
+                        G += Gn;
+                        anc |= an;
+                        nxt = nn;
+                    }
+                }
+                if (lane < KP) sm.anc[lane] = anc;
+            } else {
+                G = lane_scan<KP>(g);
+            }
             if (lane < KP) {
                 sm.Gv[lane] = G;
                 sm.tok[lane].x = be;
@@ -371,8 +407,14 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
                     const int t = tm * 16 + m0 + e;
                     const float4 tt = sm.tok[t];
                     const float dec = __expf(fminf(sm.Gv[t] - Gs, 0.f));
-                    if (wa) sm.A[t][s2] = s2 < t ? tt.x * tt.z * rks * dec * d[e] : 0.f;
-                    else sm.M[t][s2] = s2 <= t ? tt.w * rks * dec * d[e] : 0.f;
+                    // s2 is an earlier token of the chain, or an ancestor of node t in a tree
+                    const bool before = TREE ? ((sm.anc[t] >> s2) & 1u) != 0 : s2 < t;
+                    if (wa) {
+                        sm.A[t][s2] = before ? tt.x * tt.z * rks * dec * d[e] : 0.f;
+                    } else {
+                        sm.M[t][s2] = (before || s2 == t) ? tt.w * rks * dec * d[e] : 0.f;
+                        if constexpr (TREE) sm.Cm[t][s2] = (before || s2 == t) ? rks * dec : 0.f;
+                    }
                 }
             }
     } else {
@@ -397,8 +439,28 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     // stream of the states H_t = gamma_t H_{t-1} + (u_t / |k_t|) k_t.  A state leaves as
     // soon as its u_t is known, so the stores of the first tokens overlap the rest of
     // the substitution.
-    float* Hrow = a.H ? a.H + ((size_t)b * (Kb - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
+    // H holds K-1 states per sequence for a chain (the last one goes to S_out), K for a tree
+    float* Hrow = a.H ? a.H + ((size_t)b * (TREE ? Kb : Kb - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
     const size_t Hstep = (size_t)Hv * SD;
+    // a tree node's state, directly from S_in (kept in S) and the u_s of its path:
+    //   H_t = e^{G_t} S_in + sum_{s on the path, s <= t} e^{G_t-G_s} u_s k^_s
+    // the ancestor mask is the same for the whole workgroup, so the loop is scalar
+    auto stream_node = [&](int t) {
+        uint32_t m = __builtin_amdgcn_readfirstlane(sm.anc[t]) | (1u << t);
+        const float eG = sm.tok[t].y;
+        f32x4_t Ht = {eG * S[0], eG * S[1], eG * S[2], eG * S[3]};
+        while (m) {
+            const int s = __builtin_ctz(m);
+            m &= m - 1;
+            const float cf = sm.Cm[t][s] * sm.U[rloc][s];
+            const float4 kx = lds4<IN_BF16>(&sm.k[s][c]);
+            Ht[0] = __builtin_fmaf(cf, kx.x, Ht[0]);
+            Ht[1] = __builtin_fmaf(cf, kx.y, Ht[1]);
+            Ht[2] = __builtin_fmaf(cf, kx.z, Ht[2]);
+            Ht[3] = __builtin_fmaf(cf, kx.w, Ht[3]);
+        }
+        if (live && t < K) store_f4<NT>(Hrow + (size_t)t * Hstep, Ht);
+    };
     auto stream_token = [&](int t, float ut) {
         const float gm = sm.gam[t];
         const float cu = ut * sm.tok[t].z;
@@ -450,7 +512,14 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             // A[j][t] = 0 for t >= j, so finished lanes keep their value
             part = __builtin_fmaf(-arow[t], mine, part);
             ot = __builtin_fmaf(mrow[t], mine, ot);  // M[j][t] = 0 for t > j
-            stream_token(t, mine);
+            if constexpr (TREE) {
+                // one lane per row publishes u_t; the row's lanes read it back in
+                // program order (same wave), so no barrier is needed
+                if (j == 0) sm.U[rloc][t] = mine;
+                stream_node(t);
+            } else {
+                stream_token(t, mine);
+            }
         }
         if (own && live && a.o) store1<O_BF16>(a.o, (((size_t)b * Kb + j) * Hv + h) * dv + i, ot);
     } else {
@@ -475,8 +544,17 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
                 store1<O_BF16>(a.o, (((size_t)b * Kb + t) * Hv + h) * dv + i, ot);
             }
         }
+        if constexpr (TREE) {
+            if (j == 0) {
 #pragma unroll
-        for (int t = 0; t < KMAX; ++t) stream_token(t, u[t]);
+                for (int t = 0; t < KMAX; ++t) sm.U[rloc][t] = u[t];
+            }
+#pragma unroll
+            for (int t = 0; t < KMAX; ++t) stream_node(t);
+        } else {
+#pragma unroll
+            for (int t = 0; t < KMAX; ++t) stream_token(t, u[t]);
+        }
     }
 }
 
@@ -485,7 +563,8 @@ hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
 {
     constexpr int RPG = 1024 / DK;
     dim3 grid((a.dv + RPG - 1) / RPG, a.Hv, a.B);
-    verify_kernel<DK, KMAX, IN_BF16, O_BF16, true><<<grid, dim3(kThreads), 0, s>>>(a);
+    if (a.parent) verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, true><<<grid, dim3(kThreads), 0, s>>>(a);
+    else verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false><<<grid, dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 

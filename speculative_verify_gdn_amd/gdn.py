@@ -21,7 +21,8 @@ LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked",
-           "gdn_rollback_conv_step", "gdn_conv_step_ex", "gdn_verify_ex", "gdn_rollback_ex", "gdn_replay")
+           "gdn_rollback_conv_step", "gdn_conv_step_ex", "gdn_verify_ex", "gdn_rollback_ex", "gdn_replay",
+           "gdn_conv_tree", "gdn_verify_tree", "gdn_rollback_tree")
 
 
 class GdnError(RuntimeError):
@@ -56,6 +57,9 @@ def load(path: str = LIB_PATH):
         lib.gdn_verify_ex.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
         lib.gdn_rollback_ex.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
         lib.gdn_replay.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+        lib.gdn_conv_tree.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+        lib.gdn_verify_tree.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+        lib.gdn_rollback_tree.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
         for name in EXPORTS:
             getattr(lib, name).restype = ctypes.c_char_p if name == "gdn_last_error" else I
         _lib = lib
@@ -174,3 +178,42 @@ def prefill_chunked(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, o, Hk, ch
     _check(load().gdn_prefill_chunked(_p(qkv), _p(beta_raw), _p(alpha), _p(dt_bias), _p(A_log), _p(S_in),
                                       _p(S_out), _p(o), B, T, int(chunk), Hk, Hv, dk, dv, _dtype(qkv), _dtype(o),
                                       float(eps), _stream(stream)))
+
+
+def conv_tree(x, w, hist, parent, y, stream=None):
+    """gdn_conv_tree: x [B][N][C], w [C][W], hist [B][W-1][C] (read only), parent [B][N] int32 -> y [B][N][C]."""
+    _dev(x, w, hist, parent, y)
+    B, N, C = x.shape
+    W = w.shape[1]
+    _check(load().gdn_conv_tree(_p(x), _p(w), _p(hist), _p(parent), _p(y), B, N, C, W, _dtype(x), _stream(stream)))
+
+
+def verify_tree(qkv, beta_raw, alpha, dt_bias, A_log, parent, S_in, H, o, Hk, eps=1e-6, gate_stride=None,
+                stream=None):
+    """gdn_verify_tree: qkv [B][N][C], gates [B][N][Hv] (or a strided view with gate_stride), parent [B][N]
+    int32, S_in [B][Hv][dv][dk] -> H [B][N][Hv][dv][dk] (every node's state), o [B][N][Hv][dv]."""
+    if gate_stride is None:
+        _dev(beta_raw, alpha)
+        gate_stride = S_in.shape[1]
+    elif not (beta_raw.is_cuda and alpha.is_cuda):
+        raise ValueError("libgdn takes device tensors")
+    _dev(qkv, dt_bias, A_log, parent, S_in, H, o)
+    B, N, _ = qkv.shape
+    _, Hv, dv, dk = S_in.shape
+    _check(load().gdn_verify_tree(_p(qkv), _p(beta_raw), _p(alpha), int(gate_stride), _p(dt_bias), _p(A_log),
+                                  _p(parent), _p(S_in), _p(H), _p(o), B, N, Hk, Hv, dk, dv, _dtype(qkv), _dtype(o),
+                                  float(eps), _stream(stream)))
+
+
+def rollback_tree(node, parent, S_in, H, S_out, x=None, hist=None, stream=None):
+    """gdn_rollback_tree: node [B] int32 (outside [0, N): nothing kept), parent [B][N], H [B][N][...];
+    S_out <- H[node] or S_in, hist <- the W-1 newest rows of [hist ; x along the path] when x/hist given."""
+    _dev(node, parent, S_in, H, S_out, x, hist)
+    B, N = parent.shape
+    _, Hv, dv, dk = S_in.shape
+    if hist is not None:
+        W, C, io = hist.shape[1] + 1, hist.shape[2], _dtype(hist)
+    else:
+        W, C, io = 2, 1, GDN_F32
+    _check(load().gdn_rollback_tree(_p(node), _p(parent), N, _p(S_in), _p(H), _p(S_out), _p(x), _p(hist),
+                                    B, Hv, dv, dk, C, W, io, _stream(stream)))

@@ -261,3 +261,76 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(gdn, "_lib", None)
     with pytest.raises(FileNotFoundError):
         gdn.load(str(tmp_path / "missing.so"))
+
+
+def conv_tree_call(lib, **kw):
+    a = dict(x=p(0), w=p(1), hist=p(2), par=p(3), y=p(4), B=1, N=8, C=64, W=4, io=gdn.GDN_BF16)
+    a.update(kw)
+    return lib.gdn_conv_tree(a["x"], a["w"], a["hist"], a["par"], a["y"], a["B"], a["N"], a["C"], a["W"], a["io"],
+                             None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(par=None), gdn.GDN_EINVAL),
+    (dict(par=ctypes.c_void_p(A + 3 * MB + 2)), gdn.GDN_EINVAL),   # parent not 4-byte aligned
+    (dict(N=0), gdn.GDN_EINVAL),
+    (dict(N=33), gdn.GDN_EUNSUPPORTED),
+    (dict(W=9), gdn.GDN_EUNSUPPORTED),
+    (dict(y=p(0)), gdn.GDN_EINVAL),                                 # y over x
+    (dict(y=p(3)), gdn.GDN_EINVAL),                                 # y over parent
+    (dict(io=5), gdn.GDN_EINVAL),
+])
+def test_conv_tree_rejects(lib, kw, code):
+    assert conv_tree_call(lib, **kw) == code
+
+
+def verify_tree_call(lib, **kw):
+    a = dict(qkv=p(0), beta=p(1), alpha=p(2), gs=2, dt=p(3), alog=p(4), par=p(5), S_in=p(6), H=p(8), o=p(12),
+             B=1, N=8, Hk=2, Hv=2, dk=32, dv=32, ind=gdn.GDN_BF16, od=gdn.GDN_F32, eps=1e-6)
+    a.update(kw)
+    return lib.gdn_verify_tree(a["qkv"], a["beta"], a["alpha"], a["gs"], a["dt"], a["alog"], a["par"], a["S_in"],
+                               a["H"], a["o"], a["B"], a["N"], a["Hk"], a["Hv"], a["dk"], a["dv"], a["ind"], a["od"],
+                               a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(par=None), gdn.GDN_EINVAL),
+    (dict(H=None), gdn.GDN_EINVAL),                 # every node's state is the output
+    (dict(N=33), gdn.GDN_EUNSUPPORTED),
+    (dict(N=0), gdn.GDN_EINVAL),
+    (dict(gs=1), gdn.GDN_EINVAL),
+    (dict(H=p(6)), gdn.GDN_EINVAL),                 # H over S_in
+    (dict(o=p(5)), gdn.GDN_EINVAL),                 # o over parent
+    (dict(dk=48, dv=48), gdn.GDN_EUNSUPPORTED),
+    (dict(alog=None), gdn.GDN_EINVAL),
+])
+def test_verify_tree_rejects(lib, kw, code):
+    assert verify_tree_call(lib, **kw) == code
+
+
+def rollback_tree_call(lib, **kw):
+    a = dict(node=p(0), par=p(1), N=8, S_in=p(2), H=p(3), S_out=p(6), x=p(7), hist=p(8), B=1, Hv=2, dv=32, dk=32,
+             C=64, W=4, io=gdn.GDN_BF16)
+    a.update(kw)
+    return lib.gdn_rollback_tree(a["node"], a["par"], a["N"], a["S_in"], a["H"], a["S_out"], a["x"], a["hist"],
+                                 a["B"], a["Hv"], a["dv"], a["dk"], a["C"], a["W"], a["io"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(node=None), gdn.GDN_EINVAL),
+    (dict(S_out=p(2)), gdn.GDN_EINVAL),             # S_out must not be S_in
+    (dict(S_out=p(3)), gdn.GDN_EINVAL),             # S_out over H
+    (dict(hist=None), gdn.GDN_EINVAL),              # x without hist
+    (dict(N=40), gdn.GDN_EUNSUPPORTED),
+    (dict(W=1), gdn.GDN_EUNSUPPORTED),
+    (dict(hist=p(7)), gdn.GDN_EINVAL),              # hist over x
+])
+def test_rollback_tree_rejects(lib, kw, code):
+    assert rollback_tree_call(lib, **kw) == code
+
+
+def test_tree_calls_empty_batch_are_ok(lib):
+    assert conv_tree_call(lib, B=0) == gdn.GDN_OK
+    assert verify_tree_call(lib, B=0) == gdn.GDN_OK
+    assert rollback_tree_call(lib, B=0) == gdn.GDN_OK
+    assert rollback_tree_call(lib, x=None, hist=None, B=0) == gdn.GDN_OK

@@ -1,0 +1,246 @@
+"""GPU parity of the tree verify calls (gdn_conv_tree, gdn_verify_tree,
+gdn_rollback_tree) against the CPU oracle.
+
+Bars as for the chain path: the conv bit for bit against the oracle's
+same-precision conv over the node's path window; every node's state within
+2e-3 * ||S_ref||_F per head, o within 2e-3 * ||S_node||_F (plus half a bf16 ulp
+for bf16 o); the rollback a byte copy.  Trees are seeded (synth.make_tree):
+chain, star, random (parent among the 4 previous nodes) and forest (roots
+mixed in).  Every test prints its case before touching the device.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_verify_gdn_amd import gdn, synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def say(*a):
+    print("[gpu case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(t):
+    return t.contiguous().cuda()
+
+
+def f64(t):
+    return t.double().cpu().numpy()
+
+
+def bits(t):
+    t = t.cpu().contiguous()
+    return t.view(torch.int16).numpy() if t.dtype == torch.bfloat16 else t.view(torch.int32).numpy()
+
+
+def check_states(gpu, ref, what):
+    err = np.abs(gpu.astype(np.float64) - ref).max(axis=(-1, -2))
+    fro = np.linalg.norm(ref, axis=(-1, -2))
+    worst = float(np.max(err / np.maximum(fro, 1e-30)))
+    assert np.all(err <= TOL * fro), "%s: worst err/fro = %.3g" % (what, worst)
+    return worst
+
+
+def check_outputs(o_gpu, o_ref, H_ref, bf16_out):
+    fro = np.linalg.norm(H_ref, axis=(-1, -2))  # [B][N][Hv]
+    bound = TOL * fro[..., None] + (np.abs(o_ref) * 2.0 ** -8 if bf16_out else 0.0)
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    assert np.all(err <= bound), "o: worst err/bound = %.3g" % float(np.max(err / np.maximum(bound, 1e-30)))
+
+
+# ------------------------------------------------------------------ conv
+CONV_CASES = [
+    ("verify16", dict(T=16, B=2), "random"),
+    ("verify16", dict(T=32, B=1), "forest"),
+    ("verify16", dict(T=9, B=2, W=2), "random"),
+    ("verify16", dict(T=7, B=2, W=8), "forest"),
+    ("verify16", dict(T=16, B=1), "chain"),
+    ("verify16", dict(T=5, B=3), "star"),
+    ("tiny", dict(T=12, B=2), "random"),                         # fp32
+    ("tiny", dict(Hk=1, Hv=3, dk=32, dv=40, T=11), "forest"),    # C = 184: ragged channel tail
+    ("verify16", dict(T=1, B=2), "random"),
+]
+
+
+@pytest.mark.parametrize("name,over,shape", CONV_CASES)
+def test_conv_tree_bit_exact(name, over, shape):
+    wl = synth.small(name, **over)
+    say("conv_tree", name, over, shape, "C=%d" % wl.C)
+    inp = synth.make_inputs(wl, seed=3)
+    par = synth.make_tree(wl.B, wl.T, seed=4, shape=shape)
+    x, w, hist = dev(inp["x"]), dev(inp["w"]), dev(inp["hist"])
+    hist0 = hist.clone()
+    y = torch.empty_like(x)
+    gdn.conv_tree(x, w, hist, dev(par), y)
+    torch.cuda.synchronize()
+    y_ref = oracle.conv_tree_f32(inp["x"].float().numpy(), inp["w"].numpy(), inp["hist"].float().numpy(),
+                                 par.numpy(), wl.bf16)
+    y_ref_t = torch.from_numpy(y_ref).to(inp["x"].dtype)
+    assert np.array_equal(bits(y), bits(y_ref_t))
+    assert torch.equal(hist, hist0), "gdn_conv_tree must not write the history"
+
+
+def test_conv_tree_chain_equals_conv_step():
+    wl = synth.small("verify16", T=16, B=2)
+    say("conv_tree chain == conv_step", "C=%d" % wl.C)
+    inp = synth.make_inputs(wl, seed=5)
+    x, w = dev(inp["x"]), dev(inp["w"])
+    y1, y2 = torch.empty_like(x), torch.empty_like(x)
+    gdn.conv_tree(x, w, dev(inp["hist"]), dev(synth.make_tree(wl.B, wl.T, shape="chain")), y1)
+    gdn.conv_step(x, w, dev(inp["hist"]), y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+# ------------------------------------------------------------------ GDN
+VERIFY_CASES = [
+    # (workload, overrides, tree shape, o dtype)
+    ("verify16", dict(B=2, Hk=4, Hv=12), "random", torch.float32),
+    ("verify16", dict(B=1, T=32, Hk=4, Hv=12), "forest", torch.float32),
+    ("verify16", dict(B=2, T=16, Hk=2, Hv=6), "star", torch.bfloat16),
+    ("verify16", dict(B=3, T=7, Hk=2, Hv=6, dk=64, dv=64), "forest", torch.float32),
+    ("verify16", dict(B=2, T=16, Hk=2, Hv=4, dk=32, dv=32), "random", torch.float32),   # more tokens than lanes per row
+    ("verify16", dict(B=1, T=24, Hk=2, Hv=4, dk=64, dv=48), "random", torch.float32),   # dv not a tile multiple
+    ("tiny", dict(T=9), "forest", torch.float32),                                       # fp32 inputs
+    ("verify16", dict(B=2, T=1, Hk=2, Hv=6), "random", torch.float32),
+]
+
+
+def _tree_case(wl, shape, seed):
+    inp = synth.make_inputs(wl, seed=seed)
+    qkv = synth.make_qkv(wl, seed=seed)
+    par = synth.make_tree(wl.B, wl.T, seed=seed, shape=shape)
+    return inp, qkv, par
+
+
+def _verify_tree_gpu(wl, inp, qkv, par, o_dtype=torch.float32):
+    d = {k: dev(v) for k, v in inp.items()}
+    H = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, wl.dk, device="cuda")
+    o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda", dtype=o_dtype)
+    gdn.verify_tree(dev(qkv), d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], dev(par), d["S_in"], H, o,
+                    wl.Hk)
+    torch.cuda.synchronize()
+    return H, o
+
+
+@pytest.mark.parametrize("name,over,shape,o_dtype", VERIFY_CASES)
+def test_verify_tree_matches_oracle(name, over, shape, o_dtype):
+    wl = synth.small(name, **over)
+    say("verify_tree", name, over, shape, o_dtype)
+    inp, qkv, par = _tree_case(wl, shape, seed=11)
+    H, o = _verify_tree_gpu(wl, inp, qkv, par, o_dtype)
+    H_ref, o_ref = oracle.gdn_tree_f64(f64(qkv), f64(inp["beta_raw"]), f64(inp["alpha"]), f64(inp["dt_bias"]),
+                                       f64(inp["A_log"]), par.numpy(), f64(inp["S_in"]), wl.Hk)
+    worst = check_states(H.cpu().numpy(), H_ref, "H")
+    check_outputs(o.float().cpu().numpy(), o_ref, H_ref, o_dtype == torch.bfloat16)
+    say("worst state err/fro %.3g" % worst)
+
+
+def test_verify_tree_chain_outputs_equal_chain_verify():
+    # a chain-shaped tree takes the chain kernel's arithmetic for A, M, u and o
+    # (path sums by pointer jumping are the chain's scan for N <= 16): o bit for bit,
+    # states within the bar of the chain's last state
+    wl = synth.small("verify16", B=2, Hk=4, Hv=12)
+    say("verify_tree chain == verify", wl)
+    inp, qkv, par = _tree_case(wl, "chain", seed=12)
+    H, o = _verify_tree_gpu(wl, inp, qkv, par)
+    d = {k: dev(v) for k, v in inp.items()}
+    S_out = torch.empty_like(d["S_in"])
+    Hc = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device="cuda")
+    oc = torch.empty_like(o)
+    gdn.verify(dev(qkv), d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, Hc, oc, wl.Hk)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc)
+    ref = torch.cat([Hc, S_out[:, None]], dim=1).double().cpu().numpy()
+    check_states(H.cpu().numpy(), ref, "chain states")
+
+
+def test_verify_tree_stacked_gates_and_bad_parents():
+    # beta|alpha read from one stacked row; parent entries outside [0, i) act as roots
+    wl = synth.small("verify16", B=2, T=8, Hk=2, Hv=6)
+    say("verify_tree stacked gates, out-of-range parents")
+    inp, qkv, _ = _tree_case(wl, "random", seed=13)
+    bad = torch.tensor([[5, 0, 2, -7, 3, 100, 1, 6], [-1, 0, 0, 1, -2, 4, 9, 2]], dtype=torch.int32)
+    good = torch.tensor([[-1, 0, -1, -1, 3, -1, 1, 6], [-1, 0, 0, 1, -1, 4, -1, 2]], dtype=torch.int32)
+    d = {k: dev(v) for k, v in inp.items()}
+    stacked = torch.cat([d["beta_raw"], d["alpha"]], dim=-1).contiguous()
+    H1 = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, wl.dk, device="cuda")
+    o1 = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda")
+    gdn.verify_tree(dev(qkv), stacked[..., :wl.Hv], stacked[..., wl.Hv:], d["dt_bias"], d["A_log"], dev(bad),
+                    d["S_in"], H1, o1, wl.Hk, gate_stride=2 * wl.Hv)
+    H2, o2 = _verify_tree_gpu(wl, inp, qkv, good)
+    assert torch.equal(H1, H2) and torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------------ rollback
+@pytest.mark.parametrize("bf16,W", [(True, 4), (False, 4), (True, 2), (True, 8)])
+def test_rollback_tree_bit_exact(bf16, W):
+    B, N, Hv, dv, dk, C = 4, 12, 3, 16, 32, 200
+    say("rollback_tree", bf16, W)
+    g = torch.Generator().manual_seed(21)
+    io = torch.bfloat16 if bf16 else torch.float32
+    S_in = torch.randn(B, Hv, dv, dk, generator=g)
+    H = torch.randn(B, N, Hv, dv, dk, generator=g)
+    x = torch.randn(B, N, C, generator=g).to(io)
+    hist = torch.randn(B, W - 1, C, generator=g).to(io)
+    par = synth.make_tree(B, N, seed=6, shape="forest")
+    node = torch.tensor([-1, 0, 7, N - 1], dtype=torch.int32)
+    S_out = torch.zeros_like(S_in)
+    d_S_out, d_hist = dev(S_out), dev(hist)
+    gdn.rollback_tree(dev(node), dev(par), dev(S_in), dev(H), d_S_out, dev(x), d_hist)
+    torch.cuda.synchronize()
+    ref_S = S_out.numpy().copy()
+    ref_hist = (hist.view(torch.int16) if bf16 else hist).numpy().copy()
+    xs = (x.view(torch.int16) if bf16 else x).numpy()
+    oracle.tree_rollback(node.numpy(), par.numpy(), S_in.numpy(), H.numpy(), ref_S, x=xs, hist=ref_hist)
+    assert np.array_equal(bits(d_S_out), ref_S.view(np.int32))
+    assert np.array_equal(bits(d_hist), ref_hist.view(np.int16) if bf16 else ref_hist.view(np.int32))
+
+
+# ------------------------------------------------------------------ the whole tree step
+def test_tree_step_conv_verify_rollback_against_oracle():
+    wl = synth.small("verify16", B=2, T=16, Hk=4, Hv=12)
+    say("tree step conv -> verify -> rollback", wl)
+    inp = synth.make_inputs(wl, seed=31)
+    par = synth.make_tree(wl.B, wl.T, seed=31, shape="random")
+    node = torch.tensor([9, -1], dtype=torch.int32)
+    d = {k: dev(v) for k, v in inp.items()}
+    y = torch.empty_like(d["x"])
+    gdn.conv_tree(d["x"], d["w"], d["hist"], dev(par), y)
+    H = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, wl.dk, device="cuda")
+    o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda")
+    gdn.verify_tree(y, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], dev(par), d["S_in"], H, o, wl.Hk)
+    S_out = torch.empty_like(d["S_in"])
+    gdn.rollback_tree(dev(node), dev(par), d["S_in"], H, S_out, d["x"], d["hist"])
+    torch.cuda.synchronize()
+
+    y_ref = oracle.conv_tree_f32(inp["x"].float().numpy(), inp["w"].numpy(), inp["hist"].float().numpy(),
+                                 par.numpy(), True)
+    y_ref_bf = torch.from_numpy(y_ref).to(torch.bfloat16)
+    assert torch.equal(y.cpu(), y_ref_bf)
+    H_ref, o_ref = oracle.gdn_tree_f64(f64(y_ref_bf), f64(inp["beta_raw"]), f64(inp["alpha"]), f64(inp["dt_bias"]),
+                                       f64(inp["A_log"]), par.numpy(), f64(inp["S_in"]), wl.Hk)
+    check_outputs(o.cpu().numpy(), o_ref, H_ref, False)
+    S_ref = np.stack([H_ref[0, 9], f64(inp["S_in"])[1]])
+    check_states(S_out.cpu().numpy(), S_ref, "S_out")
+    hist_ref = inp["hist"].view(torch.int16).numpy().copy()
+    S_dummy = np.zeros((wl.B, 1), np.float32)
+    oracle.tree_rollback(node.numpy(), par.numpy(), S_dummy, np.zeros((wl.B, wl.T, 1), np.float32), S_dummy.copy(),
+                         x=inp["x"].view(torch.int16).numpy(), hist=hist_ref)
+    assert np.array_equal(d["hist"].cpu().view(torch.int16).numpy(), hist_ref)
