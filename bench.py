@@ -65,6 +65,15 @@ def verify_bytes_ragged(wl, lens, o_bytes=4) -> int:
     return tot
 
 
+def verify_tree_bytes(wl, o_bytes=4) -> int:
+    """Algorithmic bytes of one gdn_verify_tree launch over N = wl.T nodes: verify_bytes with every node's
+    state written (N planes, no separate final state) and the parent indices read."""
+    ie = 2 if wl.bf16 else 4
+    st = wl.Hv * wl.dv * wl.dk * 4
+    per_b = wl.T * wl.C * ie + 2 * wl.T * wl.Hv * ie + st + wl.T * st + wl.T * wl.Hv * wl.dv * o_bytes + 4 * wl.T
+    return wl.B * per_b + 2 * wl.Hv * 4
+
+
 def conv_bytes(wl) -> int:
     """x read, hist read + written, y written, window written, taps read."""
     ie = 2 if wl.bf16 else 4
@@ -138,7 +147,7 @@ def cpu_baseline(wl, budget_s: float):
                       "one thread, %.1f s" % (steps, wl.name, el)}
 
 
-def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "prefill")):
+def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "prefill")):
     """Kernel time of gdn_verify on the decode (K=1) and batched (B=32, K=8)
     workloads, and of gdn_prefill_chunked on the prefill workload (B=4 x
     T=4096, chunk 64): graph-replayed back-to-back launches over enough buffer
@@ -244,6 +253,52 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "prefill"
                                    "replay_step_us": round(timed(rep, sets, reps), 3),
                                    "steps": "verify(H) + rollback vs verify(no H) + replay, state only"}
         del sets
+    if "tree" in only:
+        # tree verify on the verify16 shape: N = 16 and 32 nodes of a random draft tree (parent among the 4
+        # previous nodes), the conv of every node, the verify, and the rollback to a drawn node
+        for N in (16, 32):
+            wl = synth.small("verify16", T=N)
+            per = wl.B * wl.Hv * wl.dv * wl.dk * 4 * (N + 1)
+            R = max(2, math.ceil(2 * MALL_BYTES / per))
+            sets = []
+            for r in range(R):
+                inp = synth.make_inputs(wl, seed=r)
+                d = {k: v.to(dev) for k, v in inp.items()}
+                d["parent"] = synth.make_tree(wl.B, N, seed=r, shape="random").to(dev)
+                d["node"] = synth.make_tree_accept(wl.B, N, seed=r).to(dev)
+                d["y"] = torch.empty_like(d["x"])
+                d["S_out"] = torch.empty_like(d["S_in"])
+                d["H"] = torch.empty(wl.B, N, wl.Hv, wl.dv, wl.dk, device=dev)
+                d["o"] = torch.empty(wl.B, N, wl.Hv, wl.dv, device=dev)
+                sets.append(d)
+
+            def tconv(d):
+                gdn.conv_tree(d["x"], d["w"], d["hist"], d["parent"], d["y"])
+
+            def tver(d, wl=wl):
+                gdn.verify_tree(d["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["parent"], d["S_in"],
+                                d["H"], d["o"], wl.Hk)
+
+            def troll(d):
+                gdn.rollback_tree(d["node"], d["parent"], d["S_in"], d["H"], d["S_out"], d["x"], d["hist"])
+
+            def tstep(d):
+                tconv(d)
+                tver(d)
+                troll(d)
+            for fn in sets:
+                tconv(fn)
+            reps = max(1, 200 // R)
+            t_v = timed(tver, sets, reps)
+            t_s = timed(tstep, sets, reps)
+            b = verify_tree_bytes(wl)
+            res["tree%d" % N] = {"verify_tree_us": round(t_v, 3), "bytes_per_launch": b,
+                                 "GBs": round(b / (t_v * 1e-6) / 1e9, 1),
+                                 "conv_tree_us": round(timed(tconv, sets, reps), 3),
+                                 "rollback_tree_us": round(timed(troll, sets, reps), 3),
+                                 "step_us": round(t_s, 3), "nodes_per_s": round(N / (t_s * 1e-6), 1),
+                                 "tree": "random, parent among the 4 previous nodes"}
+            del sets
     if "prefill" not in only:
         return res
     wl = synth.WORKLOADS["prefill"]
@@ -289,6 +344,9 @@ def main():
                     help="skip the decode / batched / prefill kernel timings in the detail object")
     ap.add_argument("--prefill-only", action="store_true",
                     help="only time gdn_prefill_chunked on the prefill workload (B=4 x T=4096) and print its figures")
+    ap.add_argument("--only", default="", metavar="NAMES",
+                    help="comma-separated subset of decode,batched,tree,prefill: time only those workloads, print "
+                         "their figures and exit")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (HBM counter calibration) and exit")
     args = ap.parse_args()
@@ -319,6 +377,9 @@ def main():
     gdn.load()
     if args.prefill_only:
         print(json.dumps({"prefill": other_workloads(torch, gdn, synth, dev, only=("prefill",))["prefill"]}))
+        return
+    if args.only:
+        print(json.dumps(other_workloads(torch, gdn, synth, dev, only=tuple(args.only.split(",")))))
         return
 
     wl = synth.WORKLOADS[args.workload]
