@@ -74,6 +74,18 @@ def verify_tree_bytes(wl, o_bytes=4) -> int:
     return wl.B * per_b + 2 * wl.Hv * 4
 
 
+def step_bytes(wl, o_bytes=4) -> int:
+    """Algorithmic bytes of one gdn_verify_step launch (rollback of the previous window + conv step +
+    verify with capture): per sequence the raw tokens K*C*ie and the W-1 history rows, the gates, the
+    start state read once and written once as the checkpoint, H (K-1 states), S_out, o and the conv
+    window (W-1+K rows); the taps C*W*4, dt_bias and A_log once; the accept lengths."""
+    ie = 2 if wl.bf16 else 4
+    st = wl.Hv * wl.dv * wl.dk * 4
+    per_b = (wl.T * wl.C * ie + (wl.W - 1) * wl.C * ie + 2 * wl.T * wl.Hv * ie + 2 * st + (wl.T - 1) * st + st
+             + wl.T * wl.Hv * wl.dv * o_bytes + (wl.W - 1 + wl.T) * wl.C * ie + 4)
+    return wl.B * per_b + wl.C * wl.W * 4 + 2 * wl.Hv * 4
+
+
 def conv_bytes(wl) -> int:
     """x read, hist read + written, y written, window written, taps read."""
     ie = 2 if wl.bf16 else 4
@@ -335,6 +347,8 @@ def main():
     ap.add_argument("--workload", default="verify16")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled (0: enough to exceed 2x the MALL)")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of HIP graphs")
+    ap.add_argument("--two-kernel", action="store_true",
+                    help="step as rollback_conv_step -> verify (two launches) instead of the fused gdn_verify_step")
     ap.add_argument("--three-kernel", action="store_true",
                     help="step as conv_step -> verify -> rollback (three launches) instead of "
                          "rollback_conv_step -> verify")
@@ -395,6 +409,7 @@ def main():
         d["S_out"] = torch.empty_like(d["S_in"])
         d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev) if wl.T > 1 else None
         d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+        d["S_ckpt"] = torch.empty_like(d["S_in"])     # the fused step's checkpoint (start state)
         return d
 
     probe = make_set(0)
@@ -418,19 +433,40 @@ def main():
         gdn.rollback_conv_step(d["accept"], wl.T, d["S_in"], d["H"], d["S_out"], d["win_prev"], d["x"], d["w"],
                                d["hist"], d["y"], d["win"])
 
-    if args.three_kernel:
+    def set_index(d):
+        return next(r for r, s2 in enumerate(sets) if s2 is d)
+
+    def fused_first(d):
+        # a first window (from S_in and hist): fills the checkpoint, capture and window of a set
+        gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_out"], d["H"],
+                        d["o"], wl.Hk, S_in=d["S_in"], hist=d["hist"], S_ckpt=d["S_ckpt"], win=d["win"])
+
+    def fused(d):
+        # one whole step in one launch, chained as in a serving loop: set r continues from set r-1's
+        # window (its accept length picks the start state and the conv history) and writes its own
+        pv = sets[set_index(d) - 1]
+        gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_out"], d["H"],
+                        d["o"], wl.Hk, prev=(pv["accept"], pv["S_ckpt"], pv["H"], pv["S_out"], pv["win"]),
+                        S_ckpt=d["S_ckpt"], win=d["win"])
+
+    mode = "three" if args.three_kernel else ("two" if args.two_kernel else "fused")
+    if mode == "three":
         def step(d):
             conv(d)
             verify(d)
             rollback(d)
-    else:
+    elif mode == "two":
         def step(d):
             rollback_conv(d)
             verify(d)
+    else:
+        step = fused
 
-    # a valid previous window for the fused step: one conv step into win_prev
+    # a valid previous window for rollback_conv_step (one conv step into win_prev), and for the fused
+    # step a first window of every set
     for d in sets:
         gdn.conv_step(d["x"], d["w"], d["hist"], d["y"], d["win_prev"])
+        fused_first(d)
 
     # ---------------------------------------------------------------- warmup
     for s in range(args.warmup):
@@ -515,6 +551,7 @@ def main():
             torch.cuda.synchronize()
             return sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) * 1e3
 
+    t_fused = kernel_us(fused)
     t_ver = kernel_us(verify)
     t_conv = kernel_us(conv)
     t_rb = kernel_us(rollback)
@@ -540,9 +577,15 @@ def main():
     t_replay_step = kernel_us(replay_step)
 
     vb = verify_bytes(wl)
-    achieved = vb / (t_ver * 1e-6) / 1e9
-    sha = source_sha("gdn_verify.hip", "gdn_device.h")
-    traffic = read_traffic("gdn_verify", wl.name, sha)
+    sb = step_bytes(wl)
+    sha = source_sha("gdn_verify.hip", "gdn_device.h", "gdn_conv_math.h")
+    if mode == "fused":
+        # the dominant (and only) kernel of the step: gdn_verify_step
+        dom, dom_bytes, dom_us = "gdn_verify_step", sb, t_fused
+    else:
+        dom, dom_bytes, dom_us = "gdn_verify", vb, t_ver
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    traffic = read_traffic(dom, wl.name, sha)
     mean_rb_bytes = sum(rollback_bytes(wl, [a]) for a in accepts) / len(accepts)
 
     out = {
@@ -561,8 +604,11 @@ def main():
         "config": {
             "workload": wl.name, "B": wl.B, "K": wl.T, "Hk": wl.Hk, "Hv": wl.Hv, "dk": wl.dk, "dv": wl.dv,
             "C": wl.C, "conv_width": wl.W, "io_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
-            "step": ("conv_step + verify(capture) + rollback" if args.three_kernel else
-                     "rollback_conv_step (rollback of the previous window + conv_step, one launch) + verify(capture)"),
+            "step": {"three": "conv_step + verify(capture) + rollback",
+                     "two": "rollback_conv_step (rollback of the previous window + conv_step, one launch) + "
+                            "verify(capture)",
+                     "fused": "verify_step: rollback of the previous window (start state and conv history picked "
+                              "by its accept length) + conv_step + verify(capture), one launch"}[mode],
             "buffer_sets": R,
             "working_set_MB": round(R * set_bytes / 2 ** 20, 1), "launch": "eager" if args.eager else ("hip_graph, %d steps per graph" % per_graph),
         },
@@ -575,7 +621,11 @@ def main():
             "traffic": traffic,
         },
         "detail": {
-            "kernel": "gdn_verify",
+            "kernel": dom,
+            "kernel_bytes_per_launch": dom_bytes,
+            "kernel_us": round(dom_us, 3),
+            "verify_step_us": round(t_fused, 3),
+            "verify_step_bytes_per_launch": sb,
             "verify_bytes_per_launch": vb,
             "verify_us": round(t_ver, 3),
             "conv_us": round(t_conv, 3),

@@ -284,6 +284,44 @@ int gdn_prefill_chunked(const void *qkv, const void *beta_raw, const void *alpha
                         int in_dtype, int o_dtype, float l2_eps, void *stream);
 
 /*
+ * gdn_verify_step -- one whole verify step of the layer in one launch: the
+ * rollback of the previous window, the conv step of this window and the GDN
+ * verify with capture (gdn_rollback + gdn_conv_step + gdn_verify, the same
+ * arithmetic and the same bits, with no state copy and no intermediate
+ * launch; the pages' step in atlas PR #297 and lucebox PR #637 as above).
+ *
+ * Previous window (accept_prev != NULL): sequence b starts from the state its
+ * accept length a = accept_prev[b] (clamped into 0..K_prev) selects --
+ * S_prev_ckpt[b] (a = 0), H_prev[b][a-1] (0 < a < K_prev) or S_prev_out[b]
+ * (a = K_prev) -- and from the conv history rows a .. a+W-2 of win_prev.
+ * First window (accept_prev == NULL): from S_in and hist.
+ *   x [B][K][C] raw tokens, w [C][W] float taps, gates, dt_bias, A_log,
+ *   gate_stride: as gdn_conv_step and gdn_verify_ex;
+ *   S_prev_ckpt, S_prev_out [B][Hv][dv][dk], H_prev [B][K_prev-1][...],
+ *   win_prev [B][W-1+K_prev][C]: the previous step's S_ckpt, S_out, H, win;
+ *   S_in [B][Hv][dv][dk], hist [B][W-1][C]: the first window's start.
+ * Outputs:
+ *   S_ckpt [B][Hv][dv][dk]  this window's start state (nullable; the next
+ *                           step's S_prev_ckpt)
+ *   S_out, H, o             as gdn_verify (H nullable: no capture)
+ *   y [B][K][C]             the conv outputs (nullable)
+ *   win [B][W-1+K][C]       this window's conv window (nullable; the next
+ *                           step's win_prev)
+ * W must be 4.  Every output is disjoint from every input and from the other
+ * outputs: a loop keeps two sets of (S_ckpt, S_out, H, win) and alternates
+ * them.  To leave the loop, gdn_rollback(accept, K, S_ckpt, H, S_out, hist,
+ * win) materialises the state and the history.
+ */
+int gdn_verify_step(const int32_t *accept_prev, int K_prev, const float *S_prev_ckpt,
+                    const float *H_prev, const float *S_prev_out, const void *win_prev,
+                    const float *S_in, const void *hist,
+                    const void *x, const float *w, const void *beta_raw, const void *alpha,
+                    int gate_stride, const float *dt_bias, const float *A_log,
+                    float *S_ckpt, float *S_out, float *H, void *o, void *y, void *win,
+                    int B, int K, int Hk, int Hv, int dk, int dv, int W,
+                    int in_dtype, int o_dtype, float l2_eps, void *stream);
+
+/*
  * Tree verify -- the drafter proposes a tree of candidate tokens instead of a
  * chain (lucebox PR #637: DDTree drafting in the commit messages, and the tree
  * variant of the conv, ggml_ssm_conv_tree, in the review excerpt of ggml.c).

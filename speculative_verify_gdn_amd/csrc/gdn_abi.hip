@@ -337,6 +337,79 @@ int gdn_prefill_chunked(const void* qkv, const void* beta_raw, const void* alpha
                          fn);
 }
 
+int gdn_verify_step(const int32_t* accept_prev, int K_prev, const float* S_prev_ckpt, const float* H_prev,
+                    const float* S_prev_out, const void* win_prev, const float* S_in, const void* hist, const void* x,
+                    const float* w, const void* beta_raw, const void* alpha, int gate_stride, const float* dt_bias,
+                    const float* A_log, float* S_ckpt, float* S_out, float* H, void* o, void* y, void* win, int B,
+                    int K, int Hk, int Hv, int dk, int dv, int W, int in_dtype, int o_dtype, float l2_eps,
+                    void* stream)
+{
+    const char* fn = "gdn_verify_step";
+    int rc = check_gdn_shape(fn, B, K, Hk, Hv, dk, dv, in_dtype, o_dtype, l2_eps);
+    if (rc) return rc;
+    REQUIRE(K <= 32, GDN_EUNSUPPORTED, "%s: K = %d > 32", fn, K);
+    REQUIRE(W == 4, GDN_EUNSUPPORTED, "%s: W = %d (the fused step takes conv width 4)", fn, W);
+    REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
+    REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
+            "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
+    if (accept_prev) REQUIRE(K_prev >= 1 && K_prev <= 32, GDN_EINVAL, "%s: K_prev = %d not in 1..32", fn, K_prev);
+    if (B == 0) return ok();
+    REQUIRE(x && w && beta_raw && alpha && S_out && o, GDN_EINVAL, "%s: null pointer", fn);
+    if (accept_prev) {
+        REQUIRE(S_prev_ckpt && S_prev_out && win_prev && (H_prev || K_prev == 1), GDN_EINVAL,
+                "%s: the previous window needs S_prev_ckpt, S_prev_out, win_prev and (K_prev > 1) H_prev", fn);
+    } else {
+        REQUIRE(S_in && hist, GDN_EINVAL, "%s: the first window needs S_in and hist", fn);
+    }
+    REQUIRE(gate_stride >= Hv, GDN_EINVAL, "%s: gate_stride = %d < Hv = %d", fn, gate_stride, Hv);
+    const size_t ie = elem_size(in_dtype), oe = elem_size(o_dtype);
+    auto a16 = [](const void* q) { return q == nullptr || aligned16(q); };
+    REQUIRE(a16(x) && a16(w) && a16(S_prev_ckpt) && a16(H_prev) && a16(S_prev_out) && a16(win_prev) && a16(S_in) &&
+                a16(hist) && a16(dt_bias) && a16(A_log) && a16(S_ckpt) && a16(S_out) && a16(H) && a16(o) && a16(y) &&
+                a16(win),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(((uintptr_t)beta_raw % ie) == 0 && ((uintptr_t)alpha % ie) == 0 && ((uintptr_t)accept_prev & 3) == 0,
+            GDN_EINVAL, "%s: gate or accept pointers not aligned to their element size", fn);
+    const size_t C = (size_t)2 * Hk * dk + (size_t)Hv * dv;
+    const size_t st = (size_t)Hv * dv * dk * 4;
+    const size_t gspan = ((size_t)B * K - 1) * gate_stride + Hv;
+    const Span ins[] = {Span{x, (size_t)B * K * C * ie},
+                        Span{w, C * 4 * 4},
+                        Span{beta_raw, gspan * ie},
+                        Span{alpha, gspan * ie},
+                        Span{dt_bias, dt_bias ? (size_t)Hv * 4 : 0},
+                        Span{A_log, A_log ? (size_t)Hv * 4 : 0},
+                        Span{accept_prev, accept_prev ? (size_t)B * 4 : 0},
+                        Span{accept_prev ? S_prev_ckpt : nullptr, B * st},
+                        Span{accept_prev ? H_prev : nullptr, H_prev ? (size_t)B * (K_prev - 1) * st : 0},
+                        Span{accept_prev ? S_prev_out : nullptr, B * st},
+                        Span{accept_prev ? win_prev : nullptr, (size_t)B * (W - 1 + K_prev) * C * ie},
+                        Span{accept_prev ? nullptr : S_in, B * st},
+                        Span{accept_prev ? nullptr : hist, (size_t)B * (W - 1) * C * ie}};
+    const Span outs[] = {Span{S_ckpt, B * st}, Span{S_out, B * st}, Span{H, H ? (size_t)B * (K - 1) * st : 0},
+                         Span{o, (size_t)B * K * Hv * dv * oe}, Span{y, (size_t)B * K * C * ie},
+                         Span{win, (size_t)B * (W - 1 + K) * C * ie}};
+    for (const Span& q : outs)
+        for (const Span& i : ins) REQUIRE(!overlap(q, i), GDN_EINVAL, "%s: an output overlaps an input", fn);
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j) REQUIRE(!overlap(outs[i], outs[j]), GDN_EINVAL, "%s: two outputs overlap", fn);
+    gdn::VerifyArgs a{x, beta_raw, alpha, dt_bias, A_log, accept_prev ? nullptr : S_in, S_out, H, o, B, K, Hk, Hv,
+                      dk, dv, l2_eps, nullptr, gate_stride};
+    a.x = x;
+    a.w = w;
+    a.hsrc = accept_prev ? win_prev : hist;
+    a.hrows = accept_prev ? W - 1 + K_prev : W - 1;
+    a.acc_prev = accept_prev;
+    a.Kp = accept_prev ? K_prev : 0;
+    a.Sp_ckpt = S_prev_ckpt;
+    a.Sp_H = H_prev;
+    a.Sp_out = S_prev_out;
+    a.S_ckpt = S_ckpt;
+    a.y = y;
+    a.win = win;
+    return launch_status(gdn::launch_verify(a, in_dtype == GDN_BF16, o_dtype == GDN_BF16, (hipStream_t)stream), fn);
+}
+
 int gdn_conv_tree(const void* x, const float* w, const void* hist, const int32_t* parent, void* y, int B, int N,
                   int C, int W, int io_dtype, void* stream)
 {

@@ -34,6 +34,19 @@ struct VerifyArgs {
     int gstride = 0;                // elements between the gate rows of consecutive tokens (0: Hv)
     const int32_t* replay = nullptr;  // [B] accept lengths: rebuild S_out from S_in over that many tokens
     const int32_t* parent = nullptr;  // [B][K] tree verify: parent node per node (H then holds K states)
+    // fused step (conv width 4): the conv of the window and the start state picked from the previous window
+    const void* x = nullptr;           // [B][K][C] raw tokens (qkv unused)
+    const float* w = nullptr;          // [C][4] taps
+    const void* hsrc = nullptr;        // history rows: previous window [B][hrows][C] (rows a..a+2) or hist
+    int hrows = 0;                     // rows per sequence of hsrc
+    const int32_t* acc_prev = nullptr; // [B] accept lengths of the previous window, or nullptr: S_in and hist
+    int Kp = 0;                        // previous window length
+    const float* Sp_ckpt = nullptr;    // previous window's start state, capture and final state
+    const float* Sp_H = nullptr;
+    const float* Sp_out = nullptr;
+    float* S_ckpt = nullptr;           // [B][Hv][dv][dk] this window's start state, or nullptr
+    void* y = nullptr;                 // [B][K][C] conv outputs, or nullptr
+    void* win = nullptr;               // [B][3+K][C] this window's conv window, or nullptr
 };
 
 // largest draft tree (nodes per sequence) of the tree calls

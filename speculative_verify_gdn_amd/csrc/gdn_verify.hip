@@ -46,6 +46,7 @@
 //      which also gives o_t; as soon as u_t is known every lane streams
 //      H_t = gamma_t H_{t-1} + u_t k^_t with one 16-byte store -- the bulk of
 //      the bytes of the whole step.
+#include "gdn_conv_math.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -223,7 +224,46 @@ __device__ __forceinline__ float4 lds4(const void* p)
     }
 }
 
-template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT, bool TREE>
+// element e of a 16-byte piece of EPV bf16 or float values
+template <bool BF16>
+__device__ __forceinline__ float piece_elem(const uint4& u, int e)
+{
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (BF16) return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+    else return __uint_as_float(w[e]);
+}
+
+// the conv step of one 16-byte piece: EPV channels of one token from the CW
+// window rows r[0..CW-1] (oldest first) and the channels' taps tp[e*CW + j];
+// the same arithmetic and rounding as the conv kernels
+template <bool BF16, int CW>
+__device__ __forceinline__ uint4 conv_piece(const uint4 (&r)[CW], const float* tp)
+{
+    constexpr int EPV = BF16 ? 8 : 4;
+    float out[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+        float tap[CW], col[CW];
+#pragma unroll
+        for (int jj = 0; jj < CW; ++jj) {
+            tap[jj] = tp[e * CW + jj];
+            col[jj] = piece_elem<BF16>(r[jj], e);
+        }
+        out[e] = conv_silu(conv_pre<CW>(tap, col));
+    }
+    uint32_t w[4];
+    if constexpr (BF16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = (uint32_t)f32_to_bf16(out[2 * q]) | ((uint32_t)f32_to_bf16(out[2 * q + 1]) << 16);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = __float_as_uint(out[q]);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT, bool TREE, bool STEP>
 __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
 {
     constexpr int LPR = DK / 4;                  // lanes per state row (one float4 each)
@@ -267,41 +307,93 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     const int hk = h / (Hv / Hk);
     const size_t SD = (size_t)dv * DK;
     const float* Sh = a.S_in + ((size_t)b * Hv + h) * SD;
-    const in_t* X = reinterpret_cast<const in_t*>(a.qkv) + (size_t)b * Kb * C;   // this sequence's rows
+    // this sequence's rows: q|k|v, or for the fused step the raw tokens before the conv
+    const in_t* X = reinterpret_cast<const in_t*>(STEP ? a.x : a.qkv) + (size_t)b * Kb * C;
     const size_t qoff = (size_t)hk * DK, koff = (size_t)(Hk + hk) * DK;
+    constexpr int EPV = IN_BF16 ? 8 : 4;         // elements per 16-byte vector
+    constexpr int VPR = DK / EPV;                // consecutive threads per token row
+    constexpr int CW = 4;                        // conv width of the fused step
+    // fused step: the start state and the W-1 history rows come from the previous
+    // window, picked by its accept length a -- S_ckpt (a = 0), H[a-1], or its final
+    // state (a = K_prev), and window rows a .. a+W-2 -- or from S_in and hist
+    const in_t* HS = nullptr;
+    if constexpr (STEP) {
+        int ap = 0;
+        if (a.acc_prev) {
+            ap = min(max(a.acc_prev[b], 0), a.Kp);
+            const size_t hb = ((size_t)b * Hv + h) * SD;
+            Sh = ap == 0 ? a.Sp_ckpt + hb
+                         : (ap == a.Kp ? a.Sp_out + hb : a.Sp_H + (((size_t)b * (a.Kp - 1) + ap - 1) * Hv + h) * SD);
+        }
+        HS = reinterpret_cast<const in_t*>(a.hsrc) + ((size_t)b * a.hrows + ap) * C;
+    }
+    // row r of this window [W-1 history rows ; K tokens]
+    auto wrow = [&](int r) -> const in_t* { return r < CW - 1 ? HS + (size_t)r * C : X + (size_t)(r - (CW - 1)) * C; };
 
     f32x4_t S;
     // ---- 1. stage q, k and their norms, the state rows, v; gates and their running sums.
     // Every global load of the phase is issued first (addresses clamped into
     // range instead of branching), so they are in flight together.
     {
-        constexpr int EPV = IN_BF16 ? 8 : 4;     // elements per 16-byte vector
-        constexpr int VPR = DK / EPV;            // consecutive threads per token row
         static_assert(64 % VPR == 0 && (KP * VPR) % 64 == 0, "a token row is a lane group of one wave");
         constexpr int NQ = (KP * VPR + kThreads - 1) / kThreads;     // q/k pieces per thread
         constexpr int NV = (KMAX * RPG + kThreads - 1) / kThreads;   // v elements per thread
         uint4 qv[NQ], kv[NQ];
+        // fused step: thread tid convolves one q|k channel of the key head over a run of
+        // TPG tokens (its W-1+TPG window rows and its taps: coalesced loads, one read per
+        // row); threads (t, row) convolve the v channels; the window rows this step keeps
+        // for the next one are loaded here too
+        constexpr int QKC = 2 * DK;                                   // q|k channels
+        constexpr int TPC = kThreads / QKC;                           // threads per channel
+        static_assert(kThreads % QKC == 0, "whole channels per workgroup");
+        constexpr int TPG = STEP ? (KP + TPC - 1) / TPC : 1;          // tokens per thread
+        constexpr int NXR = STEP ? TPG + CW - 1 : 1;
+        constexpr int NWV = STEP ? ((CW - 1 + KMAX) * RPG + kThreads - 1) / kThreads : 1;
+        const int chi = tid % QKC, t0 = (tid / QKC) * TPG;
+        const size_t choff = chi < DK ? qoff + chi : koff + (chi - DK);
+        float xrow[NXR];
+        float4 tp = make_float4(0.f, 0.f, 0.f, 0.f);
+        float vrow[STEP ? NV : 1][CW];
+        float4 vtp[STEP ? NV : 1];
+        float wv[NWV];
+        if constexpr (STEP) {
+            tp = *reinterpret_cast<const float4*>(a.w + choff * CW);
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            const int idx = tid + n * kThreads;
-            if (idx < KP * VPR) {
-                const int t = idx / VPR, cc = (idx % VPR) * EPV;
-                const in_t* row = X + (size_t)(t < K ? t : K - 1) * C;
-                qv[n] = *reinterpret_cast<const uint4*>(row + qoff + cc);
-                kv[n] = *reinterpret_cast<const uint4*>(row + koff + cc);
+            for (int m = 0; m < NXR; ++m) {
+                const int r = t0 + m;
+                xrow[m] = load1<IN_BF16>(wrow(r < CW - 2 + K ? r : CW - 2 + K), choff);
+            }
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                const int idx = tid + n * kThreads;
+                const int t = idx / RPG, rr = idx % RPG;
+                const int gr = blockIdx.x * RPG + rr;
+                const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
+                const int tc = t < K ? t : K - 1;
+                vtp[n] = *reinterpret_cast<const float4*>(a.w + vch * CW);
+#pragma unroll
+                for (int jj = 0; jj < CW; ++jj) vrow[n][jj] = load1<IN_BF16>(wrow(tc + jj), vch);
+            }
+#pragma unroll
+            for (int n = 0; n < NWV; ++n) {
+                const int idx = tid + n * kThreads;
+                const int r = idx / RPG, gr = blockIdx.x * RPG + idx % RPG;
+                const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
+                wv[n] = load1<IN_BF16>(wrow(r < CW - 2 + K ? r : CW - 2 + K), vch);
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) {
+                const int idx = tid + n * kThreads;
+                if (idx < KP * VPR) {
+                    const int t = idx / VPR, cc = (idx % VPR) * EPV;
+                    const in_t* row = X + (size_t)(t < K ? t : K - 1) * C;
+                    qv[n] = *reinterpret_cast<const uint4*>(row + qoff + cc);
+                    kv[n] = *reinterpret_cast<const uint4*>(row + koff + cc);
+                }
             }
         }
         f32x4_t S0 = load_f4(Sh + (size_t)ic * DK + c);
-        float vv[NV];
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            const int idx = tid + n * kThreads;
-            const int t = idx / RPG, rr = idx % RPG;
-            const int gr = blockIdx.x * RPG + rr;
-            const in_t* row = X + (size_t)(t < K ? t : (K - 1)) * C;
-            vv[n] = idx < KMAX * RPG ? load1<IN_BF16>(row, 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1))
-                                     : 0.f;
-        }
         float braw = 0.f, bal = 0.f;
         int par = -1;
         if (wave == kWaves - 1 && lane < K) {
@@ -310,21 +402,105 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             bal = load1<IN_BF16>(a.alpha, gi);
             if constexpr (TREE) par = a.parent[(size_t)b * Kb + lane];
         }
-
+        float vv[NV];
+        if constexpr (!STEP) {
 #pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            const int idx = tid + n * kThreads;
-            if (idx < KP * VPR) {
-                const int t = idx / VPR, cc = (idx % VPR) * EPV;
-                if (t >= K) qv[n] = kv[n] = make_uint4(0, 0, 0, 0);
-                *reinterpret_cast<uint4*>(&sm.q[t][cc]) = qv[n];
-                *reinterpret_cast<uint4*>(&sm.k[t][cc]) = kv[n];
-                // 1/|q_t|, 1/|k_t| (padded tokens keep q^ = k^ = 0, never 0 * 1/sqrt(0))
-                const float sq = group_sum<VPR>(sumsq16<IN_BF16>(qv[n]));
-                const float sk = group_sum<VPR>(sumsq16<IN_BF16>(kv[n]));
-                if (cc == 0) {
-                    sm.tok[t].z = t < K ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.0f;
-                    sm.tok[t].w = t < K ? __builtin_amdgcn_rsqf(sq + a.eps) : 0.0f;
+            for (int n = 0; n < NV; ++n) {
+                const int idx = tid + n * kThreads;
+                const int t = idx / RPG, rr = idx % RPG;
+                const int gr = blockIdx.x * RPG + rr;
+                const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
+                vv[n] = idx < KMAX * RPG ? load1<IN_BF16>(X + (size_t)(t < K ? t : K - 1) * C, vch) : 0.f;
+            }
+        }
+        if constexpr (STEP) {
+            // the checkpoint: this window's start state
+            if (a.S_ckpt && live) store_f4<true>(a.S_ckpt + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S0);
+            // the conv, as the conv kernels compute it; the conv outputs and the window
+            // rows are written by one workgroup per key head (q, k) and by each
+            // workgroup for its own rows (v)
+            const bool qk_writer = (h % (Hv / Hk)) == 0 && blockIdx.x == 0;
+            in_t(*Xd)[Smem::QW] = chi < DK ? sm.q : sm.k;
+            const int cl = chi < DK ? chi : chi - DK;
+            const float tap[CW] = {tp.x, tp.y, tp.z, tp.w};
+#pragma unroll
+            for (int m = 0; m < TPG; ++m) {
+                const int t = t0 + m;
+                if (t < KP) {
+                    const float col[CW] = {xrow[m], xrow[m + 1], xrow[m + 2], xrow[m + 3]};
+                    float v = t < K ? conv_silu(conv_pre<CW>(tap, col)) : 0.f;
+                    if constexpr (IN_BF16) {
+                        const uint16_t hb = f32_to_bf16(v);
+                        Xd[t][cl] = hb;
+                        if (a.y && qk_writer && t < K)
+                            reinterpret_cast<uint16_t*>(a.y)[((size_t)b * Kb + t) * C + choff] = hb;
+                    } else {
+                        Xd[t][cl] = v;
+                        if (a.y && qk_writer && t < K) reinterpret_cast<float*>(a.y)[((size_t)b * Kb + t) * C + choff] = v;
+                    }
+                }
+            }
+            in_t* Wb = a.win ? reinterpret_cast<in_t*>(a.win) + (size_t)b * (CW - 1 + Kb) * C : nullptr;
+            if (Wb && qk_writer) {
+                // rows t0+W-1 .. t0+TPG+W-2 (the newest of each token), and the history rows for t0 = 0
+#pragma unroll
+                for (int m = 0; m < NXR; ++m) {
+                    const int r = t0 + m;
+                    if ((m >= CW - 1 || t0 == 0) && r < CW - 1 + K) store1<IN_BF16>(Wb, (size_t)r * C + choff, xrow[m]);
+                }
+            }
+            if (Wb) {
+#pragma unroll
+                for (int n = 0; n < NWV; ++n) {
+                    const int idx = tid + n * kThreads;
+                    const int r = idx / RPG, gr = blockIdx.x * RPG + idx % RPG;
+                    if (idx < (CW - 1 + KMAX) * RPG && r < CW - 1 + K && gr < dv)
+                        store1<IN_BF16>(Wb, (size_t)r * C + 2 * (size_t)Hk * DK + (size_t)h * dv + gr, wv[n]);
+                }
+            }
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                const int idx = tid + n * kThreads;
+                const int t = idx / RPG, rr = idx % RPG;
+                const int gr = blockIdx.x * RPG + rr;
+                const float tv[CW] = {vtp[n].x, vtp[n].y, vtp[n].z, vtp[n].w};
+                float v = conv_silu(conv_pre<CW>(tv, vrow[n]));
+                if constexpr (IN_BF16) v = bf16_to_f32(f32_to_bf16(v));
+                vv[n] = idx < KMAX * RPG ? v : 0.f;
+                if (a.y && idx < KMAX * RPG && t < K && gr < dv)
+                    store1<IN_BF16>(a.y, ((size_t)b * Kb + t) * C + 2 * (size_t)Hk * DK + (size_t)h * dv + gr, v);
+            }
+            __syncthreads();  // q, k of every token in LDS
+            // their norms, as the staging threads of the plain verify form them
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) {
+                const int idx = tid + n * kThreads;
+                if (idx < KP * VPR) {
+                    const int t = idx / VPR, cc = (idx % VPR) * EPV;
+                    const float sq = group_sum<VPR>(sumsq16<IN_BF16>(*reinterpret_cast<const uint4*>(&sm.q[t][cc])));
+                    const float sk = group_sum<VPR>(sumsq16<IN_BF16>(*reinterpret_cast<const uint4*>(&sm.k[t][cc])));
+                    if (cc == 0) {
+                        sm.tok[t].z = t < K ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.0f;
+                        sm.tok[t].w = t < K ? __builtin_amdgcn_rsqf(sq + a.eps) : 0.0f;
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int n = 0; n < NQ; ++n) {
+                const int idx = tid + n * kThreads;
+                if (idx < KP * VPR) {
+                    const int t = idx / VPR, cc = (idx % VPR) * EPV;
+                    if (t >= K) qv[n] = kv[n] = make_uint4(0, 0, 0, 0);
+                    *reinterpret_cast<uint4*>(&sm.q[t][cc]) = qv[n];
+                    *reinterpret_cast<uint4*>(&sm.k[t][cc]) = kv[n];
+                    // 1/|q_t|, 1/|k_t| (padded tokens keep q^ = k^ = 0, never 0 * 1/sqrt(0))
+                    const float sq = group_sum<VPR>(sumsq16<IN_BF16>(qv[n]));
+                    const float sk = group_sum<VPR>(sumsq16<IN_BF16>(kv[n]));
+                    if (cc == 0) {
+                        sm.tok[t].z = t < K ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.0f;
+                        sm.tok[t].w = t < K ? __builtin_amdgcn_rsqf(sq + a.eps) : 0.0f;
+                    }
                 }
             }
         }
@@ -563,8 +739,9 @@ hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
 {
     constexpr int RPG = 1024 / DK;
     dim3 grid((a.dv + RPG - 1) / RPG, a.Hv, a.B);
-    if (a.parent) verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, true><<<grid, dim3(kThreads), 0, s>>>(a);
-    else verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false><<<grid, dim3(kThreads), 0, s>>>(a);
+    if (a.parent) verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, true, false><<<grid, dim3(kThreads), 0, s>>>(a);
+    else if (a.x) verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, true><<<grid, dim3(kThreads), 0, s>>>(a);
+    else verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, false><<<grid, dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 

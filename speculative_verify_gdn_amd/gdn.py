@@ -22,7 +22,7 @@ GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked",
            "gdn_rollback_conv_step", "gdn_conv_step_ex", "gdn_verify_ex", "gdn_rollback_ex", "gdn_replay",
-           "gdn_conv_tree", "gdn_verify_tree", "gdn_rollback_tree")
+           "gdn_conv_tree", "gdn_verify_tree", "gdn_rollback_tree", "gdn_verify_step")
 
 
 class GdnError(RuntimeError):
@@ -57,6 +57,8 @@ def load(path: str = LIB_PATH):
         lib.gdn_verify_ex.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
         lib.gdn_rollback_ex.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
         lib.gdn_replay.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+        lib.gdn_verify_step.argtypes = [P, I, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P,
+                                        I, I, I, I, I, I, I, I, I, F, P]
         lib.gdn_conv_tree.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
         lib.gdn_verify_tree.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
         lib.gdn_rollback_tree.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
@@ -217,3 +219,32 @@ def rollback_tree(node, parent, S_in, H, S_out, x=None, hist=None, stream=None):
         W, C, io = 2, 1, GDN_F32
     _check(load().gdn_rollback_tree(_p(node), _p(parent), N, _p(S_in), _p(H), _p(S_out), _p(x), _p(hist),
                                     B, Hv, dv, dk, C, W, io, _stream(stream)))
+
+
+def verify_step(x, w, beta_raw, alpha, dt_bias, A_log, S_out, H, o, Hk, prev=None, S_in=None, hist=None,
+                S_ckpt=None, y=None, win=None, eps=1e-6, gate_stride=None, stream=None):
+    """gdn_verify_step: rollback of the previous window + conv step + verify in one launch.
+
+    prev = (accept, S_ckpt, H, S_out, win) of the previous step (K_prev from its window), or None with
+    S_in, hist for the first window.  x [B][K][C] raw tokens, w [C][4]; outputs S_out, H, o and the
+    optional S_ckpt (this window's start state), y (conv outputs) and win (this window's conv window)."""
+    if gate_stride is None:
+        _dev(beta_raw, alpha)
+        gate_stride = S_out.shape[1]
+    elif not (beta_raw.is_cuda and alpha.is_cuda):
+        raise ValueError("libgdn takes device tensors")
+    _dev(x, w, dt_bias, A_log, S_out, H, o, S_in, hist, S_ckpt, y, win)
+    B, K, C = x.shape
+    _, Hv, dv, dk = S_out.shape
+    W = w.shape[1]
+    if prev is not None:
+        acc, p_ckpt, p_H, p_out, p_win = prev
+        _dev(acc, p_ckpt, p_H, p_out, p_win)
+        K_prev = p_win.shape[1] - (W - 1)
+    else:
+        acc = p_ckpt = p_H = p_out = p_win = None
+        K_prev = 0
+    _check(load().gdn_verify_step(_p(acc), int(K_prev), _p(p_ckpt), _p(p_H), _p(p_out), _p(p_win), _p(S_in),
+                                  _p(hist), _p(x), _p(w), _p(beta_raw), _p(alpha), int(gate_stride), _p(dt_bias),
+                                  _p(A_log), _p(S_ckpt), _p(S_out), _p(H), _p(o), _p(y), _p(win), B, K, Hk, Hv, dk,
+                                  dv, W, _dtype(x), _dtype(o), float(eps), _stream(stream)))

@@ -334,3 +334,38 @@ def test_tree_calls_empty_batch_are_ok(lib):
     assert verify_tree_call(lib, B=0) == gdn.GDN_OK
     assert rollback_tree_call(lib, B=0) == gdn.GDN_OK
     assert rollback_tree_call(lib, x=None, hist=None, B=0) == gdn.GDN_OK
+
+
+def step_call(lib, **kw):
+    a = dict(acc=p(0), Kp=16, pck=p(1), pH=p(2), pout=p(3), pwin=p(4), S_in=None, hist=None, x=p(5), w=p(6),
+             beta=p(7), alpha=p(8), gs=2, dt=p(9), alog=p(10), ck=p(11), S_out=p(12), H=p(13), o=p(14), y=p(15),
+             win=p(16), B=1, K=16, Hk=2, Hv=2, dk=32, dv=32, W=4, ind=gdn.GDN_BF16, od=gdn.GDN_F32, eps=1e-6)
+    a.update(kw)
+    return lib.gdn_verify_step(a["acc"], a["Kp"], a["pck"], a["pH"], a["pout"], a["pwin"], a["S_in"], a["hist"],
+                               a["x"], a["w"], a["beta"], a["alpha"], a["gs"], a["dt"], a["alog"], a["ck"],
+                               a["S_out"], a["H"], a["o"], a["y"], a["win"], a["B"], a["K"], a["Hk"], a["Hv"],
+                               a["dk"], a["dv"], a["W"], a["ind"], a["od"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(W=3), gdn.GDN_EUNSUPPORTED),                       # the fused step takes conv width 4
+    (dict(K=33), gdn.GDN_EUNSUPPORTED),
+    (dict(Kp=0), gdn.GDN_EINVAL),
+    (dict(pck=None), gdn.GDN_EINVAL),                        # the previous window needs its checkpoint
+    (dict(pH=None), gdn.GDN_EINVAL),                         # ... and its capture when K_prev > 1
+    (dict(acc=None), gdn.GDN_EINVAL),                        # first window without S_in / hist
+    (dict(x=None), gdn.GDN_EINVAL),
+    (dict(S_out=p(3)), gdn.GDN_EINVAL),                      # S_out over the previous final state
+    (dict(win=p(4)), gdn.GDN_EINVAL),                        # win over win_prev
+    (dict(ck=p(12)), gdn.GDN_EINVAL),                        # two outputs overlap
+    (dict(acc=ctypes.c_void_p(A + 2)), gdn.GDN_EINVAL),      # accept not 4-byte aligned
+    (dict(gs=1), gdn.GDN_EINVAL),
+])
+def test_verify_step_rejects(lib, kw, code):
+    assert step_call(lib, **kw) == code
+
+
+def test_verify_step_first_window_and_empty_batch(lib):
+    assert step_call(lib, B=0) == gdn.GDN_OK
+    assert step_call(lib, acc=None, S_in=p(20), hist=p(21), B=0) == gdn.GDN_OK
+    assert step_call(lib, acc=None, S_in=p(20), hist=None) == gdn.GDN_EINVAL

@@ -1,0 +1,176 @@
+"""GPU parity of the fused verify step (gdn_verify_step): one launch that
+rolls back the previous window, runs the conv step of this window and the GDN
+verify with capture.
+
+It must give the bits of the separate calls (gdn_rollback, gdn_conv_step,
+gdn_verify on the same inputs) -- y, the window, the checkpoint, S_out, every
+H_t and o -- and, through them, the oracle: the conv bit for bit against the
+oracle's same-precision conv, the GDN within 2e-3 * ||S_ref||_F per head.
+Steps are chained as in a serving loop (two buffer sets alternating), with
+accept lengths covering 0, partial and the whole window.  Every test prints
+its case before touching the device.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from speculative_verify_gdn_amd import gdn, synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def say(*a):
+    print("[gpu case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(t):
+    return t.contiguous().cuda()
+
+
+def f64(t):
+    return t.double().cpu().numpy()
+
+
+def outputs(wl, o_dtype=torch.float32):
+    B, K, Hv, dv, dk, C, W = wl.B, wl.T, wl.Hv, wl.dv, wl.dk, wl.C, wl.W
+    io = torch.bfloat16 if wl.bf16 else torch.float32
+    return dict(S_ckpt=torch.empty(B, Hv, dv, dk, device="cuda"), S_out=torch.empty(B, Hv, dv, dk, device="cuda"),
+                H=torch.empty(B, K - 1, Hv, dv, dk, device="cuda") if K > 1 else None,
+                o=torch.empty(B, K, Hv, dv, device="cuda", dtype=o_dtype),
+                y=torch.empty(B, K, C, device="cuda", dtype=io), win=torch.empty(B, W - 1 + K, C, device="cuda", dtype=io))
+
+
+def fused(wl, d, out, prev=None):
+    gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], out["S_out"], out["H"],
+                    out["o"], wl.Hk, prev=prev, S_in=None if prev else d["S_in"], hist=None if prev else d["hist"],
+                    S_ckpt=out["S_ckpt"], y=out["y"], win=out["win"])
+
+
+def separate(wl, d, out, S_start, hist):
+    """conv step from hist, verify from S_start: what the fused step must reproduce."""
+    hist = hist.clone()
+    gdn.conv_step(d["x"], d["w"], hist, out["y"], out["win"])
+    gdn.verify(out["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], S_start, out["S_out"], out["H"],
+               out["o"], wl.Hk)
+    out["S_ckpt"].copy_(S_start)
+
+
+def assert_same(a, b, what):
+    for k in ("S_ckpt", "S_out", "H", "o", "y", "win"):
+        if a[k] is None:
+            continue
+        assert torch.equal(a[k], b[k]), "%s: %s differs" % (what, k)
+
+
+CASES = [
+    ("verify16", dict(B=4, Hk=4, Hv=12), [0, 5, 16, 11]),
+    ("verify16", dict(B=2, Hk=2, Hv=6, T=7), [7, 3]),
+    ("verify16", dict(B=2, Hk=2, Hv=6, T=32), [31, 0]),
+    ("verify16", dict(B=1, Hk=2, Hv=6, T=1), [1]),
+    ("verify16", dict(B=3, Hk=2, Hv=4, dk=64, dv=64), [2, 16, 0]),
+    ("verify16", dict(B=2, Hk=2, Hv=4, dk=32, dv=32, T=9), [4, 9]),
+    ("tiny", dict(B=2), [1, 4]),                                   # fp32 inputs
+]
+
+
+@pytest.mark.parametrize("name,over,acc", CASES)
+def test_fused_step_equals_separate_calls(name, over, acc):
+    wl = synth.small(name, **over)
+    say("verify_step", name, over, "accept", acc)
+    inp1 = synth.make_inputs(wl, seed=41)
+    inp2 = synth.make_inputs(wl, seed=42)
+    d1 = {k: dev(v) for k, v in inp1.items()}
+    d2 = {k: dev(v) for k, v in inp2.items()}
+    d2["w"] = d1["w"]
+    accept = torch.tensor(acc, dtype=torch.int32, device="cuda")
+
+    # first window: from S_in and hist
+    A, A_ref = outputs(wl), outputs(wl)
+    fused(wl, d1, A)
+    separate(wl, d1, A_ref, d1["S_in"], d1["hist"])
+    torch.cuda.synchronize()
+    assert_same(A, A_ref, "first window")
+
+    # second window: from the first one's buffers, by accept length
+    Bo, B_ref = outputs(wl), outputs(wl)
+    fused(wl, d2, Bo, prev=(accept, A["S_ckpt"], A["H"], A["S_out"], A["win"]))
+    S_start = torch.empty_like(d1["S_in"])
+    S_start.copy_(A_ref["S_out"])
+    hist = d1["hist"].clone()
+    gdn.rollback(accept, wl.T, A_ref["S_ckpt"], A_ref["H"], S_start, hist, A_ref["win"])
+    separate(wl, d2, B_ref, S_start, hist)
+    torch.cuda.synchronize()
+    assert_same(Bo, B_ref, "second window")
+
+
+def test_fused_step_chain_against_oracle():
+    wl = synth.small("verify16", B=3, Hk=4, Hv=12)
+    acc1 = [4, 0, 16]
+    say("verify_step two windows vs oracle", wl, acc1)
+    inp1 = synth.make_inputs(wl, seed=51)
+    inp2 = synth.make_inputs(wl, seed=52)
+    d1 = {k: dev(v) for k, v in inp1.items()}
+    d2 = {k: dev(v) for k, v in inp2.items()}
+    d2["w"] = d1["w"]
+    A, Bo = outputs(wl), outputs(wl)
+    fused(wl, d1, A)
+    fused(wl, d2, Bo, prev=(torch.tensor(acc1, dtype=torch.int32, device="cuda"), A["S_ckpt"], A["H"], A["S_out"],
+                            A["win"]))
+    torch.cuda.synchronize()
+
+    # oracle: conv, GDN, rollback of window 1; conv, GDN of window 2 from the kept state
+    w = inp1["w"].numpy()
+    y1, _, win1 = oracle.conv_step_f32(inp1["x"].float().numpy(), w, inp1["hist"].float().numpy(), True)
+    y1b = torch.from_numpy(y1).to(torch.bfloat16)
+    gates = lambda inp: (f64(inp["beta_raw"]), f64(inp["alpha"]), f64(inp["dt_bias"]), f64(inp["A_log"]))
+    S1, H1, _ = oracle.gdn_recurrent_f64(f64(y1b), *gates(inp1), f64(inp1["S_in"]), wl.Hk)
+    S_keep = S1.copy()
+    hist2 = np.empty((wl.B, wl.W - 1, wl.C), np.float32)
+    oracle.rollback(acc1, wl.T, f64(inp1["S_in"]), H1, S_keep, win=win1, hist=hist2)
+    y2, _, win2 = oracle.conv_step_f32(inp2["x"].float().numpy(), w, hist2, True)
+    y2b = torch.from_numpy(y2).to(torch.bfloat16)
+    assert torch.equal(Bo["y"].cpu(), y2b)
+    assert torch.equal(Bo["win"].cpu().float(), torch.from_numpy(win2))
+    S2, H2, o2 = oracle.gdn_recurrent_f64(f64(y2b), *gates(inp2), S_keep, wl.Hk)
+
+    def close(gpu, ref, what):
+        err = np.abs(gpu.double().cpu().numpy() - ref).max(axis=(-1, -2))
+        fro = np.linalg.norm(ref, axis=(-1, -2))
+        assert np.all(err <= TOL * fro), "%s: worst %.3g" % (what, float(np.max(err / fro)))
+    close(Bo["S_ckpt"], S_keep, "S_ckpt")
+    close(Bo["S_out"], S2, "S_out")
+    close(Bo["H"], H2, "H")
+    states = np.concatenate([H2, S2[:, None]], axis=1)
+    bound = TOL * np.linalg.norm(states, axis=(-1, -2))[..., None]
+    assert np.all(np.abs(Bo["o"].double().cpu().numpy() - o2) <= bound)
+
+
+def test_fused_step_nullable_outputs():
+    # no checkpoint, no y, no window, no capture: S_out and o as with every output
+    wl = synth.small("verify16", B=2, Hk=2, Hv=6)
+    say("verify_step nullable outputs")
+    inp = synth.make_inputs(wl, seed=61)
+    d = {k: dev(v) for k, v in inp.items()}
+    full = outputs(wl)
+    fused(wl, d, full)
+    S_out = torch.empty_like(full["S_out"])
+    o = torch.empty_like(full["o"])
+    gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], S_out, None, o, wl.Hk,
+                    S_in=d["S_in"], hist=d["hist"])
+    torch.cuda.synchronize()
+    assert torch.equal(S_out, full["S_out"]) and torch.equal(o, full["o"])
