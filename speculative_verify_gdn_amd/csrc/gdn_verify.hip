@@ -263,8 +263,8 @@ __device__ __forceinline__ uint4 conv_piece(const uint4 (&r)[CW], const float* t
     return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT, bool TREE, bool STEP>
-__global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
+template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT, bool TREE, bool STEP, int NG = 1>
+__global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
 {
     constexpr int LPR = DK / 4;                  // lanes per state row (one float4 each)
     constexpr int RPW = 64 / LPR;                // rows per wave
@@ -274,13 +274,18 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
     constexpr int NTL = (RPG + 15) / 16;         // 16-row MFMA blocks
     using Smem = VerifySmem<DK, KP, RPG, IN_BF16, TREE>;
     using in_t = typename Smem::in_t;
-    __shared__ Smem sm;
+    // NG value heads of one key head per workgroup (fused step): group `sub` of four
+    // waves owns head h and its own copy of the head's LDS; the q|k conv of the key
+    // head is shared by the whole workgroup
+    __shared__ Smem smg[NG];
+    const int gtid = threadIdx.x, sub = gtid / kThreads;
+    Smem& sm = smg[sub];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = gtid % kThreads, lane = tid & 63, wave = tid >> 6;
     const int j = lane % LPR;                    // float4 index inside the row
     const int c = 4 * j;
     const int rloc = wave * RPW + lane / LPR;    // row inside the workgroup
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.y * NG + sub, b = blockIdx.z;
     const int i = blockIdx.x * RPG + rloc;
     // Kb: the window of the buffers (strides); K: this sequence's tokens (masks)
     const int Kb = a.K, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
@@ -344,12 +349,12 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
         // row); threads (t, row) convolve the v channels; the window rows this step keeps
         // for the next one are loaded here too
         constexpr int QKC = 2 * DK;                                   // q|k channels
-        constexpr int TPC = kThreads / QKC;                           // threads per channel
-        static_assert(kThreads % QKC == 0, "whole channels per workgroup");
+        constexpr int TPC = kThreads * NG / QKC;                       // threads per channel
+        static_assert((kThreads * NG) % QKC == 0, "whole channels per workgroup");
         constexpr int TPG = STEP ? (KP + TPC - 1) / TPC : 1;          // tokens per thread
         constexpr int NXR = STEP ? TPG + CW - 1 : 1;
         constexpr int NWV = STEP ? ((CW - 1 + KMAX) * RPG + kThreads - 1) / kThreads : 1;
-        const int chi = tid % QKC, t0 = (tid / QKC) * TPG;
+        const int chi = gtid % QKC, t0 = (gtid / QKC) * TPG;
         const size_t choff = chi < DK ? qoff + chi : koff + (chi - DK);
         float xrow[NXR];
         float4 tp = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -419,8 +424,7 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
             // the conv, as the conv kernels compute it; the conv outputs and the window
             // rows are written by one workgroup per key head (q, k) and by each
             // workgroup for its own rows (v)
-            const bool qk_writer = (h % (Hv / Hk)) == 0 && blockIdx.x == 0;
-            in_t(*Xd)[Smem::QW] = chi < DK ? sm.q : sm.k;
+            const bool qk_writer = ((blockIdx.y * NG) % (Hv / Hk)) == 0 && blockIdx.x == 0;
             const int cl = chi < DK ? chi : chi - DK;
             const float tap[CW] = {tp.x, tp.y, tp.z, tp.w};
 #pragma unroll
@@ -431,11 +435,13 @@ __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyArgs a)
                     float v = t < K ? conv_silu(conv_pre<CW>(tap, col)) : 0.f;
                     if constexpr (IN_BF16) {
                         const uint16_t hb = f32_to_bf16(v);
-                        Xd[t][cl] = hb;
+#pragma unroll
+                        for (int g2 = 0; g2 < NG; ++g2) (chi < DK ? smg[g2].q : smg[g2].k)[t][cl] = hb;
                         if (a.y && qk_writer && t < K)
                             reinterpret_cast<uint16_t*>(a.y)[((size_t)b * Kb + t) * C + choff] = hb;
                     } else {
-                        Xd[t][cl] = v;
+#pragma unroll
+                        for (int g2 = 0; g2 < NG; ++g2) (chi < DK ? smg[g2].q : smg[g2].k)[t][cl] = v;
                         if (a.y && qk_writer && t < K) reinterpret_cast<float*>(a.y)[((size_t)b * Kb + t) * C + choff] = v;
                     }
                 }
@@ -739,9 +745,25 @@ hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
 {
     constexpr int RPG = 1024 / DK;
     dim3 grid((a.dv + RPG - 1) / RPG, a.Hv, a.B);
-    if (a.parent) verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, true, false><<<grid, dim3(kThreads), 0, s>>>(a);
-    else if (a.x) verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, true><<<grid, dim3(kThreads), 0, s>>>(a);
-    else verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, false><<<grid, dim3(kThreads), 0, s>>>(a);
+    if (a.parent) {
+        verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, true, false><<<grid, dim3(kThreads), 0, s>>>(a);
+    } else if (a.x) {
+        // the fused step: three value heads per workgroup when the heads come in groups of
+        // three and three copies of the head's LDS fit in a CU
+        using Sm = VerifySmem<DK, (KMAX + 15) / 16 * 16, RPG, IN_BF16, false>;
+        constexpr bool kFit3 = 3 * sizeof(Sm) <= 160 * 1024;
+        bool three = false;
+        if constexpr (kFit3) three = (a.Hv / a.Hk) % 3 == 0;
+        if (three) {
+            grid.y = a.Hv / 3;
+            if constexpr (kFit3)
+                verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, true, 3><<<grid, dim3(3 * kThreads), 0, s>>>(a);
+        } else {
+            verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, true, 1><<<grid, dim3(kThreads), 0, s>>>(a);
+        }
+    } else {
+        verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, false><<<grid, dim3(kThreads), 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
