@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void conv_step_kernel(ConvArgs a)
             float acc = 0.0f;
 #pragma unroll
             for (int jj = 0; jj < W; ++jj) acc = __builtin_fmaf(wt[e][jj], col[jj][e], acc);
-            out[e] = conv_silu(acc);
+            out[e] = BF16 ? bf16_to_f32(conv_silu_bf16(acc)) : conv_silu(acc);
         }
         store_row8<BF16>(a.y, xb + (size_t)t * C + c0, nch, vec, out);
         if (a.win) {
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void rollback_conv_kernel(RollConvArgs a,
             float acc2 = 0.0f;
 #pragma unroll
             for (int jj = 0; jj < W; ++jj) acc2 = __builtin_fmaf(wt[e][jj], col[jj][e], acc2);
-            out[e] = conv_silu(acc2);
+            out[e] = BF16 ? bf16_to_f32(conv_silu_bf16(acc2)) : conv_silu(acc2);
         }
         store_row8<BF16>(a.y, xb + (size_t)t * C + c0, nch, vec, out);
         store_row8<BF16>(a.win, (size_t)b * (W - 1 + T) * C + (size_t)(t + W - 1) * C + c0, nch, vec, col[W - 1]);
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kThreads) void conv_tree_kernel(ConvTreeArgs a)
         float acc = 0.0f;
 #pragma unroll
         for (int jj = 0; jj < W; ++jj) acc = __builtin_fmaf(wt[e][jj], col[jj][e], acc);
-        out[e] = conv_silu(acc);
+        out[e] = BF16 ? bf16_to_f32(conv_silu_bf16(acc)) : conv_silu(acc);
     }
     store_row8<BF16>(a.y, xb + (size_t)t * C + c0, nch, vec, out);
 }

@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn_device.h"
+
 namespace gdn {
 
 // e^x for the SiLU of the conv step.
@@ -55,6 +57,33 @@ __device__ __forceinline__ float conv_silu(float pre)
     const float e = conv_exp(-pre);
     const float den = 1.0f + e;
     return pre / den;
+}
+
+// bf16(conv_silu(pre)), bit for bit, for bfloat16 outputs.  A fast estimate s
+// from the hardware exp2 and reciprocal comes with a bound d on its distance to
+// conv_silu(pre); when s - d and s + d round to the same bfloat16, so does every
+// value between them (round to nearest even is monotone), conv_silu(pre) among
+// them, and that bfloat16 is the result; otherwise (or outside the range the
+// bound covers) the exact path decides.  The bound, relative to |s|, with
+// x = -pre log2(e):
+//   estimate:  x rounded (2^-23 |x| relative: the product and the constant),
+//              so e^.. off by |x| ln2 2^-23; exp2 and rcp within 2 ulp each;
+//              1 + e and pre * r rounded once each: < |x| 2^-23.5 + 2^-20.6
+//   exact path: its exp within 1.5 ulp of e^x, two roundings: < 2^-21.4
+// d = |s| (|x| 2^-22 + 2^-18) is more than twice their sum.  For |pre| <= 64
+// every intermediate is a normal float.
+__device__ __forceinline__ uint16_t conv_silu_bf16(float pre)
+{
+    const float ap = fabsf(pre);
+    const float x = pre * -1.44269504f;
+    const float e = __builtin_amdgcn_exp2f(x);
+    const float s = pre * __builtin_amdgcn_rcpf(1.0f + e);
+    const float d = fabsf(s) * __builtin_fmaf(fabsf(x), 0x1p-22f, 0x1p-18f);
+    const uint16_t lo = f32_to_bf16(s - d);
+    const bool fast = (ap <= 64.0f) & (ap >= 0x1p-60f) & (lo == f32_to_bf16(s + d));
+    uint16_t out = lo;
+    if (__builtin_expect(!fast, 0)) out = f32_to_bf16(conv_silu(pre));
+    return out;
 }
 
 // pre-activation of one channel over a window of W rows (oldest first)

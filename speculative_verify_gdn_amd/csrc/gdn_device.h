@@ -18,13 +18,14 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// float -> bfloat16 bits, round to nearest even; NaN stays NaN (quiet bit set)
+// float -> bfloat16 bits, round to nearest even; NaN stays NaN (quiet bit set).
+// Both results are formed and one is selected, so no lane branches.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t nan = (u >> 16) | 0x0040u;
+    return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? nan : rne);
 }
 
 // load 4 consecutive elements (bf16 or f32) as floats; p is 8 / 16 byte aligned

@@ -280,6 +280,9 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     __shared__ Smem smg[NG];
     const int gtid = threadIdx.x, sub = gtid / kThreads;
     Smem& sm = smg[sub];
+    // the raw q, k of the key head: one copy, the first group's
+    in_t(&qs)[KP][Smem::QW] = smg[0].q;
+    in_t(&ks)[KP][Smem::QW] = smg[0].k;
 
     const int tid = gtid % kThreads, lane = tid & 63, wave = tid >> 6;
     const int j = lane % LPR;                    // float4 index inside the row
@@ -332,8 +335,10 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
         }
         HS = reinterpret_cast<const in_t*>(a.hsrc) + ((size_t)b * a.hrows + ap) * C;
     }
-    // row r of this window [W-1 history rows ; K tokens]
+    // row r of this window [W-1 history rows ; K tokens]; only rows r < W-1 depend on the
+    // accept length, so rows known to be tokens take xrow_at and their loads need not wait for it
     auto wrow = [&](int r) -> const in_t* { return r < CW - 1 ? HS + (size_t)r * C : X + (size_t)(r - (CW - 1)) * C; };
+    auto xrow_at = [&](int r) -> const in_t* { return X + (size_t)(r - (CW - 1)) * C; };
 
     f32x4_t S;
     // ---- 1. stage q, k and their norms, the state rows, v; gates and their running sums.
@@ -361,12 +366,22 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
         float vrow[STEP ? NV : 1][CW];
         float4 vtp[STEP ? NV : 1];
         float wv[NWV];
+        float braw = 0.f, bal = 0.f;
+        int par = -1;
+        if (wave == kWaves - 1 && lane < K) {
+            const size_t gi = ((size_t)b * Kb + lane) * gs + h;
+            braw = load1<IN_BF16>(a.beta_raw, gi);
+            bal = load1<IN_BF16>(a.alpha, gi);
+            if constexpr (TREE) par = a.parent[(size_t)b * Kb + lane];
+        }
         if constexpr (STEP) {
+            // in issue order: first every load that does not depend on the accept length
+            // (taps, token rows), then the history rows it selects
             tp = *reinterpret_cast<const float4*>(a.w + choff * CW);
 #pragma unroll
-            for (int m = 0; m < NXR; ++m) {
-                const int r = t0 + m;
-                xrow[m] = load1<IN_BF16>(wrow(r < CW - 2 + K ? r : CW - 2 + K), choff);
+            for (int m = CW - 1; m < NXR; ++m) {
+                const int r = t0 + m < CW - 2 + K ? t0 + m : CW - 2 + K;
+                xrow[m] = load1<IN_BF16>(xrow_at(r), choff);
             }
 #pragma unroll
             for (int n = 0; n < NV; ++n) {
@@ -376,8 +391,22 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
                 const int tc = t < K ? t : K - 1;
                 vtp[n] = *reinterpret_cast<const float4*>(a.w + vch * CW);
+                vrow[n][CW - 1] = load1<IN_BF16>(xrow_at(tc + CW - 1), vch);
+            }
 #pragma unroll
-                for (int jj = 0; jj < CW; ++jj) vrow[n][jj] = load1<IN_BF16>(wrow(tc + jj), vch);
+            for (int m = 0; m < CW - 1; ++m) {
+                const int r = t0 + m < CW - 2 + K ? t0 + m : CW - 2 + K;
+                xrow[m] = load1<IN_BF16>(wrow(r), choff);
+            }
+#pragma unroll
+            for (int n = 0; n < NV; ++n) {
+                const int idx = tid + n * kThreads;
+                const int t = idx / RPG, rr = idx % RPG;
+                const int gr = blockIdx.x * RPG + rr;
+                const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
+                const int tc = t < K ? t : K - 1;
+#pragma unroll
+                for (int jj = 0; jj < CW - 1; ++jj) vrow[n][jj] = load1<IN_BF16>(wrow(tc + jj), vch);
             }
 #pragma unroll
             for (int n = 0; n < NWV; ++n) {
@@ -399,14 +428,6 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             }
         }
         f32x4_t S0 = load_f4(Sh + (size_t)ic * DK + c);
-        float braw = 0.f, bal = 0.f;
-        int par = -1;
-        if (wave == kWaves - 1 && lane < K) {
-            const size_t gi = ((size_t)b * Kb + lane) * gs + h;
-            braw = load1<IN_BF16>(a.beta_raw, gi);
-            bal = load1<IN_BF16>(a.alpha, gi);
-            if constexpr (TREE) par = a.parent[(size_t)b * Kb + lane];
-        }
         float vv[NV];
         if constexpr (!STEP) {
 #pragma unroll
@@ -432,16 +453,14 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 const int t = t0 + m;
                 if (t < KP) {
                     const float col[CW] = {xrow[m], xrow[m + 1], xrow[m + 2], xrow[m + 3]};
-                    float v = t < K ? conv_silu(conv_pre<CW>(tap, col)) : 0.f;
                     if constexpr (IN_BF16) {
-                        const uint16_t hb = f32_to_bf16(v);
-#pragma unroll
-                        for (int g2 = 0; g2 < NG; ++g2) (chi < DK ? smg[g2].q : smg[g2].k)[t][cl] = hb;
+                        const uint16_t hb = t < K ? conv_silu_bf16(conv_pre<CW>(tap, col)) : (uint16_t)0;
+                        (chi < DK ? qs : ks)[t][cl] = hb;
                         if (a.y && qk_writer && t < K)
                             reinterpret_cast<uint16_t*>(a.y)[((size_t)b * Kb + t) * C + choff] = hb;
                     } else {
-#pragma unroll
-                        for (int g2 = 0; g2 < NG; ++g2) (chi < DK ? smg[g2].q : smg[g2].k)[t][cl] = v;
+                        const float v = t < K ? conv_silu(conv_pre<CW>(tap, col)) : 0.f;
+                        (chi < DK ? qs : ks)[t][cl] = v;
                         if (a.y && qk_writer && t < K) reinterpret_cast<float*>(a.y)[((size_t)b * Kb + t) * C + choff] = v;
                     }
                 }
@@ -470,8 +489,9 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 const int t = idx / RPG, rr = idx % RPG;
                 const int gr = blockIdx.x * RPG + rr;
                 const float tv[CW] = {vtp[n].x, vtp[n].y, vtp[n].z, vtp[n].w};
-                float v = conv_silu(conv_pre<CW>(tv, vrow[n]));
-                if constexpr (IN_BF16) v = bf16_to_f32(f32_to_bf16(v));
+                float v;
+                if constexpr (IN_BF16) v = bf16_to_f32(conv_silu_bf16(conv_pre<CW>(tv, vrow[n])));
+                else v = conv_silu(conv_pre<CW>(tv, vrow[n]));
                 vv[n] = idx < KMAX * RPG ? v : 0.f;
                 if (a.y && idx < KMAX * RPG && t < K && gr < dv)
                     store1<IN_BF16>(a.y, ((size_t)b * Kb + t) * C + 2 * (size_t)Hk * DK + (size_t)h * dv + gr, v);
@@ -483,8 +503,8 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 const int idx = tid + n * kThreads;
                 if (idx < KP * VPR) {
                     const int t = idx / VPR, cc = (idx % VPR) * EPV;
-                    const float sq = group_sum<VPR>(sumsq16<IN_BF16>(*reinterpret_cast<const uint4*>(&sm.q[t][cc])));
-                    const float sk = group_sum<VPR>(sumsq16<IN_BF16>(*reinterpret_cast<const uint4*>(&sm.k[t][cc])));
+                    const float sq = group_sum<VPR>(sumsq16<IN_BF16>(*reinterpret_cast<const uint4*>(&qs[t][cc])));
+                    const float sk = group_sum<VPR>(sumsq16<IN_BF16>(*reinterpret_cast<const uint4*>(&ks[t][cc])));
                     if (cc == 0) {
                         sm.tok[t].z = t < K ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.0f;
                         sm.tok[t].w = t < K ? __builtin_amdgcn_rsqf(sq + a.eps) : 0.0f;
@@ -498,8 +518,8 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 if (idx < KP * VPR) {
                     const int t = idx / VPR, cc = (idx % VPR) * EPV;
                     if (t >= K) qv[n] = kv[n] = make_uint4(0, 0, 0, 0);
-                    *reinterpret_cast<uint4*>(&sm.q[t][cc]) = qv[n];
-                    *reinterpret_cast<uint4*>(&sm.k[t][cc]) = kv[n];
+                    *reinterpret_cast<uint4*>(&qs[t][cc]) = qv[n];
+                    *reinterpret_cast<uint4*>(&ks[t][cc]) = kv[n];
                     // 1/|q_t|, 1/|k_t| (padded tokens keep q^ = k^ = 0, never 0 * 1/sqrt(0))
                     const float sq = group_sum<VPR>(sumsq16<IN_BF16>(qv[n]));
                     const float sk = group_sum<VPR>(sumsq16<IN_BF16>(kv[n]));
@@ -581,8 +601,8 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                     }
                     continue;
                 }
-                const f32x4_t d = wa ? gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.k, sm.k, tm, tn, lane)
-                                     : gram_tile<DK, Smem::QW, IN_BF16, in_t>(sm.q, sm.k, tm, tn, lane);
+                const f32x4_t d = wa ? gram_tile<DK, Smem::QW, IN_BF16, in_t>(ks, ks, tm, tn, lane)
+                                     : gram_tile<DK, Smem::QW, IN_BF16, in_t>(qs, ks, tm, tn, lane);
                 const float Gs = sm.Gv[s2], rks = sm.tok[s2].z;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -601,7 +621,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             }
     } else {
         // raw K S^T (wave 1) or Q S^T (wave 2), stored per state row
-        const in_t(*Xs)[Smem::QW] = wave == 1 ? sm.k : sm.q;
+        const in_t(*Xs)[Smem::QW] = wave == 1 ? ks : qs;
         float(*D)[KP + 4] = wave == 1 ? sm.P : sm.R;
 #pragma unroll
         for (int tm = 0; tm < TB; ++tm)
@@ -635,7 +655,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             const int s = __builtin_ctz(m);
             m &= m - 1;
             const float cf = sm.Cm[t][s] * sm.U[rloc][s];
-            const float4 kx = lds4<IN_BF16>(&sm.k[s][c]);
+            const float4 kx = lds4<IN_BF16>(&ks[s][c]);
             Ht[0] = __builtin_fmaf(cf, kx.x, Ht[0]);
             Ht[1] = __builtin_fmaf(cf, kx.y, Ht[1]);
             Ht[2] = __builtin_fmaf(cf, kx.z, Ht[2]);
@@ -646,7 +666,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     auto stream_token = [&](int t, float ut) {
         const float gm = sm.gam[t];
         const float cu = ut * sm.tok[t].z;
-        const float4 kx = lds4<IN_BF16>(&sm.k[t][c]);
+        const float4 kx = lds4<IN_BF16>(&ks[t][c]);
         S[0] = __builtin_fmaf(cu, kx.x, gm * S[0]);
         S[1] = __builtin_fmaf(cu, kx.y, gm * S[1]);
         S[2] = __builtin_fmaf(cu, kx.z, gm * S[2]);
