@@ -230,6 +230,48 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
                                  "GBs": round(b / (us * 1e-6) / 1e9, 1),
                                  "tokens_per_s": round(int(lens.sum()) / (us * 1e-6), 1)}
         del sets
+    for name in [n for n in ("decode", "batched") if n in only]:
+        # the whole step in one launch (gdn_verify_step) against the separate launches, sets chained as in
+        # a serving loop (set r continues from set r-1's window)
+        wl = synth.WORKLOADS[name]
+        per = wl.B * wl.Hv * wl.dv * wl.dk * 4 * (wl.T + 2)
+        R = max(2, math.ceil(2 * MALL_BYTES / per))
+        sets = []
+        for r in range(R):
+            inp = synth.make_inputs(wl, seed=r)
+            d = {k: v.to(dev) for k, v in inp.items()}
+            d["S_ckpt"] = torch.empty_like(d["S_in"])
+            d["S_out"] = torch.empty_like(d["S_in"])
+            d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev) if wl.T > 1 else None
+            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+            d["y"] = torch.empty_like(d["x"])
+            d["win"] = torch.empty(wl.B, wl.W - 1 + wl.T, wl.C, device=dev, dtype=d["x"].dtype)
+            d["win_prev"] = torch.empty_like(d["win"])
+            sets.append(d)
+        for d in sets:
+            gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_out"], d["H"],
+                            d["o"], wl.Hk, S_in=d["S_in"], hist=d["hist"], S_ckpt=d["S_ckpt"], win=d["win"])
+            gdn.conv_step(d["x"], d["w"], d["hist"].clone(), d["y"], d["win_prev"])
+        idx = {id(d): r for r, d in enumerate(sets)}
+
+        def fused(d, wl=wl):
+            pv = sets[idx[id(d)] - 1]
+            gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_out"], d["H"],
+                            d["o"], wl.Hk, prev=(pv["accept"], pv["S_ckpt"], pv["H"], pv["S_out"], pv["win"]),
+                            S_ckpt=d["S_ckpt"], win=d["win"])
+
+        def two(d, wl=wl):
+            gdn.rollback_conv_step(d["accept"], wl.T, d["S_in"], d["H"], d["S_out"], d["win_prev"], d["x"], d["w"],
+                                   d["hist"], d["y"], d["win"])
+            gdn.verify(d["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"], d["H"],
+                       d["o"], wl.Hk)
+        reps = max(1, 200 // R)
+        t_f, t_2 = timed(fused, sets, reps), timed(two, sets, reps)
+        res[name + "_step"] = {"verify_step_us": round(t_f, 3), "two_launch_step_us": round(t_2, 3),
+                               "tokens_per_s": round(wl.B * wl.T / (t_f * 1e-6), 1),
+                               "step_bytes_per_launch": step_bytes(wl),
+                               "GBs": round(step_bytes(wl) / (t_f * 1e-6) / 1e9, 1)}
+        del sets
     if "batched" in only:
         # rollback by capture (verify writes every H_t, rollback copies H_{a-1}) against checkpoint + replay
         # (verify writes the final state only, replay re-runs the accepted prefix from S_in), state only,
@@ -267,8 +309,9 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
         del sets
     if "tree" in only:
         # tree verify on the verify16 shape: N = 16 and 32 nodes of a random draft tree (parent among the 4
-        # previous nodes), the conv of every node, the verify, and the rollback to a drawn node
-        for N in (16, 32):
+        # previous nodes) and of a breadth-first binary tree; the conv of every node, the verify, and the
+        # rollback to a drawn node
+        for N, shape in ((16, "random"), (32, "random"), (16, "binary"), (32, "binary")):
             wl = synth.small("verify16", T=N)
             per = wl.B * wl.Hv * wl.dv * wl.dk * 4 * (N + 1)
             R = max(2, math.ceil(2 * MALL_BYTES / per))
@@ -276,7 +319,7 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
             for r in range(R):
                 inp = synth.make_inputs(wl, seed=r)
                 d = {k: v.to(dev) for k, v in inp.items()}
-                d["parent"] = synth.make_tree(wl.B, N, seed=r, shape="random").to(dev)
+                d["parent"] = synth.make_tree(wl.B, N, seed=r, shape=shape).to(dev)
                 d["node"] = synth.make_tree_accept(wl.B, N, seed=r).to(dev)
                 d["y"] = torch.empty_like(d["x"])
                 d["S_out"] = torch.empty_like(d["S_in"])
@@ -304,12 +347,14 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
             t_v = timed(tver, sets, reps)
             t_s = timed(tstep, sets, reps)
             b = verify_tree_bytes(wl)
-            res["tree%d" % N] = {"verify_tree_us": round(t_v, 3), "bytes_per_launch": b,
+            res["tree%d%s" % (N, "" if shape == "random" else "_" + shape)] = {
+                                 "verify_tree_us": round(t_v, 3), "bytes_per_launch": b,
                                  "GBs": round(b / (t_v * 1e-6) / 1e9, 1),
                                  "conv_tree_us": round(timed(tconv, sets, reps), 3),
                                  "rollback_tree_us": round(timed(troll, sets, reps), 3),
                                  "step_us": round(t_s, 3), "nodes_per_s": round(N / (t_s * 1e-6), 1),
-                                 "tree": "random, parent among the 4 previous nodes"}
+                                 "tree": {"random": "random, parent among the 4 previous nodes",
+                                          "binary": "complete binary, breadth-first numbering"}[shape]}
             del sets
     if "prefill" not in only:
         return res

@@ -77,6 +77,7 @@ struct VerifySmem {
     // tree only (one element otherwise)
     static constexpr int TK = TREE ? KP : 1, TR = TREE ? RPG : 1;
     uint32_t anc[TK];               // strict ancestors of node t, one bit per node
+    int par[TK];                    // parent of node t (-1: a root)
     float Cm[TK][KP + 4];           // e^{G_t-G_s}/|k_s| for s an ancestor of t or t itself, else 0
     float U[TR][KP + 4];            // u_s of each row, for the direct state sums
 };
@@ -553,6 +554,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 // (t included) and nxt is the next node above them (-1 past the root)
                 int nxt = (lane < K && par >= 0 && par < lane) ? par : -1;
                 uint32_t anc = nxt >= 0 ? 1u << nxt : 0u;
+                if (lane < KP) sm.par[lane] = nxt;
                 G = g;
 #pragma unroll
                 for (int r = 1; r < KP; r *= 2) {
@@ -644,23 +646,48 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     // H holds K-1 states per sequence for a chain (the last one goes to S_out), K for a tree
     float* Hrow = a.H ? a.H + ((size_t)b * (TREE ? Kb : Kb - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
     const size_t Hstep = (size_t)Hv * SD;
-    // a tree node's state, directly from S_in (kept in S) and the u_s of its path:
+    // a tree node's state.  When its parent is one of the four nodes before it (or a root),
+    // from the parent's state kept in registers: H_t = gamma_t H_parent + u_t k^_t (slot
+    // t mod 4 of hc holds H_t; t is a constant of the unrolled token loop, so the slots are
+    // registers); otherwise directly from S_in (kept in S) and the u_s of its path:
     //   H_t = e^{G_t} S_in + sum_{s on the path, s <= t} e^{G_t-G_s} u_s k^_s
-    // the ancestor mask is the same for the whole workgroup, so the loop is scalar
-    auto stream_node = [&](int t) {
-        uint32_t m = __builtin_amdgcn_readfirstlane(sm.anc[t]) | (1u << t);
-        const float eG = sm.tok[t].y;
-        f32x4_t Ht = {eG * S[0], eG * S[1], eG * S[2], eG * S[3]};
-        while (m) {
-            const int s = __builtin_ctz(m);
-            m &= m - 1;
-            const float cf = sm.Cm[t][s] * sm.U[rloc][s];
-            const float4 kx = lds4<IN_BF16>(&ks[s][c]);
-            Ht[0] = __builtin_fmaf(cf, kx.x, Ht[0]);
-            Ht[1] = __builtin_fmaf(cf, kx.y, Ht[1]);
-            Ht[2] = __builtin_fmaf(cf, kx.z, Ht[2]);
-            Ht[3] = __builtin_fmaf(cf, kx.w, Ht[3]);
+    // The parent and the ancestor mask are the same over the workgroup, so every branch
+    // here is uniform.
+    f32x4_t hc[4];
+    auto stream_node = [&](int t, float ut) {
+        const int p = __builtin_amdgcn_readfirstlane(sm.par[t]);
+        f32x4_t Ht;
+        const int back = t - 1 - p;               // 0..3: the parent is in slot (t-1-back) mod 4
+        if (p < 0 || back < 4) {
+            f32x4_t base = S;
+            if (p >= 0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (back == q && t - 1 - q >= 0) base = hc[(t - 1 - q) & 3];
+            }
+            const float gm = sm.gam[t];
+            const float cu = ut * sm.tok[t].z;
+            const float4 kx = lds4<IN_BF16>(&ks[t][c]);
+            Ht[0] = __builtin_fmaf(cu, kx.x, gm * base[0]);
+            Ht[1] = __builtin_fmaf(cu, kx.y, gm * base[1]);
+            Ht[2] = __builtin_fmaf(cu, kx.z, gm * base[2]);
+            Ht[3] = __builtin_fmaf(cu, kx.w, gm * base[3]);
+        } else {
+            uint32_t m = __builtin_amdgcn_readfirstlane(sm.anc[t]) | (1u << t);
+            const float eG = sm.tok[t].y;
+            Ht = f32x4_t{eG * S[0], eG * S[1], eG * S[2], eG * S[3]};
+            while (m) {
+                const int s = __builtin_ctz(m);
+                m &= m - 1;
+                const float cf = sm.Cm[t][s] * sm.U[rloc][s];
+                const float4 kx = lds4<IN_BF16>(&ks[s][c]);
+                Ht[0] = __builtin_fmaf(cf, kx.x, Ht[0]);
+                Ht[1] = __builtin_fmaf(cf, kx.y, Ht[1]);
+                Ht[2] = __builtin_fmaf(cf, kx.z, Ht[2]);
+                Ht[3] = __builtin_fmaf(cf, kx.w, Ht[3]);
+            }
         }
+        hc[t & 3] = Ht;
         if (live && t < K) store_f4<NT>(Hrow + (size_t)t * Hstep, Ht);
     };
     auto stream_token = [&](int t, float ut) {
@@ -718,7 +745,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 // one lane per row publishes u_t; the row's lanes read it back in
                 // program order (same wave), so no barrier is needed
                 if (j == 0) sm.U[rloc][t] = mine;
-                stream_node(t);
+                stream_node(t, mine);
             } else {
                 stream_token(t, mine);
             }
@@ -752,7 +779,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 for (int t = 0; t < KMAX; ++t) sm.U[rloc][t] = u[t];
             }
 #pragma unroll
-            for (int t = 0; t < KMAX; ++t) stream_node(t);
+            for (int t = 0; t < KMAX; ++t) stream_node(t, u[t]);
         } else {
 #pragma unroll
             for (int t = 0; t < KMAX; ++t) stream_token(t, u[t]);

@@ -113,7 +113,9 @@ def make_tree(B: int, N: int, seed: int = 0, shape: str = "random", fan: int = 4
     star:   every node a root (N one-token continuations of the committed state);
     random: node 0 a root, node i >= 1 picks its parent uniformly among the
             `fan` nodes before it (depth about N / (fan/2 + 1));
-    forest: like random, with the committed state (-1) as one more choice.
+    forest: like random, with the committed state (-1) as one more choice;
+    binary: a complete binary tree numbered breadth first (parent (i-1)/2), the
+            numbering of a level-by-level top-2 expansion: parents lie far back.
     """
     g = torch.Generator().manual_seed(seed + 104729)
     par = torch.empty(B, N, dtype=torch.int32)
@@ -123,6 +125,8 @@ def make_tree(B: int, N: int, seed: int = 0, shape: str = "random", fan: int = 4
                 p = i - 1
             elif shape == "star":
                 p = -1
+            elif shape == "binary":
+                p = (i - 1) // 2 if i > 0 else -1
             elif shape in ("random", "forest"):
                 lo = max(0, i - fan)
                 choices = list(range(lo, i)) + ([-1] if (shape == "forest" or i == 0) else [])
