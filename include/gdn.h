@@ -287,8 +287,10 @@ int gdn_prefill_chunked(const void *qkv, const void *beta_raw, const void *alpha
  * gdn_verify_step -- one whole verify step of the layer in one launch: the
  * rollback of the previous window, the conv step of this window and the GDN
  * verify with capture (gdn_rollback + gdn_conv_step + gdn_verify, the same
- * arithmetic and the same bits, with no state copy and no intermediate
- * launch; the pages' step in atlas PR #297 and lucebox PR #637 as above).
+ * arithmetic and the same bits -- at K = 1, where gdn_verify takes a decode
+ * kernel, the same recurrence in another rounding order -- with no state copy
+ * and no intermediate launch; the pages' step in atlas PR #297 and lucebox
+ * PR #637 as above).
  *
  * Previous window (accept_prev != NULL): sequence b starts from the state its
  * accept length a = accept_prev[b] (clamped into 0..K_prev) selects --

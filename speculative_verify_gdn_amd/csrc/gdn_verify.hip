@@ -787,6 +787,54 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     }
 }
 
+// One token (K = 1: a decode step) needs no WY solve, no LDS and no barrier.  A lane
+// owns one float4 of one state row (a row is DK/4 lanes of one wave); the q/k norms
+// and the contractions are sums over the row's lanes (DPP):
+//   u = beta (v - gamma S k^),   S' = gamma S + u k^^T,   o = S' q^
+// The same recurrence as the window kernel's first token, in another rounding order.
+template <int DK, bool IN_BF16, bool O_BF16>
+__global__ __launch_bounds__(kThreads) void decode_kernel(VerifyArgs a)
+{
+    constexpr int LPR = DK / 4, RPW = 64 / LPR, RPG = kWaves * RPW;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = 4 * (lane % LPR);
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int i = blockIdx.x * RPG + wave * RPW + lane / LPR;
+    const int Hk = a.Hk, Hv = a.Hv, dv = a.dv;
+    const bool live = i < dv;
+    const int ic = live ? i : dv - 1;
+    const size_t C = 2 * (size_t)Hk * DK + (size_t)Hv * dv;
+    const int hk = h / (Hv / Hk);
+    const size_t SD = (size_t)dv * DK;
+    const size_t xb = (size_t)b * C;                 // the token's row (K = 1)
+    const size_t gi = (size_t)b * (a.gstride > 0 ? a.gstride : Hv) + h;
+    const size_t so = ((size_t)b * Hv + h) * SD + (size_t)ic * DK + c;
+    const float4 qx = load4<IN_BF16>(a.qkv, xb + (size_t)hk * DK + c);
+    const float4 kx = load4<IN_BF16>(a.qkv, xb + (size_t)(Hk + hk) * DK + c);
+    const float v = load1<IN_BF16>(a.qkv, xb + 2 * (size_t)Hk * DK + (size_t)h * dv + ic);
+    const f32x4_t S = load_f4(a.S_in + so);
+    const float braw = load1<IN_BF16>(a.beta_raw, gi), bal = load1<IN_BF16>(a.alpha, gi);
+    float beta, g;
+    gate(braw, bal, a.dt_bias, a.A_log, h, beta, g);
+    const float gm = __expf(g);
+    const float rk = __builtin_amdgcn_rsqf(
+        group_sum<LPR>(kx.x * kx.x + kx.y * kx.y + kx.z * kx.z + kx.w * kx.w) + a.eps);
+    const float rq = __builtin_amdgcn_rsqf(
+        group_sum<LPR>(qx.x * qx.x + qx.y * qx.y + qx.z * qx.z + qx.w * qx.w) + a.eps);
+    const float sk = group_sum<LPR>(S[0] * kx.x + S[1] * kx.y + S[2] * kx.z + S[3] * kx.w) * rk;
+    const float cu = beta * (v - gm * sk) * rk;      // u / |k|
+    f32x4_t Sn;
+    Sn[0] = __builtin_fmaf(cu, kx.x, gm * S[0]);
+    Sn[1] = __builtin_fmaf(cu, kx.y, gm * S[1]);
+    Sn[2] = __builtin_fmaf(cu, kx.z, gm * S[2]);
+    Sn[3] = __builtin_fmaf(cu, kx.w, gm * S[3]);
+    const float o = group_sum<LPR>(Sn[0] * qx.x + Sn[1] * qx.y + Sn[2] * qx.z + Sn[3] * qx.w) * rq;
+    if (live) {
+        store_f4<false>(a.S_out + so, Sn);
+        if (a.o && c == 0) store1<O_BF16>(a.o, ((size_t)b * Hv + h) * dv + i, o);
+    }
+}
+
 template <int DK, int KMAX, bool IN_BF16, bool O_BF16>
 hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
 {
@@ -808,6 +856,8 @@ hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
         } else {
             verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, true, 1><<<grid, dim3(kThreads), 0, s>>>(a);
         }
+    } else if (KMAX == 1 && a.K == 1 && !a.replay) {
+        decode_kernel<DK, IN_BF16, O_BF16><<<grid, dim3(kThreads), 0, s>>>(a);
     } else {
         verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, false, false><<<grid, dim3(kThreads), 0, s>>>(a);
     }

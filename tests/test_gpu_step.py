@@ -4,7 +4,8 @@ verify with capture.
 
 It must give the bits of the separate calls (gdn_rollback, gdn_conv_step,
 gdn_verify on the same inputs) -- y, the window, the checkpoint, S_out, every
-H_t and o -- and, through them, the oracle: the conv bit for bit against the
+H_t and o (at K = 1, where gdn_verify takes its decode kernel, the states and o
+within 1e-5) -- and, through them, the oracle: the conv bit for bit against the
 oracle's same-precision conv, the GDN within 2e-3 * ||S_ref||_F per head.
 Steps are chained as in a serving loop (two buffer sets alternating), with
 accept lengths covering 0, partial and the whole window.  Every test prints
@@ -70,9 +71,16 @@ def separate(wl, d, out, S_start, hist):
     out["S_ckpt"].copy_(S_start)
 
 
-def assert_same(a, b, what):
+def assert_same(a, b, what, K):
     for k in ("S_ckpt", "S_out", "H", "o", "y", "win"):
         if a[k] is None:
+            continue
+        if K == 1 and k in ("S_ckpt", "S_out", "o"):
+            # at K = 1 the separate gdn_verify takes its decode kernel (another rounding order),
+            # and a second window starts from the first one's state
+            ref = b[k].double()
+            assert (a[k].double() - ref).abs().max() <= 1e-5 * max(1.0, float(ref.abs().max())), \
+                "%s: %s differs" % (what, k)
             continue
         assert torch.equal(a[k], b[k]), "%s: %s differs" % (what, k)
 
@@ -104,7 +112,7 @@ def test_fused_step_equals_separate_calls(name, over, acc):
     fused(wl, d1, A)
     separate(wl, d1, A_ref, d1["S_in"], d1["hist"])
     torch.cuda.synchronize()
-    assert_same(A, A_ref, "first window")
+    assert_same(A, A_ref, "first window", wl.T)
 
     # second window: from the first one's buffers, by accept length
     Bo, B_ref = outputs(wl), outputs(wl)
@@ -115,7 +123,7 @@ def test_fused_step_equals_separate_calls(name, over, acc):
     gdn.rollback(accept, wl.T, A_ref["S_ckpt"], A_ref["H"], S_start, hist, A_ref["win"])
     separate(wl, d2, B_ref, S_start, hist)
     torch.cuda.synchronize()
-    assert_same(Bo, B_ref, "second window")
+    assert_same(Bo, B_ref, "second window", wl.T)
 
 
 def test_fused_step_chain_against_oracle():
