@@ -375,6 +375,46 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             bal = load1<IN_BF16>(a.alpha, gi);
             if constexpr (TREE) par = a.parent[(size_t)b * Kb + lane];
         }
+        // the gates of every token and their running sums (the last wave): they need only
+        // the gate loads, so the fused step forms them before its conv, in the wait for the rows
+        auto do_gates = [&]() {
+            if (wave == kWaves - 1) {
+                // lane t: gates of token t, then G_t = g_0 + ... + g_t by a scan over the lanes
+                float be = 0.f, g = 0.f;
+                if (lane < K) gate(braw, bal, a.dt_bias, a.A_log, h, be, g);
+                float G;
+                if constexpr (TREE) {
+                    // G_t = sum of g over the root path of node t, and its strict ancestors, by
+                    // pointer jumping: after round r, G covers the 2^r nearest nodes of the path
+                    // (t included) and nxt is the next node above them (-1 past the root)
+                    int nxt = (lane < K && par >= 0 && par < lane) ? par : -1;
+                    uint32_t anc = nxt >= 0 ? 1u << nxt : 0u;
+                    if (lane < KP) sm.par[lane] = nxt;
+                    G = g;
+    #pragma unroll
+                    for (int r = 1; r < KP; r *= 2) {
+                        const int src = nxt >= 0 ? nxt : lane;
+                        const float Gn = __shfl(G, src, 64);
+                        const uint32_t an = (uint32_t)__shfl((int)anc, src, 64);
+                        const int nn = __shfl(nxt, src, 64);
+                        if (nxt >= 0) {
+                            G += Gn;
+                            anc |= an;
+                            nxt = nn;
+                        }
+                    }
+                    if (lane < KP) sm.anc[lane] = anc;
+                } else {
+                    G = lane_scan<KP>(g);
+                }
+                if (lane < KP) {
+                    sm.Gv[lane] = G;
+                    sm.tok[lane].x = be;
+                    sm.tok[lane].y = __expf(G);
+                    sm.gam[lane] = __expf(g);
+                }
+            }
+        };
         if constexpr (STEP) {
             // in issue order: first every load that does not depend on the accept length
             // (taps, token rows), then the history rows it selects
@@ -441,6 +481,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             }
         }
         if constexpr (STEP) {
+            do_gates();
             // the checkpoint: this window's start state
             if (a.S_ckpt && live) store_f4<true>(a.S_ckpt + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S0);
             // the conv, as the conv kernels compute it; the conv outputs and the window
@@ -543,42 +584,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             const int idx = tid + n * kThreads;
             if (idx < KMAX * RPG) sm.V[idx / RPG][idx % RPG] = vv[n];
         }
-        if (wave == kWaves - 1) {
-            // lane t: gates of token t, then G_t = g_0 + ... + g_t by a scan over the lanes
-            float be = 0.f, g = 0.f;
-            if (lane < K) gate(braw, bal, a.dt_bias, a.A_log, h, be, g);
-            float G;
-            if constexpr (TREE) {
-                // G_t = sum of g over the root path of node t, and its strict ancestors, by
-                // pointer jumping: after round r, G covers the 2^r nearest nodes of the path
-                // (t included) and nxt is the next node above them (-1 past the root)
-                int nxt = (lane < K && par >= 0 && par < lane) ? par : -1;
-                uint32_t anc = nxt >= 0 ? 1u << nxt : 0u;
-                if (lane < KP) sm.par[lane] = nxt;
-                G = g;
-#pragma unroll
-                for (int r = 1; r < KP; r *= 2) {
-                    const int src = nxt >= 0 ? nxt : lane;
-                    const float Gn = __shfl(G, src, 64);
-                    const uint32_t an = (uint32_t)__shfl((int)anc, src, 64);
-                    const int nn = __shfl(nxt, src, 64);
-                    if (nxt >= 0) {
-                        G += Gn;
-                        anc |= an;
-                        nxt = nn;
-                    }
-                }
-                if (lane < KP) sm.anc[lane] = anc;
-            } else {
-                G = lane_scan<KP>(g);
-            }
-            if (lane < KP) {
-                sm.Gv[lane] = G;
-                sm.tok[lane].x = be;
-                sm.tok[lane].y = __expf(G);
-                sm.gam[lane] = __expf(g);
-            }
-        }
+        if constexpr (!STEP) do_gates();
     }
     __syncthreads();
 
