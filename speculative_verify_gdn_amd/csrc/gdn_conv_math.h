@@ -61,27 +61,34 @@ __device__ __forceinline__ float conv_silu(float pre)
 
 // bf16(conv_silu(pre)), bit for bit, for bfloat16 outputs.  A fast estimate s
 // from the hardware exp2 and reciprocal comes with a bound d on its distance to
-// conv_silu(pre); when s - d and s + d round to the same bfloat16, so does every
-// value between them (round to nearest even is monotone), conv_silu(pre) among
-// them, and that bfloat16 is the result; otherwise (or outside the range the
-// bound covers) the exact path decides.  The bound, relative to |s|, with
-// x = -pre log2(e):
+// conv_silu(pre), so the exact value lies in [s - d, s + d].  Round to nearest
+// even is odd-symmetric, so the magnitude is rounded and the sign put back.  On
+// positive floats it is monotone in the bit pattern u: every value whose u has
+// no tie point (low 16 bits 0x8000) between those of |s| - d and |s| + d rounds
+// to (u + 0x8000) >> 16, the same for all of them.  (u + 0x7fff) >> 16 of the
+// lower end equals that of the upper end exactly when there is no such tie (a
+// tie at the lower end itself gives one less), so the fast result is taken
+// only then; otherwise (or outside the range the bound covers, NaN and
+// infinities included) the exact path decides.  The bound, relative to |s|,
+// with x = -pre log2(e):
 //   estimate:  x rounded (2^-23 |x| relative: the product and the constant),
 //              so e^.. off by |x| ln2 2^-23; exp2 and rcp within 2 ulp each;
 //              1 + e and pre * r rounded once each: < |x| 2^-23.5 + 2^-20.6
 //   exact path: its exp within 1.5 ulp of e^x, two roundings: < 2^-21.4
-// d = |s| (|x| 2^-22 + 2^-18) is more than twice their sum.  For |pre| <= 64
-// every intermediate is a normal float.
+// d = |s| (|x| 2^-22 + 2^-18) is more than twice their sum, and below |s|.
+// For |pre| <= 64 every intermediate is a normal float.
 __device__ __forceinline__ uint16_t conv_silu_bf16(float pre)
 {
     const float ap = fabsf(pre);
     const float x = pre * -1.44269504f;
     const float e = __builtin_amdgcn_exp2f(x);
     const float s = pre * __builtin_amdgcn_rcpf(1.0f + e);
-    const float d = fabsf(s) * __builtin_fmaf(fabsf(x), 0x1p-22f, 0x1p-18f);
-    const uint16_t lo = f32_to_bf16(s - d);
-    const bool fast = (ap <= 64.0f) & (ap >= 0x1p-60f) & (lo == f32_to_bf16(s + d));
-    uint16_t out = lo;
+    const float as = fabsf(s);
+    const float d = as * __builtin_fmaf(fabsf(x), 0x1p-22f, 0x1p-18f);
+    const uint32_t lo = (__float_as_uint(as - d) + 0x7fffu) >> 16;
+    const uint32_t hi = (__float_as_uint(as + d) + 0x8000u) >> 16;
+    const bool fast = (ap <= 64.0f) & (ap >= 0x1p-60f) & (lo == hi);
+    uint16_t out = (uint16_t)(hi | ((__float_as_uint(s) >> 16) & 0x8000u));
     if (__builtin_expect(!fast, 0)) out = f32_to_bf16(conv_silu(pre));
     return out;
 }

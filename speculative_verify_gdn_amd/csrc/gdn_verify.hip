@@ -131,19 +131,26 @@ __device__ __forceinline__ float sumsq16(const uint4 u)
     return s;
 }
 
-// gates of one token for value head h
-__device__ __forceinline__ void gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
-                                     float& beta, float& g)
+// gates of one token: raw (dtb, alog = the head's dt_bias and A_log) or, with
+// raw false, beta and g given directly
+__device__ __forceinline__ void gate(float braw, float al, bool raw, float dtb, float alog, float& beta, float& g)
 {
-    if (dt_bias != nullptr) {
+    if (raw) {
         beta = __frcp_rn(1.0f + __expf(-braw));
-        const float a = al + dt_bias[h];
+        const float a = al + dtb;
         const float sp = a > 20.0f ? a : __logf(1.0f + __expf(a));
-        g = -sp * __expf(A_log[h]);
+        g = -sp * __expf(alog);
     } else {
         beta = braw;
         g = al;
     }
+}
+
+__device__ __forceinline__ void gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
+                                     float& beta, float& g)
+{
+    if (dt_bias != nullptr) gate(braw, al, true, dt_bias[h], A_log[h], beta, g);
+    else gate(braw, al, false, 0.f, 0.f, beta, g);
 }
 
 // bf16 halves of 8 floats: hi = top 16 bits, lo = top 16 bits of the remainder
@@ -212,6 +219,25 @@ __device__ __forceinline__ f32x4_t state_tile(const in_t (*X)[QW], const float (
         }
     }
     return acc;
+}
+
+// the raw bits of one element (bf16 zero-extended, or f32): loaded without a
+// conversion, so that a load inside a branch is not waited for at its end
+template <bool BF16>
+__device__ __forceinline__ uint32_t ldraw(const void* base, size_t idx)
+{
+    if constexpr (BF16) return reinterpret_cast<const uint16_t*>(base)[idx];
+    else return reinterpret_cast<const uint32_t*>(base)[idx];
+}
+
+template <bool BF16>
+__device__ __forceinline__ float rawf(uint32_t u) { return __uint_as_float(BF16 ? u << 16 : u); }
+
+template <bool BF16>
+__device__ __forceinline__ void straw(void* base, size_t idx, uint32_t u)
+{
+    if constexpr (BF16) reinterpret_cast<uint16_t*>(base)[idx] = (uint16_t)u;
+    else reinterpret_cast<uint32_t*>(base)[idx] = u;
 }
 
 template <bool IN_BF16>
@@ -325,17 +351,21 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     // fused step: the start state and the W-1 history rows come from the previous
     // window, picked by its accept length a -- S_ckpt (a = 0), H[a-1], or its final
     // state (a = K_prev), and window rows a .. a+W-2 -- or from S_in and hist
+    // The accept length is loaded only once every load that does not depend on it has
+    // been issued (pick_start), so its round trip overlaps theirs.
     const in_t* HS = nullptr;
-    if constexpr (STEP) {
-        int ap = 0;
-        if (a.acc_prev) {
-            ap = min(max(a.acc_prev[b], 0), a.Kp);
-            const size_t hb = ((size_t)b * Hv + h) * SD;
-            Sh = ap == 0 ? a.Sp_ckpt + hb
-                         : (ap == a.Kp ? a.Sp_out + hb : a.Sp_H + (((size_t)b * (a.Kp - 1) + ap - 1) * Hv + h) * SD);
+    auto pick_start = [&]() {
+        if constexpr (STEP) {
+            int ap = 0;
+            if (a.acc_prev) {
+                ap = min(max(a.acc_prev[b], 0), a.Kp);
+                const size_t hb = ((size_t)b * Hv + h) * SD;
+                Sh = ap == 0 ? a.Sp_ckpt + hb
+                             : (ap == a.Kp ? a.Sp_out + hb : a.Sp_H + (((size_t)b * (a.Kp - 1) + ap - 1) * Hv + h) * SD);
+            }
+            HS = reinterpret_cast<const in_t*>(a.hsrc) + ((size_t)b * a.hrows + ap) * C;
         }
-        HS = reinterpret_cast<const in_t*>(a.hsrc) + ((size_t)b * a.hrows + ap) * C;
-    }
+    };
     // row r of this window [W-1 history rows ; K tokens]; only rows r < W-1 depend on the
     // accept length, so rows known to be tokens take xrow_at and their loads need not wait for it
     auto wrow = [&](int r) -> const in_t* { return r < CW - 1 ? HS + (size_t)r * C : X + (size_t)(r - (CW - 1)) * C; };
@@ -360,28 +390,49 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
         constexpr int TPG = STEP ? (KP + TPC - 1) / TPC : 1;          // tokens per thread
         constexpr int NXR = STEP ? TPG + CW - 1 : 1;
         constexpr int NWV = STEP ? ((CW - 1 + KMAX) * RPG + kThreads - 1) / kThreads : 1;
-        const int chi = gtid % QKC, t0 = (gtid / QKC) * TPG;
+        // QKC is a multiple of 64, so a wave shares its run of tokens t0 .. t0+TPG-1
+        const int chi = gtid % QKC, t0 = __builtin_amdgcn_readfirstlane((gtid / QKC) * TPG);
         const size_t choff = chi < DK ? qoff + chi : koff + (chi - DK);
-        float xrow[NXR];
+        uint32_t xrow[NXR];                                           // raw window rows
         float4 tp = make_float4(0.f, 0.f, 0.f, 0.f);
-        float vrow[STEP ? NV : 1][CW];
+        uint32_t vrow[STEP ? NV : 1][CW];
         float4 vtp[STEP ? NV : 1];
-        float wv[NWV];
-        float braw = 0.f, bal = 0.f;
+        uint32_t wv[NWV];
         int par = -1;
-        if (wave == kWaves - 1 && lane < K) {
-            const size_t gi = ((size_t)b * Kb + lane) * gs + h;
-            braw = load1<IN_BF16>(a.beta_raw, gi);
-            bal = load1<IN_BF16>(a.alpha, gi);
-            if constexpr (TREE) par = a.parent[(size_t)b * Kb + lane];
+        // the gates of group sub are formed by wave kWaves-1-sub, so that in a workgroup of
+        // several groups they fall on different SIMDs.  Every lane loads the raw bits of
+        // one token's gates (index clamped, no branch), and they are converted where they
+        // are used, so no wave waits for them here.
+        const int gwave = kWaves - 1 - sub % kWaves;
+        uint32_t braw_bits, bal_bits;
+        const bool raw_gates = a.dt_bias != nullptr;
+        float dtb, alog;                             // the head's dt_bias and A_log (raw gates)
+        {
+            // (with pre-activated gates these read a word of the token rows, and are ignored)
+            const float* fb = reinterpret_cast<const float*>(X);
+            dtb = *(raw_gates ? a.dt_bias + h : fb);
+            alog = *(raw_gates ? a.A_log + h : fb);
+            const size_t gi = ((size_t)b * Kb + (lane < K ? lane : K - 1)) * gs + h;
+            if constexpr (IN_BF16) {
+                braw_bits = reinterpret_cast<const uint16_t*>(a.beta_raw)[gi];
+                bal_bits = reinterpret_cast<const uint16_t*>(a.alpha)[gi];
+            } else {
+                braw_bits = reinterpret_cast<const uint32_t*>(a.beta_raw)[gi];
+                bal_bits = reinterpret_cast<const uint32_t*>(a.alpha)[gi];
+            }
+            if constexpr (TREE) {
+                if (wave == gwave && lane < K) par = a.parent[(size_t)b * Kb + lane];
+            }
         }
         // the gates of every token and their running sums (the last wave): they need only
         // the gate loads, so the fused step forms them before its conv, in the wait for the rows
         auto do_gates = [&]() {
-            if (wave == kWaves - 1) {
+            if (wave == gwave) {
                 // lane t: gates of token t, then G_t = g_0 + ... + g_t by a scan over the lanes
                 float be = 0.f, g = 0.f;
-                if (lane < K) gate(braw, bal, a.dt_bias, a.A_log, h, be, g);
+                const float braw = __uint_as_float(IN_BF16 ? braw_bits << 16 : braw_bits);
+                const float bal = __uint_as_float(IN_BF16 ? bal_bits << 16 : bal_bits);
+                if (lane < K) gate(braw, bal, raw_gates, dtb, alog, be, g);
                 float G;
                 if constexpr (TREE) {
                     // G_t = sum of g over the root path of node t, and its strict ancestors, by
@@ -422,7 +473,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
 #pragma unroll
             for (int m = CW - 1; m < NXR; ++m) {
                 const int r = t0 + m < CW - 2 + K ? t0 + m : CW - 2 + K;
-                xrow[m] = load1<IN_BF16>(xrow_at(r), choff);
+                xrow[m] = ldraw<IN_BF16>(xrow_at(r), choff);
             }
 #pragma unroll
             for (int n = 0; n < NV; ++n) {
@@ -432,12 +483,15 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
                 const int tc = t < K ? t : K - 1;
                 vtp[n] = *reinterpret_cast<const float4*>(a.w + vch * CW);
-                vrow[n][CW - 1] = load1<IN_BF16>(xrow_at(tc + CW - 1), vch);
+                vrow[n][CW - 1] = ldraw<IN_BF16>(xrow_at(tc + CW - 1), vch);
             }
+            // then the accept length, the start state it picks and the window rows that
+            // depend on it (the history rows; for runs past them, token rows again)
+            pick_start();
 #pragma unroll
             for (int m = 0; m < CW - 1; ++m) {
                 const int r = t0 + m < CW - 2 + K ? t0 + m : CW - 2 + K;
-                xrow[m] = load1<IN_BF16>(wrow(r), choff);
+                xrow[m] = ldraw<IN_BF16>(wrow(r), choff);
             }
 #pragma unroll
             for (int n = 0; n < NV; ++n) {
@@ -447,14 +501,14 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
                 const int tc = t < K ? t : K - 1;
 #pragma unroll
-                for (int jj = 0; jj < CW - 1; ++jj) vrow[n][jj] = load1<IN_BF16>(wrow(tc + jj), vch);
+                for (int jj = 0; jj < CW - 1; ++jj) vrow[n][jj] = ldraw<IN_BF16>(wrow(tc + jj), vch);
             }
 #pragma unroll
             for (int n = 0; n < NWV; ++n) {
                 const int idx = tid + n * kThreads;
                 const int r = idx / RPG, gr = blockIdx.x * RPG + idx % RPG;
                 const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
-                wv[n] = load1<IN_BF16>(wrow(r < CW - 2 + K ? r : CW - 2 + K), vch);
+                wv[n] = ldraw<IN_BF16>(wrow(r < CW - 2 + K ? r : CW - 2 + K), vch);
             }
         } else {
 #pragma unroll
@@ -482,19 +536,20 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
         }
         if constexpr (STEP) {
             do_gates();
-            // the checkpoint: this window's start state
-            if (a.S_ckpt && live) store_f4<true>(a.S_ckpt + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S0);
             // the conv, as the conv kernels compute it; the conv outputs and the window
             // rows are written by one workgroup per key head (q, k) and by each
-            // workgroup for its own rows (v)
+            // workgroup for its own rows (v).  The tokens whose rows are all token rows
+            // come first, so the history rows picked by the accept length arrive meanwhile.
             const bool qk_writer = ((blockIdx.y * NG) % (Hv / Hk)) == 0 && blockIdx.x == 0;
             const int cl = chi < DK ? chi : chi - DK;
             const float tap[CW] = {tp.x, tp.y, tp.z, tp.w};
 #pragma unroll
-            for (int m = 0; m < TPG; ++m) {
+            for (int mm = 0; mm < TPG; ++mm) {
+                const int m = (mm + CW - 1) % TPG;   // a rotation of 0 .. TPG-1
                 const int t = t0 + m;
                 if (t < KP) {
-                    const float col[CW] = {xrow[m], xrow[m + 1], xrow[m + 2], xrow[m + 3]};
+                    const float col[CW] = {rawf<IN_BF16>(xrow[m]), rawf<IN_BF16>(xrow[m + 1]), rawf<IN_BF16>(xrow[m + 2]),
+                                           rawf<IN_BF16>(xrow[m + 3])};
                     if constexpr (IN_BF16) {
                         const uint16_t hb = t < K ? conv_silu_bf16(conv_pre<CW>(tap, col)) : (uint16_t)0;
                         (chi < DK ? qs : ks)[t][cl] = hb;
@@ -507,13 +562,15 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                     }
                 }
             }
+            // the checkpoint: this window's start state
+            if (a.S_ckpt && live) store_f4<true>(a.S_ckpt + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S0);
             in_t* Wb = a.win ? reinterpret_cast<in_t*>(a.win) + (size_t)b * (CW - 1 + Kb) * C : nullptr;
             if (Wb && qk_writer) {
                 // rows t0+W-1 .. t0+TPG+W-2 (the newest of each token), and the history rows for t0 = 0
 #pragma unroll
                 for (int m = 0; m < NXR; ++m) {
                     const int r = t0 + m;
-                    if ((m >= CW - 1 || t0 == 0) && r < CW - 1 + K) store1<IN_BF16>(Wb, (size_t)r * C + choff, xrow[m]);
+                    if ((m >= CW - 1 || t0 == 0) && r < CW - 1 + K) straw<IN_BF16>(Wb, (size_t)r * C + choff, xrow[m]);
                 }
             }
             if (Wb) {
@@ -522,7 +579,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                     const int idx = tid + n * kThreads;
                     const int r = idx / RPG, gr = blockIdx.x * RPG + idx % RPG;
                     if (idx < (CW - 1 + KMAX) * RPG && r < CW - 1 + K && gr < dv)
-                        store1<IN_BF16>(Wb, (size_t)r * C + 2 * (size_t)Hk * DK + (size_t)h * dv + gr, wv[n]);
+                        straw<IN_BF16>(Wb, (size_t)r * C + 2 * (size_t)Hk * DK + (size_t)h * dv + gr, wv[n]);
                 }
             }
 #pragma unroll
@@ -531,9 +588,12 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 const int t = idx / RPG, rr = idx % RPG;
                 const int gr = blockIdx.x * RPG + rr;
                 const float tv[CW] = {vtp[n].x, vtp[n].y, vtp[n].z, vtp[n].w};
+                float vc[CW];
+#pragma unroll
+                for (int jj = 0; jj < CW; ++jj) vc[jj] = rawf<IN_BF16>(vrow[n][jj]);
                 float v;
-                if constexpr (IN_BF16) v = bf16_to_f32(conv_silu_bf16(conv_pre<CW>(tv, vrow[n])));
-                else v = conv_silu(conv_pre<CW>(tv, vrow[n]));
+                if constexpr (IN_BF16) v = bf16_to_f32(conv_silu_bf16(conv_pre<CW>(tv, vc)));
+                else v = conv_silu(conv_pre<CW>(tv, vc));
                 vv[n] = idx < KMAX * RPG ? v : 0.f;
                 if (a.y && idx < KMAX * RPG && t < K && gr < dv)
                     store1<IN_BF16>(a.y, ((size_t)b * Kb + t) * C + 2 * (size_t)Hk * DK + (size_t)h * dv + gr, v);
@@ -708,7 +768,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             if (t < K - 1) {
                 if (Hrow) store_f4<NT>(Hrow + (size_t)t * Hstep, S);
             } else if (t == K - 1) {
-                store_f4<false>(a.S_out + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S);
+                store_f4<NT>(a.S_out + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S);
             }
         }
     };
