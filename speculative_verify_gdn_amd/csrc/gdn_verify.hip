@@ -1,51 +1,58 @@
 // gdn_verify.hip -- gated delta rule over a K-token verify window with
-// intermediate-state capture, chunkwise in WY form (gfx950).
+// intermediate-state capture (gfx950): the chain as a token recurrence with
+// the state in registers, the draft tree chunkwise in WY form on MFMA.
 //
-// The step the pages describe as a fused WY-chunkwise GDN verify that writes
-// the final state and every intermediate state in one pass (atlas PR #297,
-// commit message on gated_delta_rule_wy16.cu), with the raw gates applied in
-// the kernel, q/k broadcast from key heads and one L2 normalisation of the
-// q|k slab (lucebox PR #637, commit messages on raw-gate gated_delta_net and
-// the DeltaNet block; review excerpt of gated_delta_net.cu).
+// The step the pages describe as a fused GDN verify that writes the final
+// state and every intermediate state in one pass (atlas PR #297, commit message
+// on gated_delta_rule_wy16.cu), with the raw gates applied in the kernel, q/k
+// broadcast from key heads and one L2 normalisation of the q|k slab (lucebox
+// PR #637, commit messages on raw-gate gated_delta_net and the DeltaNet block;
+// review excerpt of gated_delta_net.cu).
 //
-// Math, per sequence b and value head h, with G_t = sum_{s<=t} g_s:
-//   A[t][s] = beta_t e^{G_t-G_s} k^_t.k^_s        (s < t)
-//   M[t][s] = e^{G_t-G_s} q^_t.k^_s                (s <= t)
-//   (I + A) u = beta (v - e^{G} S_in k^)            (one column per state row)
-//   o_t = e^{G_t} S_in q^_t + sum_{s<=t} M[t][s] u_s
-//   H_t = e^{g_t} H_{t-1} + u_t k^_t^T,  H_{-1} = S_in
+// Chain (a window of consecutive tokens), per sequence b and value head h:
+//   p = H_{t-1} k^_t,  u_t = beta_t (v_t - gamma_t p),
+//   H_t = gamma_t H_{t-1} + u_t k^_t^T,  o_t = H_t q^_t,  H_{-1} = S_in.
+// Every H_t is written out, so the chunkwise WY form would save no bytes here;
+// the token order lets H_0 leave as soon as the window is staged, and each later
+// state one row sum after its predecessor.  (Measured on the K=16 window: the
+// WY form's MFMA prologue and triangular solve put the first store 1 us later,
+// and the launch took 0.7 us longer.)
+//
 // Tree verify (the drafted tokens form a tree; lucebox PR #637, DDTree drafting
-// in the commit messages): node t continues its parent's state, so G_t sums g
-// along the root path, A and M keep only the pairs (t, s) with s an ancestor of t
-// (or t itself, for M), and H_t = e^{G_t} S_in + sum over the path of
-// e^{G_t-G_s} u_s k^_s^T is formed directly for every node (no state leaves a
-// register chain, since nodes of different branches interleave).
-// (I + A)^{-1} is the WY / UT transform of the window: it turns the K delta
+// in the commit messages), with G_t = sum of g along the root path of node t:
+//   A[t][s] = beta_t e^{G_t-G_s} k^_t.k^_s        (s a strict ancestor of t)
+//   M[t][s] = e^{G_t-G_s} q^_t.k^_s                (s an ancestor of t or t)
+//   (I + A) u = beta (v - e^{G} S_in k^)            (one column per state row)
+//   o_t = e^{G_t} S_in q^_t + sum_s M[t][s] u_s
+//   H_t = e^{G_t} S_in + sum over the path of e^{G_t-G_s} u_s k^_s^T
+// (I + A)^{-1} is the WY / UT transform of the tree: it turns the delta
 // corrections into one triangular solve that needs S_in only through the
-// contractions S_in K^T and S_in Q^T.  Only exponentials of G_t - G_s with
-// s <= t are formed (no ratio of decays).
+// contractions S_in K^T and S_in Q^T, so nodes of different branches, which
+// interleave in the numbering, need no state chain.  Only exponentials of
+// G_t - G_s with s an ancestor are formed (no ratio of decays).
 //
 // Mapping.  A workgroup is 4 waves holding RPG = 1024/DK consecutive state
-// rows of one head.  In the streaming phase a lane owns one float4 of one row
-// (a row is DK/4 lanes), so one store instruction of a wave writes whole rows
-// -- 1 KB contiguous at DK=128.
-//   1. the raw q, k of the key head, the workgroup's S_in rows and their v
-//      values go to LDS with a few 16-byte loads per thread (branch-free, so
-//      they are in flight together); the q/k norms come from the staging
-//      threads (dot products and DPP row sums), the gates and their running
-//      sums from the last wave; each lane keeps its own state float4;
-//   2. the contractions run on MFMA, one job per wave: K K^T and A (wave 0);
-//      Q K^T and M (wave 3); K S^T (wave 1) and Q S^T (wave 2).  The norms,
-//      gates and running sums of g are already known from phase 1.  Operands:
+// rows of one head.  A lane owns one float4 of one row (a row is DK/4 lanes),
+// so one store instruction of a wave writes whole rows -- 1 KB contiguous at
+// DK=128.
+//   1. the raw q, k of the key head and the v values of the workgroup's rows
+//      go to LDS with a few 16-byte loads per thread (branch-free, so they are
+//      in flight together); the q/k norms come from the staging threads (dot
+//      products and DPP row sums), the gates and their running sums from one
+//      wave; each lane keeps its own state float4 in registers;
+//   chain: 2. per token, the two row sums (p, o_t) are DPP sums over the row's
+//      lanes; every lane streams H_t with one 16-byte store -- the bulk of the
+//      bytes of the whole step -- and lane j of a row keeps o_j;
+//   tree: 2. the contractions run on MFMA, one job per wave: K K^T and A (wave
+//      0); Q K^T and M (wave 3); K S^T (wave 1) and Q S^T (wave 2).  Operands:
 //      raw q, k in bf16 (products of bf16 are exact, accumulation is fp32)
 //      against the state split into two bf16 halves (hi + lo keeps about 16
-//      bits), 16x16x32 bf16 instructions; for f32 inputs 16x16x4 f32
-//      instructions on the unsplit values;
-//   3. per row: the forward substitution for u_t is shared by the row's lanes
-//      (lane j owns token j, each finished u_t is broadcast with v_readlane),
-//      which also gives o_t; as soon as u_t is known every lane streams
-//      H_t = gamma_t H_{t-1} + u_t k^_t with one 16-byte store -- the bulk of
-//      the bytes of the whole step.
+//      bits, split once while staging), 16x16x32 bf16 instructions; for f32
+//      inputs 16x16x4 f32 instructions on the unsplit values;
+//   tree: 3. per row: the forward substitution for u_t is shared by the row's
+//      lanes (lane j owns node j, each finished u_t is broadcast with
+//      v_readlane), which also gives o_t; node states stream as their u_t
+//      become known.
 #include "gdn_conv_math.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -65,7 +72,13 @@ struct VerifySmem {
     static constexpr int QW = DK + (IN_BF16 ? 8 : 4);   // padded row: rows start 4 banks apart
     in_t q[KP][QW];                 // raw q of the key head, rows >= K zero
     in_t k[KP][QW];                 // raw k
-    float S[NP][DK + 4];            // S_in rows of the workgroup (rows >= RPG zero)
+    // S_in rows of the workgroup (rows >= RPG zero): fp32 rows for f32 inputs; for bf16
+    // inputs the MFMA operands, each value split into bf16 halves hi + lo (hi = top 16
+    // bits, lo = top 16 bits of the remainder), rows padded like q and k
+    using s_t = typename std::conditional<IN_BF16, uint16_t, float>::type;
+    static constexpr int SW = IN_BF16 ? DK + 8 : DK + 4;
+    s_t S[NP][SW];                  // the rows, or their hi halves
+    s_t Slo[IN_BF16 ? NP : 1][SW];  // lo halves (bf16 inputs only)
     float P[RPG][KP + 4];           // raw k_t . S_in[row]
     float R[RPG][KP + 4];           // raw q_t . S_in[row]
     float A[KP][KP + 4];            // beta_t e^{G_t-G_s} k^_t.k^_s, s < t
@@ -153,20 +166,6 @@ __device__ __forceinline__ void gate(float braw, float al, const float* dt_bias,
     else gate(braw, al, false, 0.f, 0.f, beta, g);
 }
 
-// bf16 halves of 8 floats: hi = top 16 bits, lo = top 16 bits of the remainder
-__device__ __forceinline__ void split8(const float4& x0, const float4& x1, bf16x8_t& hi, bf16x8_t& lo)
-{
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t u = __float_as_uint(xs[e]);
-        const uint32_t uh = u & 0xffff0000u;
-        const float rem = xs[e] - __uint_as_float(uh);
-        hi[e] = (short)(uh >> 16);
-        lo[e] = (short)(__float_as_uint(rem) >> 16);
-    }
-}
-
 // D[m][n] = sum_c X[tm*16+m][c] Y[tn*16+n][c] over the DK columns.
 // X, Y raw q/k rows in LDS.  Lane l feeds row l%16 of both operands with the
 // same k-slice, so the product is the contraction whatever order the
@@ -194,9 +193,11 @@ __device__ __forceinline__ f32x4_t gram_tile(const in_t (*X)[QW], const in_t (*Y
     return acc;
 }
 
-// D[m][n] = sum_c X[tm*16+m][c] S[tn*16+n][c]: raw q/k rows against fp32 state rows
-template <int DK, int QW, int SW, bool IN_BF16, typename in_t>
-__device__ __forceinline__ f32x4_t state_tile(const in_t (*X)[QW], const float (*S)[SW], int tm, int tn, int lane)
+// D[m][n] = sum_c X[tm*16+m][c] S[tn*16+n][c]: raw q/k rows against the state rows
+// (bf16: S holds the hi halves and Sl the lo halves of the fp32 state)
+template <int DK, int QW, int SW, bool IN_BF16, typename in_t, typename s_t>
+__device__ __forceinline__ f32x4_t state_tile(const in_t (*X)[QW], const s_t (*S)[SW], const s_t (*Sl)[SW], int tm,
+                                              int tn, int lane)
 {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int r = lane & 15, ks = lane >> 4;
@@ -204,9 +205,8 @@ __device__ __forceinline__ f32x4_t state_tile(const in_t (*X)[QW], const float (
 #pragma unroll
         for (int kk = 0; kk < DK / 32; ++kk) {
             const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&X[tm * 16 + r][32 * kk + 8 * ks]);
-            const float* sp = &S[tn * 16 + r][32 * kk + 8 * ks];
-            bf16x8_t hi, lo;
-            split8(*reinterpret_cast<const float4*>(sp), *reinterpret_cast<const float4*>(sp + 4), hi, lo);
+            const bf16x8_t hi = *reinterpret_cast<const bf16x8_t*>(&S[tn * 16 + r][32 * kk + 8 * ks]);
+            const bf16x8_t lo = *reinterpret_cast<const bf16x8_t*>(&Sl[tn * 16 + r][32 * kk + 8 * ks]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, hi, acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, lo, acc, 0, 0, 0);
         }
@@ -634,10 +634,35 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
         }
         if (!live) S0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
         S = S0;
-        *reinterpret_cast<f32x4_t*>(&sm.S[rloc][c]) = S0;
-        if constexpr (RPG < 16) {
-            for (int idx = tid; idx < (16 - RPG) * LPR; idx += kThreads)
-                *reinterpret_cast<f32x4_t*>(&sm.S[RPG + idx / LPR][4 * (idx % LPR)]) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if constexpr (!TREE) {
+            // the chain path keeps the state in registers only
+        } else if constexpr (IN_BF16) {
+            // the MFMA operands of this lane's four values: bf16 halves
+            uint32_t hw[2], lw[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t u0 = __float_as_uint(S0[2 * e]), u1 = __float_as_uint(S0[2 * e + 1]);
+                const uint32_t h0 = u0 & 0xffff0000u, h1 = u1 & 0xffff0000u;
+                const uint32_t l0 = __float_as_uint(S0[2 * e] - __uint_as_float(h0)) >> 16;
+                const uint32_t l1 = __float_as_uint(S0[2 * e + 1] - __uint_as_float(h1)) & 0xffff0000u;
+                hw[e] = (h0 >> 16) | h1;
+                lw[e] = l0 | l1;
+            }
+            *reinterpret_cast<uint2*>(&sm.S[rloc][c]) = make_uint2(hw[0], hw[1]);
+            *reinterpret_cast<uint2*>(&sm.Slo[rloc][c]) = make_uint2(lw[0], lw[1]);
+        } else {
+            *reinterpret_cast<f32x4_t*>(&sm.S[rloc][c]) = S0;
+        }
+        if constexpr (TREE && RPG < 16) {
+            for (int idx = tid; idx < (16 - RPG) * LPR; idx += kThreads) {
+                const int rr = RPG + idx / LPR, cc = 4 * (idx % LPR);
+                if constexpr (IN_BF16) {
+                    *reinterpret_cast<uint2*>(&sm.S[rr][cc]) = make_uint2(0, 0);
+                    *reinterpret_cast<uint2*>(&sm.Slo[rr][cc]) = make_uint2(0, 0);
+                } else {
+                    *reinterpret_cast<f32x4_t*>(&sm.S[rr][cc]) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
         }
 #pragma unroll
         for (int n = 0; n < NV; ++n) {
@@ -648,7 +673,56 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     }
     __syncthreads();
 
-    // ---- 2. contractions on MFMA
+    if constexpr (!TREE) {
+        // ---- 2. the chain: the token recurrence, state in registers.  Every state is
+        // written out, so the WY form would save no bytes here, and the token order lets
+        // H_0 leave as soon as phase 1 is done.  Per token, with the row sums over the
+        // row's lanes (DPP):
+        //   p = S k^_t,  u = beta_t (v_t - gamma_t p),  S = gamma_t S + u k^_t,  o_t = S q^_t
+        float* Hrow = a.H ? a.H + ((size_t)b * (Kb - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
+        const size_t Hstep = (size_t)Hv * SD;
+        constexpr int NO = (KMAX + LPR - 1) / LPR;   // outputs held per lane: lane j keeps o_{j + m LPR}
+        float ot[NO];
+#pragma unroll
+        for (int m = 0; m < NO; ++m) ot[m] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KMAX; ++t) {
+            if (t < K) {
+                const float4 tt = sm.tok[t];          // beta, e^{G}, 1/|k|, 1/|q|
+                const float gm = sm.gam[t];
+                const float4 kx = lds4<IN_BF16>(&ks[t][c]);
+                const float v = sm.V[t][rloc];
+                const float sk = group_sum<LPR>(S[0] * kx.x + S[1] * kx.y + S[2] * kx.z + S[3] * kx.w) * tt.z;
+                const float cu = tt.x * (v - gm * sk) * tt.z;   // u / |k_t|
+                S[0] = __builtin_fmaf(cu, kx.x, gm * S[0]);
+                S[1] = __builtin_fmaf(cu, kx.y, gm * S[1]);
+                S[2] = __builtin_fmaf(cu, kx.z, gm * S[2]);
+                S[3] = __builtin_fmaf(cu, kx.w, gm * S[3]);
+                if (live) {
+                    if (t < K - 1) {
+                        if (Hrow) store_f4<NT>(Hrow + (size_t)t * Hstep, S);
+                    } else {
+                        store_f4<NT>(a.S_out + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S);
+                    }
+                }
+                if (a.o) {
+                    const float4 qx = lds4<IN_BF16>(&qs[t][c]);
+                    const float o = group_sum<LPR>(S[0] * qx.x + S[1] * qx.y + S[2] * qx.z + S[3] * qx.w) * tt.w;
+                    if (j == t % LPR) ot[t / LPR] = o;
+                }
+            }
+        }
+        if (a.o && live) {
+#pragma unroll
+            for (int m = 0; m < NO; ++m) {
+                const int t = m * LPR + j;
+                if (t < K) store1<O_BF16>(a.o, (((size_t)b * Kb + t) * Hv + h) * dv + i, ot[m]);
+            }
+        }
+        return;
+    }
+
+    // ---- 2. contractions on MFMA (tree)
     // wave 0: K K^T -> A
     // wave 3: Q K^T -> M
     // waves 1, 2: K S^T, Q S^T
@@ -695,7 +769,8 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
         for (int tm = 0; tm < TB; ++tm)
 #pragma unroll
             for (int tn = 0; tn < NTL; ++tn) {
-                const f32x4_t d = state_tile<DK, Smem::QW, DK + 4, IN_BF16, in_t>(Xs, sm.S, tm, tn, lane);
+                const f32x4_t d = state_tile<DK, Smem::QW, Smem::SW, IN_BF16, in_t, typename Smem::s_t>(
+                    Xs, sm.S, sm.Slo, tm, tn, lane);
                 const int row = tn * 16 + n16;
                 if (row < RPG) {
 #pragma unroll
@@ -756,22 +831,6 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
         hc[t & 3] = Ht;
         if (live && t < K) store_f4<NT>(Hrow + (size_t)t * Hstep, Ht);
     };
-    auto stream_token = [&](int t, float ut) {
-        const float gm = sm.gam[t];
-        const float cu = ut * sm.tok[t].z;
-        const float4 kx = lds4<IN_BF16>(&ks[t][c]);
-        S[0] = __builtin_fmaf(cu, kx.x, gm * S[0]);
-        S[1] = __builtin_fmaf(cu, kx.y, gm * S[1]);
-        S[2] = __builtin_fmaf(cu, kx.z, gm * S[2]);
-        S[3] = __builtin_fmaf(cu, kx.w, gm * S[3]);
-        if (live) {
-            if (t < K - 1) {
-                if (Hrow) store_f4<NT>(Hrow + (size_t)t * Hstep, S);
-            } else if (t == K - 1) {
-                store_f4<NT>(a.S_out + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S);
-            }
-        }
-    };
     if constexpr (KMAX <= LPR) {
         // Lane j of a row owns token j: it forms b_j, keeps row j of A and of M in
         // registers, and at step t the owner of token t has its u_t final; every
@@ -807,14 +866,10 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             // A[j][t] = 0 for t >= j, so finished lanes keep their value
             part = __builtin_fmaf(-arow[t], mine, part);
             ot = __builtin_fmaf(mrow[t], mine, ot);  // M[j][t] = 0 for t > j
-            if constexpr (TREE) {
-                // one lane per row publishes u_t; the row's lanes read it back in
-                // program order (same wave), so no barrier is needed
-                if (j == 0) sm.U[rloc][t] = mine;
-                stream_node(t, mine);
-            } else {
-                stream_token(t, mine);
-            }
+            // one lane per row publishes u_t; the row's lanes read it back in program
+            // order (same wave), so no barrier is needed
+            if (j == 0) sm.U[rloc][t] = mine;
+            stream_node(t, mine);
         }
         if (own && live && a.o) store1<O_BF16>(a.o, (((size_t)b * Kb + j) * Hv + h) * dv + i, ot);
     } else {
@@ -839,17 +894,12 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 store1<O_BF16>(a.o, (((size_t)b * Kb + t) * Hv + h) * dv + i, ot);
             }
         }
-        if constexpr (TREE) {
-            if (j == 0) {
+        if (j == 0) {
 #pragma unroll
-                for (int t = 0; t < KMAX; ++t) sm.U[rloc][t] = u[t];
-            }
-#pragma unroll
-            for (int t = 0; t < KMAX; ++t) stream_node(t, u[t]);
-        } else {
-#pragma unroll
-            for (int t = 0; t < KMAX; ++t) stream_token(t, u[t]);
+            for (int t = 0; t < KMAX; ++t) sm.U[rloc][t] = u[t];
         }
+#pragma unroll
+        for (int t = 0; t < KMAX; ++t) stream_node(t, u[t]);
     }
 }
 
@@ -857,7 +907,8 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
 // owns one float4 of one state row (a row is DK/4 lanes of one wave); the q/k norms
 // and the contractions are sums over the row's lanes (DPP):
 //   u = beta (v - gamma S k^),   S' = gamma S + u k^^T,   o = S' q^
-// The same recurrence as the window kernel's first token, in another rounding order.
+// The same recurrence as the window kernel's first token, with the norms summed in
+// another order.
 template <int DK, bool IN_BF16, bool O_BF16>
 __global__ __launch_bounds__(kThreads) void decode_kernel(VerifyArgs a)
 {

@@ -154,12 +154,12 @@ def test_verify_tree_matches_oracle(name, over, shape, o_dtype):
     say("worst state err/fro %.3g" % worst)
 
 
-def test_verify_tree_chain_outputs_equal_chain_verify():
-    # a chain-shaped tree takes the chain kernel's arithmetic for A, M, u and o (path sums
-    # by pointer jumping are the chain's scan for N <= 16) and, every parent being the node
-    # before, the chain's state update: o and every state bit for bit
+def test_verify_tree_chain_outputs_match_chain_verify():
+    # a chain-shaped tree and the chain verify evaluate one recurrence in two orders (the
+    # tree's WY form with ancestor masks, the chain's token recurrence): every state and
+    # output agree to well inside the parity bar (2e-4 of the state's Frobenius norm)
     wl = synth.small("verify16", B=2, Hk=4, Hv=12)
-    say("verify_tree chain == verify", wl)
+    say("verify_tree chain ~ verify", wl)
     inp, qkv, par = _tree_case(wl, "chain", seed=12)
     H, o = _verify_tree_gpu(wl, inp, qkv, par)
     d = {k: dev(v) for k, v in inp.items()}
@@ -168,8 +168,13 @@ def test_verify_tree_chain_outputs_equal_chain_verify():
     oc = torch.empty_like(o)
     gdn.verify(dev(qkv), d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, Hc, oc, wl.Hk)
     torch.cuda.synchronize()
-    assert torch.equal(o, oc)
-    assert torch.equal(H, torch.cat([Hc, S_out[:, None]], dim=1))
+    Hch = torch.cat([Hc, S_out[:, None]], dim=1).double().cpu()
+    fro = torch.linalg.norm(Hch, dim=(-1, -2))
+    err = (H.double().cpu() - Hch).abs().amax(dim=(-1, -2))
+    assert bool((err <= 2e-4 * fro).all()), float((err / fro).max())
+    # o_t[i] is row i of H_t against a unit vector: bounded by the state's norm
+    oerr = (o.double().cpu() - oc.double().cpu()).abs().amax(dim=-1)
+    assert bool((oerr <= 2e-4 * fro).all()), float((oerr / fro).max())
 
 
 def test_verify_tree_stacked_gates_and_bad_parents():
