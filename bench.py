@@ -3,8 +3,8 @@
 
 One step is one pass of the whole hot path of one GDN layer over one verify
 window: gdn_conv_step (fused causal conv1d + SiLU, history write-back, window
-capture) -> gdn_verify (gated delta rule over K=16 tokens, WY form, every
-intermediate state written) -> gdn_rollback (restore conv and GDN state to a
+capture) -> gdn_verify (gated delta rule over K=16 tokens, every intermediate
+state written) -> gdn_rollback (restore conv and GDN state to a
 drawn accept length).  Workload: B=1, Hk=16 key heads, Hv=48 value heads,
 d=128, conv width 4 over C=10240 channels, bf16 inputs, fp32 state; seeded
 synthetic inputs (speculative_verify_gdn_amd.synth), accept length ~ U{0..16}.

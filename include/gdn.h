@@ -13,8 +13,9 @@
  *      intermediates);
  *   2. the gated delta rule over the K window tokens with raw gates applied
  *      inside the kernel, q and k L2-normalised and broadcast from key heads
- *      to value heads, evaluated chunkwise in WY form, writing the final state
- *      plus every intermediate state H_0..H_{K-2} (lucebox PR #637: commit
+ *      to value heads, writing the final state plus every intermediate state
+ *      H_0..H_{K-2} (token by token for a chain of drafts, chunkwise in WY
+ *      form for a draft tree and for prefill) (lucebox PR #637: commit
  *      messages on raw-gate gated_delta_net and the single l2_norm over the
  *      q|k slab, review excerpt of gated_delta_net.cu; atlas PR #297: commit
  *      message on gated_delta_rule_wy16.cu and its opt-in fp32 output);
@@ -114,11 +115,12 @@ int gdn_conv_step(const void *x, const float *w, void *hist, void *y, void *win_
  * switches to the identity above 20).  If both are NULL, beta_raw holds beta
  * and alpha holds g already activated.  One NULL and one not is GDN_EINVAL.
  *
- * Evaluation: chunkwise WY form over the window.  With G_t = sum_{s<=t} g_s,
- *   A[t][s] = beta_t exp(G_t - G_s) k^_t.k^_s  (s < t),  T = (I + A)^{-1},
- *   u = T (beta (v - exp(G) S_in k^))          (per state row),
- *   o_t = exp(G_t) S_in q^_t + sum_{s<=t} exp(G_t - G_s) (q^_t.k^_s) u_s,
- *   H_t = exp(g_t) H_{t-1} + u_t k^_t^T,       H_{-1} = S_in.
+ * Evaluation: the token recurrence over the window (every state is written, so
+ * the chunkwise WY form, which the pages name, would save no bytes here; it is
+ * the same recurrence, and gdn_verify_tree and gdn_prefill_chunked use it):
+ *   u_t = beta_t (v_t - exp(g_t) H_{t-1} k^_t),
+ *   H_t = exp(g_t) H_{t-1} + u_t k^_t^T,       H_{-1} = S_in,
+ *   o_t = H_t q^_t.
  *
  *   qkv      [B][K][C]    in_dtype; C = 2*Hk*dk + Hv*dv; per token the q of
  *                         all key heads, then their k, then the v of all
