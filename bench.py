@@ -597,6 +597,31 @@ def main():
             return sum(e0.elapsed_time(e1) for e0, e1 in evs) / len(evs) * 1e3
 
     t_fused = kernel_us(fused)
+
+    # resident: the same chained step on two buffer sets only (each continues from the other), whose
+    # working set fits the 256 MB Infinity Cache -- reported beside the HBM-bound figure, labelled
+    def resident_us():
+        def fused_from(d, pv):
+            gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_out"], d["H"],
+                            d["o"], wl.Hk, prev=(pv["accept"], pv["S_ckpt"], pv["H"], pv["S_out"], pv["win"]),
+                            S_ckpt=d["S_ckpt"], win=d["win"])
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(5):
+                fused_from(sets[0], sets[1])
+                fused_from(sets[1], sets[0])
+        g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, min(K, 400) // 10)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * 10)
+
+    t_resident = resident_us() if (mode == "fused" and R >= 2 and not args.eager) else None
     t_ver = kernel_us(verify)
     t_conv = kernel_us(conv)
     t_rb = kernel_us(rollback)
@@ -670,6 +695,8 @@ def main():
             "kernel_bytes_per_launch": dom_bytes,
             "kernel_us": round(dom_us, 3),
             "verify_step_us": round(t_fused, 3),
+            "resident_step_us": None if t_resident is None else round(t_resident, 3),
+            "resident_working_set_MB": round(2 * set_bytes / 2 ** 20, 1),
             "verify_step_bytes_per_launch": sb,
             "verify_bytes_per_launch": vb,
             "verify_us": round(t_ver, 3),
