@@ -93,6 +93,11 @@ CASES = [
     ("verify16", dict(B=3, Hk=2, Hv=4, dk=64, dv=64), [2, 16, 0]),
     ("verify16", dict(B=2, Hk=2, Hv=4, dk=32, dv=32, T=9), [4, 9]),
     ("tiny", dict(B=2), [1, 4]),                                   # fp32 inputs
+    # the full sizes, in the launch configuration the bench times (three value heads per
+    # 12-wave workgroup): verify16 (B=1, 48 value heads, d=128, K=16) and batched (B=32, K=8)
+    ("verify16", dict(), [9]),
+    ("batched", dict(), [0, 8, 3, 5, 1, 7, 2, 6, 4, 8, 0, 5, 3, 1, 7, 2, 8, 6, 4, 0, 2, 5, 7, 3, 1, 8, 6, 0, 4, 2,
+                         5, 7]),
 ]
 
 
@@ -126,9 +131,10 @@ def test_fused_step_equals_separate_calls(name, over, acc):
     assert_same(Bo, B_ref, "second window", wl.T)
 
 
-def test_fused_step_chain_against_oracle():
-    wl = synth.small("verify16", B=3, Hk=4, Hv=12)
-    acc1 = [4, 0, 16]
+@pytest.mark.parametrize("over,acc1", [(dict(B=3, Hk=4, Hv=12), [4, 0, 16]),
+                                       (dict(), [11])])        # the full verify16 shape
+def test_fused_step_chain_against_oracle(over, acc1):
+    wl = synth.small("verify16", **over)
     say("verify_step two windows vs oracle", wl, acc1)
     inp1 = synth.make_inputs(wl, seed=51)
     inp2 = synth.make_inputs(wl, seed=52)
