@@ -75,14 +75,16 @@ struct VerifySmem {
     // S_in rows of the workgroup (rows >= RPG zero): fp32 rows for f32 inputs; for bf16
     // inputs the MFMA operands, each value split into bf16 halves hi + lo (hi = top 16
     // bits, lo = top 16 bits of the remainder), rows padded like q and k
+    // (the MFMA phase's arrays exist for the tree only: the chain keeps its state in registers)
     using s_t = typename std::conditional<IN_BF16, uint16_t, float>::type;
     static constexpr int SW = IN_BF16 ? DK + 8 : DK + 4;
-    s_t S[NP][SW];                  // the rows, or their hi halves
-    s_t Slo[IN_BF16 ? NP : 1][SW];  // lo halves (bf16 inputs only)
-    float P[RPG][KP + 4];           // raw k_t . S_in[row]
-    float R[RPG][KP + 4];           // raw q_t . S_in[row]
-    float A[KP][KP + 4];            // beta_t e^{G_t-G_s} k^_t.k^_s, s < t
-    float M[KP][KP + 4];            // e^{G_t-G_s} q^_t.k^_s, s <= t
+    static constexpr int TNP = TREE ? NP : 1, TRPG = TREE ? RPG : 1, TKP = TREE ? KP : 1;
+    s_t S[TNP][SW];                 // the rows, or their hi halves
+    s_t Slo[IN_BF16 ? TNP : 1][SW]; // lo halves (bf16 inputs only)
+    float P[TRPG][KP + 4];          // raw k_t . S_in[row]
+    float R[TRPG][KP + 4];          // raw q_t . S_in[row]
+    float A[TKP][KP + 4];           // beta_t e^{G_t-G_s} k^_t.k^_s, s < t
+    float M[TKP][KP + 4];           // e^{G_t-G_s} q^_t.k^_s, s <= t
     float V[KP][RPG];               // v of the workgroup's rows, per token
     float4 tok[KP];                 // per token: beta, e^{G}, 1/|k|, 1/|q|
     float gam[KP];                  // e^{g}
@@ -720,7 +722,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
             }
         }
         return;
-    }
+    } else {
 
     // ---- 2. contractions on MFMA (tree)
     // wave 0: K K^T -> A
@@ -901,9 +903,10 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
 #pragma unroll
         for (int t = 0; t < KMAX; ++t) stream_node(t, u[t]);
     }
+    }  // tree
 }
 
-// One token (K = 1: a decode step) needs no WY solve, no LDS and no barrier.  A lane
+// One token (K = 1: a decode step) needs no solve, no LDS and no barrier.  A lane
 // owns one float4 of one state row (a row is DK/4 lanes of one wave); the q/k norms
 // and the contractions are sums over the row's lanes (DPP):
 //   u = beta (v - gamma S k^),   S' = gamma S + u k^^T,   o = S' q^
