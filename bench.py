@@ -411,8 +411,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the verify step shards "
-              "by key-head group or by sequence with no exchange; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the verify step shards "
+              "by key-head group or by sequence with no exchange between GPUs). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
