@@ -700,6 +700,10 @@ def main():
             "verify_step_bytes_per_launch": sb,
             "verify_bytes_per_launch": vb,
             "verify_us": round(t_ver, 3),
+            # state traffic alone (the start state read, every state written; the fused step also writes
+            # the checkpoint) over the kernel's duration
+            "verify_state_GBs": round((wl.T + 1) * wl.B * wl.Hv * wl.dv * wl.dk * 4 / (t_ver * 1e-6) / 1e9, 1),
+            "verify_step_state_GBs": round((wl.T + 2) * wl.B * wl.Hv * wl.dv * wl.dk * 4 / (t_fused * 1e-6) / 1e9, 1),
             "conv_us": round(t_conv, 3),
             "rollback_us": round(t_rb, 3),
             "rollback_conv_us": round(t_rc, 3),
