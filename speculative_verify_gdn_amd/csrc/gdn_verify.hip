@@ -147,26 +147,19 @@ __device__ __forceinline__ float sumsq16(const uint4 u)
 }
 
 // gates of one token: raw (dtb, alog = the head's dt_bias and A_log) or, with
-// raw false, beta and g given directly
+// raw false, beta and g given directly.  Both forms are formed and one selected:
+// with no branch, nothing lets the compiler sink the loads of dtb and alog behind
+// the gate data.
 __device__ __forceinline__ void gate(float braw, float al, bool raw, float dtb, float alog, float& beta, float& g)
 {
-    if (raw) {
-        beta = __frcp_rn(1.0f + __expf(-braw));
-        const float a = al + dtb;
-        const float sp = a > 20.0f ? a : __logf(1.0f + __expf(a));
-        g = -sp * __expf(alog);
-    } else {
-        beta = braw;
-        g = al;
-    }
+    const float br = __frcp_rn(1.0f + __expf(-braw));
+    const float a = al + dtb;
+    const float sp = a > 20.0f ? a : __logf(1.0f + __expf(a));
+    const float gr = -sp * __expf(alog);
+    beta = raw ? br : braw;
+    g = raw ? gr : al;
 }
 
-__device__ __forceinline__ void gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
-                                     float& beta, float& g)
-{
-    if (dt_bias != nullptr) gate(braw, al, true, dt_bias[h], A_log[h], beta, g);
-    else gate(braw, al, false, 0.f, 0.f, beta, g);
-}
 
 // D[m][n] = sum_c X[tm*16+m][c] Y[tn*16+n][c] over the DK columns.
 // X, Y raw q/k rows in LDS.  Lane l feeds row l%16 of both operands with the
@@ -929,13 +922,22 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(VerifyArgs a)
     const size_t xb = (size_t)b * C;                 // the token's row (K = 1)
     const size_t gi = (size_t)b * (a.gstride > 0 ? a.gstride : Hv) + h;
     const size_t so = ((size_t)b * Hv + h) * SD + (size_t)ic * DK + c;
+    // the head's dt_bias and A_log with the other loads (no branch: with pre-activated gates a
+    // word of the token row is read instead and ignored), so the gates wait for one round trip.
+    // The index is zero (the host rejects a negative eps) but depends on the lane, so these are
+    // vector loads issued here rather than scalar loads placed next to their first use.
+    const bool raw_gates = a.dt_bias != nullptr;
+    const float* fb = reinterpret_cast<const float*>(a.qkv);
+    const int z0 = (int)(a.eps < 0.f) & (int)(threadIdx.x & 63);
+    const float dtb = (raw_gates ? a.dt_bias + h : fb)[z0];
+    const float alog = (raw_gates ? a.A_log + h : fb)[z0];
     const float4 qx = load4<IN_BF16>(a.qkv, xb + (size_t)hk * DK + c);
     const float4 kx = load4<IN_BF16>(a.qkv, xb + (size_t)(Hk + hk) * DK + c);
     const float v = load1<IN_BF16>(a.qkv, xb + 2 * (size_t)Hk * DK + (size_t)h * dv + ic);
     const f32x4_t S = load_f4(a.S_in + so);
     const float braw = load1<IN_BF16>(a.beta_raw, gi), bal = load1<IN_BF16>(a.alpha, gi);
     float beta, g;
-    gate(braw, bal, a.dt_bias, a.A_log, h, beta, g);
+    gate(braw, bal, raw_gates, dtb, alog, beta, g);
     const float gm = __expf(g);
     const float rk = __builtin_amdgcn_rsqf(
         group_sum<LPR>(kx.x * kx.x + kx.y * kx.y + kx.z * kx.z + kx.w * kx.w) + a.eps);
