@@ -388,7 +388,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="verify16")
     ap.add_argument("--sets", type=int, default=0, help="buffer sets cycled (0: enough to exceed 2x the MALL)")
     ap.add_argument("--eager", action="store_true", help="launch every step from Python instead of HIP graphs")
