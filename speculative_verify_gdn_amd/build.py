@@ -1,6 +1,11 @@
 """Build libgdn.so (the HIP library behind include/gdn.h) for gfx950.
 
-    python -m speculative_verify_gdn_amd.build
+    python -m speculative_verify_gdn_amd.build [--timeline]
+
+--timeline builds libgdn_timeline.so instead: the same library with the
+wall-clock marks of csrc/gdn_timeline.h compiled into the fused verify step
+(-DGDN_TIMELINE, objects in _build_timeline/), read back by
+speculative_verify_gdn_amd/timeline.py.  The product library never has them.
 
 Each .hip file under csrc/ is compiled to an object in _build/ (in parallel),
 then linked into speculative_verify_gdn_amd/libgdn.so.  Flags:
@@ -37,32 +42,35 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source and link libgdn.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Compile every HIP source and link libgdn.so (or, with timeline, libgdn_timeline.so); returns its path."""
+    build_dir = os.path.join(PKG, "_build_timeline") if timeline else BUILD
+    lib = os.path.join(PKG, "libgdn_timeline.so") if timeline else LIB
+    extra = ("-DGDN_TIMELINE",) if timeline else ()
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")), key=lambda f: -os.path.getsize(f))  # largest first
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda f: _compile(f, build_dir, extra), srcs))
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, timeline="--timeline" in sys.argv[1:])
     sys.exit(0)

@@ -139,7 +139,7 @@ int gdn_verify_ex(const void* qkv, const void* beta_raw, const void* alpha, int 
     const char* fn = "gdn_verify";
     int rc = check_gdn_shape(fn, B, K, Hk, Hv, dk, dv, in_dtype, o_dtype, l2_eps);
     if (rc) return rc;
-    REQUIRE(K <= 32, GDN_EUNSUPPORTED, "%s: K = %d > 32", fn, K);
+    REQUIRE(K <= gdn::kVerifyMax, GDN_EUNSUPPORTED, "%s: K = %d > %d", fn, K, gdn::kVerifyMax);
     REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
     REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
             "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
@@ -227,7 +227,7 @@ int gdn_replay(const int32_t* accept, const void* qkv, const void* beta_raw, con
     const char* fn = "gdn_replay";
     int rc = check_gdn_shape(fn, B, K, Hk, Hv, dk, dv, in_dtype, GDN_F32, l2_eps);
     if (rc) return rc;
-    REQUIRE(K <= 32, GDN_EUNSUPPORTED, "%s: K = %d > 32", fn, K);
+    REQUIRE(K <= gdn::kVerifyMax, GDN_EUNSUPPORTED, "%s: K = %d > %d", fn, K, gdn::kVerifyMax);
     REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
     REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
             "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
@@ -347,12 +347,14 @@ int gdn_verify_step(const int32_t* accept_prev, int K_prev, const float* S_prev_
     const char* fn = "gdn_verify_step";
     int rc = check_gdn_shape(fn, B, K, Hk, Hv, dk, dv, in_dtype, o_dtype, l2_eps);
     if (rc) return rc;
-    REQUIRE(K <= 32, GDN_EUNSUPPORTED, "%s: K = %d > 32", fn, K);
+    REQUIRE(K <= gdn::kVerifyMax, GDN_EUNSUPPORTED, "%s: K = %d > %d", fn, K, gdn::kVerifyMax);
     REQUIRE(W == 4, GDN_EUNSUPPORTED, "%s: W = %d (the fused step takes conv width 4)", fn, W);
     REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
     REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
             "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
-    if (accept_prev) REQUIRE(K_prev >= 1 && K_prev <= 32, GDN_EINVAL, "%s: K_prev = %d not in 1..32", fn, K_prev);
+    if (accept_prev)
+        REQUIRE(K_prev >= 1 && K_prev <= gdn::kVerifyMax, GDN_EINVAL, "%s: K_prev = %d not in 1..%d", fn, K_prev,
+                gdn::kVerifyMax);
     if (B == 0) return ok();
     REQUIRE(x && w && beta_raw && alpha && S_out && o, GDN_EINVAL, "%s: null pointer", fn);
     if (accept_prev) {
@@ -407,7 +409,7 @@ int gdn_verify_step(const int32_t* accept_prev, int K_prev, const float* S_prev_
     a.S_ckpt = S_ckpt;
     a.y = y;
     a.win = win;
-    return launch_status(gdn::launch_verify(a, in_dtype == GDN_BF16, o_dtype == GDN_BF16, (hipStream_t)stream), fn);
+    return launch_status(gdn::launch_step(a, in_dtype == GDN_BF16, o_dtype == GDN_BF16, (hipStream_t)stream), fn);
 }
 
 int gdn_conv_tree(const void* x, const float* w, const void* hist, const int32_t* parent, void* y, int B, int N,

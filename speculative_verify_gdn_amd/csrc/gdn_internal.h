@@ -49,6 +49,9 @@ struct VerifyArgs {
     void* win = nullptr;               // [B][3+K][C] this window's conv window, or nullptr
 };
 
+// longest verify window (tokens per sequence) of the chain calls
+constexpr int kVerifyMax = 64;
+
 // largest draft tree (nodes per sequence) of the tree calls
 constexpr int kTreeMax = 32;
 
@@ -118,6 +121,8 @@ struct PrefillArgs {
 
 hipError_t launch_conv_step(const ConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_verify(const VerifyArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
+// the fused verify step (VerifyArgs with x set): the pipelined step kernel, or the verify kernel's step mode
+hipError_t launch_step(const VerifyArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
 hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
 hipError_t launch_rollback_conv(const RollConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);

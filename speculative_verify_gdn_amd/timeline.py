@@ -1,0 +1,114 @@
+"""Phase timeline of the fused verify step (gdn_verify_step) on the verify16 workload.
+
+    python -m speculative_verify_gdn_amd.build --timeline
+    python -m speculative_verify_gdn_amd.timeline [--launches 6] [--sets 12]
+
+Loads libgdn_timeline.so (the library built with the wall-clock marks of
+csrc/gdn_timeline.h) and runs the step chained over buffer sets as bench.py
+does (set r continues from set r-1's window; the sets together exceed the
+Infinity Cache).  After warm-up, each measured launch runs alone: the marks
+are cleared, one step is launched and synchronised, and the marks are read.
+Marks (lane 0 of every wave, 100 MHz real-time counter):
+  8 entry      the wave's first instruction (before the kernel arguments are read)
+  0 start      the accept-length load issued
+  5 accept     the accept length has arrived
+  6 state      the start state has arrived (issued after the accept length)
+  7 gates_v    the gates and the v conv are done
+  1 conv0      the first chunk's q|k conv done, the checkpoint store issued
+  2 barrier    past the first barrier (the recurrence may start)
+  3 store0     the first state (H_0) store issued
+  4 end        the wave's last store issued
+Printed: one JSON line per launch with [min, p10, median, p90, max] of every
+mark in microseconds after the launch's earliest entry, the median entry and
+end per XCD (workgroup index mod 8) and the end of the slowest wave.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from speculative_verify_gdn_amd import gdn, synth  # noqa: E402
+
+TL_GROUPS, TL_WAVES, TL_MARKS = 2048, 16, 16
+NAMES = {8: "entry", 0: "start", 5: "accept", 6: "state", 7: "gates_v", 1: "conv0", 2: "barrier", 3: "store0", 4: "end"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--launches", type=int, default=6)
+    ap.add_argument("--sets", type=int, default=12)
+    ap.add_argument("--warmup", type=int, default=200)
+    args = ap.parse_args()
+    lib = gdn.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn_timeline.so"))
+    lib.gdn_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.gdn_timeline_read.restype = ctypes.c_int
+    lib.gdn_timeline_clear.restype = ctypes.c_int
+    wl = synth.WORKLOADS["verify16"]
+    dev = torch.device("cuda", 0)
+
+    def make_set(seed):
+        inp = synth.make_inputs(wl, seed=seed)
+        d = {k: v.to(dev) for k, v in inp.items()}
+        d["win"] = torch.empty(wl.B, wl.W - 1 + wl.T, wl.C, dtype=d["x"].dtype, device=dev)
+        d["S_out"] = torch.empty_like(d["S_in"])
+        d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev)
+        d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+        d["S_ckpt"] = torch.empty_like(d["S_in"])
+        return d
+
+    sets = [make_set(r) for r in range(args.sets)]
+
+    def step(r, first=False):
+        d = sets[r % len(sets)]
+        if first:
+            gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_out"], d["H"],
+                            d["o"], wl.Hk, S_in=d["S_in"], hist=d["hist"], S_ckpt=d["S_ckpt"], win=d["win"])
+            return
+        pv = sets[(r - 1) % len(sets)]
+        gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_out"], d["H"],
+                        d["o"], wl.Hk, prev=(pv["accept"], pv["S_ckpt"], pv["H"], pv["S_out"], pv["win"]),
+                        S_ckpt=d["S_ckpt"], win=d["win"])
+
+    for r in range(len(sets)):
+        step(r, first=True)
+    for r in range(args.warmup):
+        step(r)
+    torch.cuda.synchronize()
+    grid = (wl.dv // 8) * (wl.Hv // 3) * wl.B
+    nw = 12
+    buf = np.zeros(TL_GROUPS * TL_WAVES * TL_MARKS, dtype=np.uint64)
+    for n in range(args.launches):
+        assert lib.gdn_timeline_clear() == 0
+        torch.cuda.synchronize()
+        step(args.warmup + n)
+        torch.cuda.synchronize()
+        assert lib.gdn_timeline_read(buf.ctypes.data, buf.nbytes) == 0
+        t = buf.reshape(TL_GROUPS, TL_WAVES, TL_MARKS)[:grid, :nw].astype(np.int64)
+        st = t[:, :, 8]
+        t0 = st[st > 0].min()
+        out = {"launch": n}
+        for k, nm in NAMES.items():
+            v = t[:, :, k]
+            v = (v[v > 0] - t0) * 0.01   # 100 MHz -> us
+            if v.size:
+                out[nm] = [round(float(q), 2) for q in (v.min(), np.percentile(v, 10), np.median(v),
+                                                        np.percentile(v, 90), v.max())]
+        end = np.where(t[:, :, 4] > 0, (t[:, :, 4] - t0) * 0.01, np.nan).max(axis=1)   # per workgroup
+        ent = np.where(t[:, :, 8] > 0, (t[:, :, 8] - t0) * 0.01, np.nan).min(axis=1)
+        out["entry_median_by_xcd"] = [round(float(np.nanmedian(ent[x::8])), 2) for x in range(8)]
+        out["end_median_by_xcd"] = [round(float(np.nanmedian(end[x::8])), 2) for x in range(8)]
+        out["last_end"] = round(float(np.nanmax(end)), 2)
+        print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,7 +70,7 @@ def verify_call(lib, **kw):
     (dict(o=None), gdn.GDN_EINVAL),
     (dict(qkv=ctypes.c_void_p(A + 4)), gdn.GDN_EINVAL),          # misaligned
     (dict(K=0), gdn.GDN_EINVAL),
-    (dict(K=33), gdn.GDN_EUNSUPPORTED),
+    (dict(K=65), gdn.GDN_EUNSUPPORTED),
     (dict(dk=48, dv=48), gdn.GDN_EUNSUPPORTED),
     (dict(dv=20), gdn.GDN_EUNSUPPORTED),
     (dict(Hk=2, Hv=3), gdn.GDN_EINVAL),
@@ -225,7 +225,7 @@ def replay_call(lib, **kw):
     (dict(S_out=p(6)), gdn.GDN_EINVAL),        # the checkpoint must survive
     (dict(hist=None), gdn.GDN_EINVAL),         # hist without win
     (dict(gs=1), gdn.GDN_EINVAL),
-    (dict(K=33), gdn.GDN_EUNSUPPORTED),
+    (dict(K=65), gdn.GDN_EUNSUPPORTED),
     (dict(S_out=p(1)), gdn.GDN_EINVAL),        # over qkv
     (dict(W=9), gdn.GDN_EUNSUPPORTED),
 ])
@@ -349,8 +349,9 @@ def step_call(lib, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(W=3), gdn.GDN_EUNSUPPORTED),                       # the fused step takes conv width 4
-    (dict(K=33), gdn.GDN_EUNSUPPORTED),
+    (dict(K=65), gdn.GDN_EUNSUPPORTED),
     (dict(Kp=0), gdn.GDN_EINVAL),
+    (dict(Kp=65), gdn.GDN_EINVAL),                           # the previous window is a verify window too
     (dict(pck=None), gdn.GDN_EINVAL),                        # the previous window needs its checkpoint
     (dict(pH=None), gdn.GDN_EINVAL),                         # ... and its capture when K_prev > 1
     (dict(acc=None), gdn.GDN_EINVAL),                        # first window without S_in / hist

@@ -154,6 +154,9 @@ VERIFY_CASES = [
     ("verify16", dict(T=12, Hk=2, Hv=4, dk=32, dv=32), {}),
     ("verify16", dict(T=20, Hk=2, Hv=6), {}),
     ("verify16", dict(T=32, Hk=2, Hv=4), {}),
+    ("verify16", dict(T=48, Hk=2, Hv=6), {}),                       # the longest windows (K <= 64)
+    ("verify16", dict(T=64, Hk=2, Hv=4, dk=64, dv=64), {}),
+    ("verify16", dict(T=64, Hk=1, Hv=2, dk=32, dv=32), dict(o_bf16=True)),
     ("verify16", dict(T=16, Hk=2, Hv=4, dk=64, dv=128), {}),
     ("verify16", dict(T=16, Hk=2, Hv=4, dk=128, dv=24), {}),
     ("verify16", dict(Hk=4, Hv=12), dict(weak=True)),

@@ -93,6 +93,17 @@ CASES = [
     ("verify16", dict(B=3, Hk=2, Hv=4, dk=64, dv=64), [2, 16, 0]),
     ("verify16", dict(B=2, Hk=2, Hv=4, dk=32, dv=32, T=9), [4, 9]),
     ("tiny", dict(B=2), [1, 4]),                                   # fp32 inputs
+    # three value heads per key head (the pipelined step kernel) at dk 64 and 32, dv != dk, a partial
+    # row block (dk 32: 32 rows per head and workgroup, dv 40), several chunks of the q|k conv
+    ("verify16", dict(B=2, Hk=2, Hv=6, dk=64, dv=64, T=16), [3, 16]),
+    ("verify16", dict(B=2, Hk=2, Hv=6, dk=32, dv=32, T=20), [20, 1]),
+    ("verify16", dict(B=2, Hk=2, Hv=6, dk=128, dv=64, T=13), [0, 6]),
+    ("verify16", dict(B=1, Hk=1, Hv=3, dk=32, dv=40, T=30), [12]),
+    ("verify16", dict(B=1, Hk=2, Hv=12, T=5), [2]),                # six value heads per key head
+    # the longest windows: K = 48 and 64 (both kernels: three and two value heads per key head)
+    ("verify16", dict(B=2, Hk=2, Hv=6, T=48), [48, 17]),
+    ("verify16", dict(B=1, Hk=2, Hv=6, dk=64, dv=64, T=64), [40]),
+    ("verify16", dict(B=2, Hk=2, Hv=4, T=64), [0, 64]),
     # the full sizes, in the launch configuration the bench times (three value heads per
     # 12-wave workgroup): verify16 (B=1, 48 value heads, d=128, K=16) and batched (B=32, K=8)
     ("verify16", dict(), [9]),
@@ -188,3 +199,74 @@ def test_fused_step_nullable_outputs():
                     S_in=d["S_in"], hist=d["hist"])
     torch.cuda.synchronize()
     assert torch.equal(S_out, full["S_out"]) and torch.equal(o, full["o"])
+
+
+@pytest.mark.parametrize("K1,K2,acc", [(8, 16, [5, 8]), (16, 8, [16, 9]), (16, 1, [0, 13]), (64, 16, [33, 64])])
+def test_fused_step_previous_window_of_another_length(K1, K2, acc):
+    """A window of K2 tokens after one of K1 != K2: the previous window's capture stride (K1 - 1 states)
+    and window rows (3 + K1) are read with K1, checked against gdn_rollback + the separate calls."""
+    wl1 = synth.small("verify16", B=2, Hk=2, Hv=6, T=K1)
+    wl2 = synth.small("verify16", B=2, Hk=2, Hv=6, T=K2)
+    say("verify_step K_prev=%d K=%d" % (K1, K2), "accept", acc)
+    inp1 = synth.make_inputs(wl1, seed=71)
+    inp2 = synth.make_inputs(wl2, seed=72)
+    d1 = {k: dev(v) for k, v in inp1.items()}
+    d2 = {k: dev(v) for k, v in inp2.items()}
+    d2["w"] = d1["w"]
+    accept = torch.tensor(acc, dtype=torch.int32, device="cuda")
+    A, A_ref = outputs(wl1), outputs(wl1)
+    fused(wl1, d1, A)
+    separate(wl1, d1, A_ref, d1["S_in"], d1["hist"])
+    torch.cuda.synchronize()
+    assert_same(A, A_ref, "first window", K1)
+    Bo, B_ref = outputs(wl2), outputs(wl2)
+    fused(wl2, d2, Bo, prev=(accept, A["S_ckpt"], A["H"], A["S_out"], A["win"]))
+    S_start = A_ref["S_out"].clone()
+    hist = d1["hist"].clone()
+    gdn.rollback(accept, K1, A_ref["S_ckpt"], A_ref["H"], S_start, hist, A_ref["win"])
+    separate(wl2, d2, B_ref, S_start, hist)
+    torch.cuda.synchronize()
+    assert_same(Bo, B_ref, "second window", K2)
+
+
+def test_accept_lengths_out_of_range_are_clamped():
+    """Accept lengths below 0 or above K act as 0 and K, bit for bit, in gdn_verify_step,
+    gdn_rollback and gdn_rollback_conv_step."""
+    wl = synth.small("verify16", B=4, Hk=2, Hv=6, T=8)
+    say("accept clamping")
+    inp1 = synth.make_inputs(wl, seed=81)
+    inp2 = synth.make_inputs(wl, seed=82)
+    d1 = {k: dev(v) for k, v in inp1.items()}
+    d2 = {k: dev(v) for k, v in inp2.items()}
+    d2["w"] = d1["w"]
+    wild = torch.tensor([-3, 99, -2147483647, 2147483647], dtype=torch.int32, device="cuda")
+    tame = torch.tensor([0, 8, 0, 8], dtype=torch.int32, device="cuda")
+    A = outputs(wl)
+    fused(wl, d1, A)
+    prev_w = (wild, A["S_ckpt"], A["H"], A["S_out"], A["win"])
+    prev_t = (tame, A["S_ckpt"], A["H"], A["S_out"], A["win"])
+    Bw, Bt = outputs(wl), outputs(wl)
+    fused(wl, d2, Bw, prev=prev_w)
+    fused(wl, d2, Bt, prev=prev_t)
+    torch.cuda.synchronize()
+    assert_same(Bw, Bt, "verify_step", wl.T)
+    # gdn_rollback
+    outs = []
+    for acc in (wild, tame):
+        S = A["S_out"].clone()
+        hist = d1["hist"].clone()
+        gdn.rollback(acc, wl.T, A["S_ckpt"], A["H"], S, hist, A["win"])
+        outs.append((S, hist))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # gdn_rollback_conv_step
+    outs = []
+    for acc in (wild, tame):
+        S = A["S_out"].clone()
+        hist = torch.empty_like(d1["hist"])
+        y, win = torch.empty_like(d2["x"]), torch.empty_like(A["win"])
+        gdn.rollback_conv_step(acc, wl.T, A["S_ckpt"], A["H"], S, A["win"], d2["x"], d1["w"], hist, y, win)
+        outs.append((S, hist, y, win))
+    torch.cuda.synchronize()
+    for a_, b_ in zip(*outs):
+        assert torch.equal(a_, b_)
