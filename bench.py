@@ -2,25 +2,29 @@
 """GDN verify tokens/s per layer (K=16) and achieved HBM bandwidth on one MI355X.
 
 One step is one pass of the whole hot path of one GDN layer over one verify
-window: gdn_conv_step (fused causal conv1d + SiLU, history write-back, window
-capture) -> gdn_verify (gated delta rule over K=16 tokens, every intermediate
-state written) -> gdn_rollback (restore conv and GDN state to a
-drawn accept length).  Workload: B=1, Hk=16 key heads, Hv=48 value heads,
-d=128, conv width 4 over C=10240 channels, bf16 inputs, fp32 state; seeded
-synthetic inputs (speculative_verify_gdn_amd.synth), accept length ~ U{0..16}.
+window, in one launch (gdn_verify_step): the rollback of the previous window
+(its accept length picks the start state and the conv history), the conv step
+(fused causal conv1d + SiLU, history write-back, window capture) and the gated
+delta rule over K=16 tokens with every intermediate state written.  Workload:
+B=1, Hk=16 key heads, Hv=48 value heads, d=128, conv width 4 over C=10240
+channels, bf16 inputs and outputs, fp32 state; seeded synthetic inputs
+(speculative_verify_gdn_amd.synth), accept lengths ~ U{0..16}.
 
 Inputs are resident in HBM before timing starts.  The step cycles over R
-independent buffer sets whose total size is at least twice the 256 MB
-Infinity Cache, so the state traffic really goes to HBM.  Each buffer set's
-step is captured once in a HIP graph and the timed region replays exactly
-K steps.
+buffer sets whose total size is at least twice the 256 MB Infinity Cache, so
+the state traffic really goes to HBM; set r continues from set r-1's window as
+in a serving loop.  The steps are captured in HIP graphs; after W warm-up
+steps and a clock-settle phase (untimed), each of --trials timed trials
+replays exactly K steps between device synchronisations, and the median trial
+is the figure (min and max beside it).
 
-Printed: one JSON line with the metric, the roofline of the dominant kernel
-(gdn_verify: algorithmic bytes per launch / its average duration, timed with
-HIP events on the launch stream around graph-replayed back-to-back launches of
-that kernel alone), and the CPU oracle timed on the host as a baseline.
+Printed: one JSON line with the metric, the roofline of the step's kernel
+(algorithmic bytes per launch / its median duration, timed with HIP events on
+the launch stream around graph-replayed back-to-back launches of that kernel
+alone; the measured device-copy rate beside the published peak), and the CPU
+oracle timed on the host as a baseline (one thread and all usable cores).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials 5]
 """
 from __future__ import annotations
 
@@ -36,12 +40,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "GDN verify tokens/s per layer (K=16) + achieved HBM GB/s vs peak"
+# the sources of the step's kernel (gdn_verify_step on bf16 slabs); the committed counter profile of
+# the kernel is used only while they hash to the value recorded with it
+STEP_SOURCES = ("gdn_step.hip", "gdn_verify_common.h", "gdn_device.h", "gdn_conv_math.h", "gdn_timeline.h")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+O_DTYPE = [None]               # torch dtype of o, set in main (bf16 unless --o-f32)
 MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
-def verify_bytes(wl, o_bytes=4) -> int:
+O_BYTES = 2                    # o in bf16 (fp32 is the opt-in: --o-f32)
+
+
+def verify_bytes(wl, o_bytes=None) -> int:
     """Algorithmic bytes of one gdn_verify launch: every input read once,
     every output written once.
 
@@ -49,14 +60,16 @@ def verify_bytes(wl, o_bytes=4) -> int:
                   + H (K-1)*Hv*dv*dk*4 + S_out Hv*dv*dk*4 + o K*Hv*dv*ob
     plus dt_bias and A_log (2*Hv*4) once.
     """
+    o_bytes = O_BYTES if o_bytes is None else o_bytes
     ie = 2 if wl.bf16 else 4
     st = wl.Hv * wl.dv * wl.dk * 4
     per_b = wl.T * wl.C * ie + 2 * wl.T * wl.Hv * ie + st + (wl.T - 1) * st + st + wl.T * wl.Hv * wl.dv * o_bytes
     return wl.B * per_b + 2 * wl.Hv * 4
 
 
-def verify_bytes_ragged(wl, lens, o_bytes=4) -> int:
+def verify_bytes_ragged(wl, lens, o_bytes=None) -> int:
     """verify_bytes for a ragged batch: sequence b reads and writes as a window of lens[b] tokens."""
+    o_bytes = O_BYTES if o_bytes is None else o_bytes
     ie = 2 if wl.bf16 else 4
     st = wl.Hv * wl.dv * wl.dk * 4
     tot = 2 * wl.Hv * 4
@@ -65,20 +78,22 @@ def verify_bytes_ragged(wl, lens, o_bytes=4) -> int:
     return tot
 
 
-def verify_tree_bytes(wl, o_bytes=4) -> int:
+def verify_tree_bytes(wl, o_bytes=None) -> int:
     """Algorithmic bytes of one gdn_verify_tree launch over N = wl.T nodes: verify_bytes with every node's
     state written (N planes, no separate final state) and the parent indices read."""
+    o_bytes = O_BYTES if o_bytes is None else o_bytes
     ie = 2 if wl.bf16 else 4
     st = wl.Hv * wl.dv * wl.dk * 4
     per_b = wl.T * wl.C * ie + 2 * wl.T * wl.Hv * ie + st + wl.T * st + wl.T * wl.Hv * wl.dv * o_bytes + 4 * wl.T
     return wl.B * per_b + 2 * wl.Hv * 4
 
 
-def step_bytes(wl, o_bytes=4) -> int:
+def step_bytes(wl, o_bytes=None) -> int:
     """Algorithmic bytes of one gdn_verify_step launch (rollback of the previous window + conv step +
     verify with capture): per sequence the raw tokens K*C*ie and the W-1 history rows, the gates, the
     start state read once and written once as the checkpoint, H (K-1 states), S_out, o and the conv
     window (W-1+K rows); the taps C*W*4, dt_bias and A_log once; the accept lengths."""
+    o_bytes = O_BYTES if o_bytes is None else o_bytes
     ie = 2 if wl.bf16 else 4
     st = wl.Hv * wl.dv * wl.dk * 4
     per_b = (wl.T * wl.C * ie + (wl.W - 1) * wl.C * ie + 2 * wl.T * wl.Hv * ie + 2 * st + (wl.T - 1) * st + st
@@ -128,9 +143,34 @@ def read_traffic(kernel: str, workload: str, sha: str):
         return None
 
 
+def host_info():
+    """The host's logical CPU count, the CPUs this process may run on, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
 def cpu_baseline(wl, budget_s: float):
-    """The oracle (single-threaded C: float conv, double GDN, rollback) on the
-    same workload, full steps until the time budget is spent."""
+    """The oracle (C: float conv, double GDN with capture, rollback) on the same workload, on the
+    host: one thread, then one thread per group of key heads (up to the usable CPUs, at most one
+    per key head), each calling the unchanged oracle functions on its own heads and their conv
+    channels (key heads and their value heads are independent; the ctypes calls release the
+    GIL).  Each leg: one warm-up step, then 5 runs of about budget/10 seconds each; the median
+    run is reported with the minimum and maximum."""
+    import concurrent.futures
+    import statistics
+
     import numpy as np
 
     import oracle
@@ -144,19 +184,57 @@ def cpu_baseline(wl, budget_s: float):
     br, al, dt, alog, S_in = f("beta_raw"), f("alpha"), f("dt_bias"), f("A_log"), f("S_in")
     acc = inp["accept"].numpy()
     o = oracle.default()
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        y, hist_out, win = o.conv_step_f32(x, w, hist, round_bf16=wl.bf16)
-        S_out, H, _ = o.gdn_recurrent_f64(y.astype(np.float64), br, al, dt, alog, S_in, wl.Hk)
-        o.rollback(acc, wl.T, S_in, H, S_out, win=win, hist=hist_out)
-        steps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": steps * wl.B * wl.T / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full steps of the %s workload (float conv + double GDN with capture + rollback), "
-                      "one thread, %.1f s" % (steps, wl.name, el)}
+    grp = wl.Hv // wl.Hk
+
+    def part(k0, k1):
+        # the sub-problem of key heads k0..k1-1: their q and k channels, their value heads' v channels
+        h0, h1 = k0 * grp, k1 * grp
+        qk = wl.Hk * wl.dk
+        idx = np.concatenate([np.arange(k0 * wl.dk, k1 * wl.dk), qk + np.arange(k0 * wl.dk, k1 * wl.dk),
+                              2 * qk + np.arange(h0 * wl.dv, h1 * wl.dv)])
+        c = np.ascontiguousarray
+        return dict(x=c(x[..., idx]), w=c(w[idx]), hist=c(hist[..., idx]), br=c(br[..., h0:h1]),
+                    al=c(al[..., h0:h1]), dt=c(dt[h0:h1]), alog=c(alog[h0:h1]), S_in=c(S_in[:, h0:h1]),
+                    Hk=k1 - k0)
+
+    def step(pt):
+        y, hist_out, win = o.conv_step_f32(pt["x"], pt["w"], pt["hist"], round_bf16=wl.bf16)
+        S_out, H, _ = o.gdn_recurrent_f64(y.astype(np.float64), pt["br"], pt["al"], pt["dt"], pt["alog"],
+                                          pt["S_in"], pt["Hk"])
+        o.rollback(acc, wl.T, pt["S_in"], H, S_out, win=win, hist=hist_out)
+        return S_out
+
+    def leg(parts):
+        with concurrent.futures.ThreadPoolExecutor(len(parts)) as ex:
+            def one():
+                list(ex.map(step, parts))
+            t0 = time.perf_counter()
+            one()                                    # warm-up
+            t_step = time.perf_counter() - t0
+            n = max(1, math.ceil(budget_s / 10 / max(t_step, 1e-6)))
+            runs = []
+            for _ in range(5):
+                t0 = time.perf_counter()
+                for _ in range(n):
+                    one()
+                runs.append(n * wl.B * wl.T / (time.perf_counter() - t0))
+        return {"value": round(statistics.median(runs), 1), "min": round(min(runs), 1), "max": round(max(runs), 1),
+                "steps_per_run": n, "threads": len(parts)}
+
+    info = host_info()
+    whole = part(0, wl.Hk)
+    single = leg([whole])
+    nt = max(1, min(info["usable_cpus"] or 1, wl.Hk))
+    bounds = [round(i * wl.Hk / nt) for i in range(nt + 1)]
+    parts = [part(bounds[i], bounds[i + 1]) for i in range(nt)]
+    # the key-head groups together give the whole problem's states, bit for bit
+    assert np.array_equal(np.concatenate([step(pt) for pt in parts], axis=1), step(whole))
+    multi = leg(parts)
+    return {"value": multi["value"], "unit": "tokens/s", "cores": multi["threads"], "kind": "oracle",
+            "sample": "the %s workload (float conv + double GDN with capture + rollback): one warm-up step, then "
+                      "5 runs of %d full steps on %d threads (one key-head group each); median run" %
+                      (wl.name, multi["steps_per_run"], multi["threads"]),
+            "min": multi["min"], "max": multi["max"], "single_thread": single, **info}
 
 
 def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "prefill")):
@@ -192,7 +270,7 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
             d["qkv"] = synth.make_qkv(wl, seed=r).to(dev)
             d["S_out"] = torch.empty_like(d["S_in"])
             d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev) if wl.T > 1 else None
-            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev, dtype=O_DTYPE[0])
             sets.append(d)
 
         def ver(d, wl=wl):
@@ -217,7 +295,7 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
             d["qkv"] = synth.make_qkv(wl, seed=r).to(dev)
             d["S_out"] = torch.empty_like(d["S_in"])
             d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev)
-            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev, dtype=O_DTYPE[0])
             d["lens"] = lens.to(dev)
             sets.append(d)
 
@@ -243,7 +321,7 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
             d["S_ckpt"] = torch.empty_like(d["S_in"])
             d["S_out"] = torch.empty_like(d["S_in"])
             d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev) if wl.T > 1 else None
-            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev, dtype=O_DTYPE[0])
             d["y"] = torch.empty_like(d["x"])
             d["win"] = torch.empty(wl.B, wl.W - 1 + wl.T, wl.C, device=dev, dtype=d["x"].dtype)
             d["win_prev"] = torch.empty_like(d["win"])
@@ -288,7 +366,7 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
             d["qkv"] = synth.make_qkv(wl, seed=r).to(dev)
             d["S_out"] = torch.empty_like(d["S_in"])
             d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev)
-            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+            d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev, dtype=O_DTYPE[0])
             d["acc"] = acc.to(dev)
             sets.append(d)
 
@@ -384,6 +462,33 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
     return res
 
 
+def copy_peak(torch, dev, mib=512, trials=5):
+    """A plain device copy of mib MiB (torch's copy kernel), replayed from a HIP graph: bytes read plus
+    bytes written per second, median of the trials; the practical HBM ceiling next to the published
+    peak."""
+    import statistics
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(4):
+            dst.copy_(src)
+    g.replay()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        runs.append(2 * n * 4 * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del src, dst
+    return {"GBs": round(statistics.median(runs), 1), "min": round(min(runs), 1), "max": round(max(runs), 1),
+            "bytes_per_copy": 2 * n * 4, "copy": "%d MiB device to device (torch copy kernel), read + write" % mib}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -397,6 +502,12 @@ def main():
     ap.add_argument("--three-kernel", action="store_true",
                     help="step as conv_step -> verify -> rollback (three launches) instead of "
                          "rollback_conv_step -> verify")
+    ap.add_argument("--trials", type=int, default=5,
+                    help="timed trials of K steps each; the median trial is reported, with min and max")
+    ap.add_argument("--settle-ms", type=float, default=50.0,
+                    help="after the W warm-up steps, replay the step for at least this long (untimed) so the "
+                         "GPU's clocks have settled before the timed trials")
+    ap.add_argument("--o-f32", action="store_true", help="fp32 outputs o (default bf16)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-workloads", action="store_true",
@@ -416,10 +527,15 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import statistics
+
     import torch
 
     from speculative_verify_gdn_amd import gdn, synth
 
+    global O_BYTES
+    O_DTYPE[0] = torch.float32 if args.o_f32 else torch.bfloat16
+    O_BYTES = 4 if args.o_f32 else 2
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     if args.copy_probe:
@@ -453,7 +569,7 @@ def main():
         d["win_prev"] = torch.empty_like(d["win"])   # the previous step's window (fused step)
         d["S_out"] = torch.empty_like(d["S_in"])
         d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev) if wl.T > 1 else None
-        d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+        d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev, dtype=O_DTYPE[0])
         d["S_ckpt"] = torch.empty_like(d["S_in"])     # the fused step's checkpoint (start state)
         return d
 
@@ -543,23 +659,41 @@ def main():
             g.replay()
         torch.cuda.synchronize()
 
+    # ---------------------------------------------------------------- clock settle (untimed)
+    settle_t0 = time.perf_counter()
+    settle_steps = 0
+    while (time.perf_counter() - settle_t0) * 1e3 < args.settle_ms:
+        if graphs is not None:
+            for g in graphs:
+                g.replay()
+            settle_steps += per_graph * len(graphs)
+        else:
+            for d in sets:
+                step(d)
+            settle_steps += R
+        torch.cuda.synchronize()
+
     # ---------------------------------------------------------------- timed steps
+    # trials of exactly K steps each, bracketed by device synchronisations; the median trial is
+    # the figure
     K = args.steps
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    trial_ms = []
     w0 = time.perf_counter()
-    ev0.record()
-    if graphs is not None:
-        for s in range(K // per_graph):
-            graphs[s % len(graphs)].replay()
-    else:
-        for s in range(K):
-            step(sets[s % R])
-    ev1.record()
-    torch.cuda.synchronize()
+    for _ in range(max(1, args.trials)):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record()
+        if graphs is not None:
+            for s_ in range(K // per_graph):
+                graphs[s_ % len(graphs)].replay()
+        else:
+            for s_ in range(K):
+                step(sets[s_ % R])
+        ev1.record()
+        torch.cuda.synchronize()
+        trial_ms.append(ev0.elapsed_time(ev1) / K)
     wall_ms = (time.perf_counter() - w0) * 1e3
-    ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / K
+    ms_per_step = statistics.median(trial_ms)
     tokens = wl.B * wl.T
     value = tokens / (ms_per_step * 1e-3)
 
@@ -576,13 +710,16 @@ def main():
         g.replay()
         torch.cuda.synchronize()
         reps = max(1, min(K, 400) // R)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / (reps * R)
+        runs = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1) * 1e3 / (reps * R))
+        return statistics.median(runs)
 
     if args.eager:
         def kernel_us(fn):  # noqa: F811  (events around each eager launch)
@@ -648,7 +785,8 @@ def main():
 
     vb = verify_bytes(wl)
     sb = step_bytes(wl)
-    sha = source_sha("gdn_verify.hip", "gdn_device.h", "gdn_conv_math.h")
+    sha = source_sha(*STEP_SOURCES)
+    cpk = copy_peak(torch, dev)
     if mode == "fused":
         # the dominant (and only) kernel of the step: gdn_verify_step
         dom, dom_bytes, dom_us = "gdn_verify_step", sb, t_fused
@@ -666,6 +804,8 @@ def main():
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 6),
+        "ms_per_step_trials": {"median": round(ms_per_step, 6), "min": round(min(trial_ms), 6),
+                               "max": round(max(trial_ms), 6), "trials": len(trial_ms)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -674,6 +814,7 @@ def main():
         "config": {
             "workload": wl.name, "B": wl.B, "K": wl.T, "Hk": wl.Hk, "Hv": wl.Hv, "dk": wl.dk, "dv": wl.dv,
             "C": wl.C, "conv_width": wl.W, "io_dtype": "bf16" if wl.bf16 else "f32", "state_dtype": "f32",
+            "o_dtype": "f32" if args.o_f32 else "bf16",
             "step": {"three": "conv_step + verify(capture) + rollback",
                      "two": "rollback_conv_step (rollback of the previous window + conv_step, one launch) + "
                             "verify(capture)",
@@ -689,6 +830,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "device_copy_GBs": cpk["GBs"],
+            "frac_of_device_copy": round(achieved / cpk["GBs"], 4),
         },
         "detail": {
             "kernel": dom,
@@ -717,6 +860,9 @@ def main():
             # tokens per second per layer counting the conv step and the verify (rollback apart)
             "conv_verify_tokens_per_s": round(tokens / ((t_conv + t_ver) * 1e-6), 1),
             "wall_ms_timed": round(wall_ms, 3),
+            "settle": {"steps": settle_steps, "min_ms": args.settle_ms},
+            "device_copy": cpk,
+            "o_dtype": "f32" if args.o_f32 else "bf16",
             "source_sha": sha,
             "accept_lengths": accepts,
         },

@@ -22,6 +22,10 @@ from speculative_verify_gdn_amd import gdn, synth
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+# regression guard, beside the bar: the observed worst state error is below 1e-6 of the state's
+# Frobenius norm (fp32 arithmetic on the oracle's own bf16 inputs; largest seen 7e-7, in the
+# prefill), so a 100x regression fails here long before it reaches the 2e-3 bar
+GUARD = 1e-4
 
 
 def say(*a):
@@ -67,8 +71,11 @@ def check_states(gpu, ref, what):
     err = np.abs(gpu - ref).max(axis=(-1, -2))
     fro = np.linalg.norm(ref, axis=(-1, -2))
     bad = err > TOL * fro
-    assert not np.any(bad), "%s: worst err/fro = %.3g" % (what, float(np.max(err / np.maximum(fro, 1e-30))))
-    return float(np.max(err / np.maximum(fro, 1e-30)))
+    worst = float(np.max(err / np.maximum(fro, 1e-30)))
+    print("[parity] %s worst err/fro %.3g" % (what, worst), flush=True)
+    assert not np.any(bad), "%s: worst err/fro = %.3g" % (what, worst)
+    assert worst <= GUARD, "%s: worst err/fro %.3g above the regression guard" % (what, worst)
+    return worst
 
 
 def check_outputs(o_gpu, o_ref, states_ref, bf16_out):

@@ -23,6 +23,10 @@ from speculative_verify_gdn_amd import gdn, synth
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+# regression guard, beside the bar: the observed worst state error is below 1e-6 of the state's
+# Frobenius norm (fp32 arithmetic on the oracle's own bf16 inputs; largest seen 7e-7, in the
+# prefill), so a 100x regression fails here long before it reaches the 2e-3 bar
+GUARD = 1e-4
 
 
 def say(*a):
@@ -176,7 +180,10 @@ def test_fused_step_chain_against_oracle(over, acc1):
     def close(gpu, ref, what):
         err = np.abs(gpu.double().cpu().numpy() - ref).max(axis=(-1, -2))
         fro = np.linalg.norm(ref, axis=(-1, -2))
-        assert np.all(err <= TOL * fro), "%s: worst %.3g" % (what, float(np.max(err / fro)))
+        worst = float(np.max(err / fro))
+        print("[parity] %s worst err/fro %.3g" % (what, worst), flush=True)
+        assert np.all(err <= TOL * fro), "%s: worst %.3g" % (what, worst)
+        assert worst <= GUARD, "%s: worst err/fro %.3g above the regression guard" % (what, worst)
     close(Bo["S_ckpt"], S_keep, "S_ckpt")
     close(Bo["S_out"], S2, "S_out")
     close(Bo["H"], H2, "H")
