@@ -468,17 +468,5 @@ hipError_t launch_step(const VerifyArgs& a, bool in_bf16, bool o_bf16, hipStream
 
 #ifdef GDN_TIMELINE
 // the marks of the last launches: [workgroup][wave][mark] 100 MHz counter values (0: not reached)
-extern "C" int gdn_timeline_read(void* dst, size_t bytes)
-{
-    if (bytes > sizeof(gdn::g_timeline)) bytes = sizeof(gdn::g_timeline);
-    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(gdn::g_timeline), bytes, 0, hipMemcpyDeviceToHost);
-}
-
-extern "C" int gdn_timeline_clear(void)
-{
-    void* p = nullptr;
-    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(gdn::g_timeline));
-    if (e == hipSuccess) e = hipMemset(p, 0, sizeof(gdn::g_timeline));
-    return (int)e;
-}
+GDN_TIMELINE_READER(gdn_timeline)
 #endif

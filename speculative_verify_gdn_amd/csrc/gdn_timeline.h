@@ -13,8 +13,23 @@
 #ifdef GDN_TIMELINE
 namespace gdn {
 constexpr int kTlGroups = 2048, kTlWaves = 16, kTlMarks = 16;
-__device__ unsigned long long g_timeline[kTlGroups * kTlWaves * kTlMarks];
+// one array per translation unit (each has its own reader, GDN_TIMELINE_READER)
+static __device__ unsigned long long g_timeline[kTlGroups * kTlWaves * kTlMarks];
 }  // namespace gdn
+// the host readers of this translation unit's marks: NAME_read(dst, bytes), NAME_clear()
+#define GDN_TIMELINE_READER(NAME)                                                                        \
+    extern "C" int NAME##_read(void* dst, size_t bytes)                                               \
+    {                                                                                                  \
+        if (bytes > sizeof(gdn::g_timeline)) bytes = sizeof(gdn::g_timeline);                          \
+        return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(gdn::g_timeline), bytes, 0, hipMemcpyDeviceToHost); \
+    }                                                                                                  \
+    extern "C" int NAME##_clear(void)                                                                 \
+    {                                                                                                  \
+        void* p = nullptr;                                                                             \
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(gdn::g_timeline));                           \
+        if (e == hipSuccess) e = hipMemset(p, 0, sizeof(gdn::g_timeline));                             \
+        return (int)e;                                                                                 \
+    }
 #define GDN_TL(n)                                                                                      \
     do {                                                                                               \
         const unsigned wg_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);          \
