@@ -44,12 +44,25 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int 
         return;
     }
 
-    // conv rows: (W-1)*C elements, copied as 16-bit units (bf16) or 32-bit units (f32)
+    // conv rows: (W-1)*C consecutive elements, 8 per thread
     if (a.hist == nullptr) return;
     const long long n = (long long)(a.W - 1) * a.C;
     const long long e = ((long long)(blockIdx.x - state_blocks) * kThreads + threadIdx.x) * 8;
     const size_t src0 = ((size_t)b * (a.W - 1 + Kb) + acc) * a.C;
     const size_t dst0 = (size_t)b * (a.W - 1) * a.C;
+    if ((a.C & 7) == 0) {
+        // every row starts 16-byte aligned (win and hist are): 16-byte copies, one per 8 bf16 or two
+        // per 8 floats; n is a multiple of 8, so e < n leaves all 8 elements in range
+        if (e < n) {
+            const uint4* s = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.win) +
+                                                            (src0 + e) * a.elem_bytes);
+            uint4* d = reinterpret_cast<uint4*>(reinterpret_cast<char*>(a.hist) + (dst0 + e) * a.elem_bytes);
+            d[0] = s[0];
+            if (a.elem_bytes == 4) d[1] = s[1];
+        }
+        return;
+    }
+    // other channel counts: 16-bit units (bf16) or 32-bit units (f32)
     if (a.elem_bytes == 2) {
         const uint16_t* s = reinterpret_cast<const uint16_t*>(a.win) + src0;
         uint16_t* d = reinterpret_cast<uint16_t*>(a.hist) + dst0;

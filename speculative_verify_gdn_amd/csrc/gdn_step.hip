@@ -63,7 +63,7 @@ struct StepSmem {
     uint16_t k[KP][QW];                          // ... and of its k channels
     uint16_t win[KP + 3][2 * DK];                // the window rows of the key head's q|k channels (raw bits)
     float4 tok[kGroups][KP];                     // per head and token: beta, gamma = e^g, 1/|k|, 1/|q|
-    float V[kGroups][KP][RPG];                   // v of the head's rows, per token
+    float V[2][kGroups][KP][RPG];                // v of the head's rows, per token (two row blocks)
 };
 
 // bf16 dot2 of a packed pair with itself, accumulated onto acc
@@ -119,7 +119,10 @@ __device__ __forceinline__ float item_sumsq(uint32_t w, int lane)
 // store is one unconditional instruction, so the compiler's wait for a chunk's window rows
 // (loaded before the previous chunk's stores) counts those stores exactly instead of draining
 // them.
-template <int DK, int KMAX, bool O_BF16, bool CAPTURE, bool LIVE>
+// RB: row blocks per workgroup (at large batches a workgroup takes RB consecutive row blocks of
+// one key head: the q|k conv, the gates and the staging are done once, and the next block's start
+// state and v rows load while the current block streams; RB > 1 needs CAPTURE and LIVE)
+template <int DK, int KMAX, bool O_BF16, bool CAPTURE, bool LIVE, int RB>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
 {
     constexpr int LPR = DK / 4;                  // lanes per state row (one float4 each)
@@ -153,7 +156,9 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     const int j = lane % LPR, c = 4 * j;
     const int rloc = wave * RPW + lane / LPR;
     const int h = blockIdx.y * kGroups + g;
-    const int i = blockIdx.x * RPG + rloc;
+    static_assert(RB == 1 || (CAPTURE && LIVE), "several row blocks per workgroup need capture and live rows");
+    const int blk0 = blockIdx.x * RB;            // the workgroup's first row block
+    const int i = blk0 * RPG + rloc;             // this lane's row in the first block
     const int K = a.K, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
     const bool live = LIVE || i < dv;
     const int ic = live ? i : dv - 1;
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     constexpr int NPR = RPG / 2;                 // channel pairs per head and workgroup
     constexpr int NVP = (KMAX * NPR + 63) / 64;  // (token, pair) items per lane
     const int vp = lane % NPR;
-    const int vi0 = blockIdx.x * RPG + 2 * vp;   // the pair's first row
+    const int vi0 = blk0 * RPG + 2 * vp;         // the pair's first row (first block)
     const bool vlive = vi0 < dv;                 // dv is even: both rows or neither
     const size_t vch = 2 * (size_t)Hk * DK + (size_t)hr * dv + (vlive ? vi0 : 0);
     float4 vt0 = make_float4(0.f, 0.f, 0.f, 0.f), vt1 = vt0;
@@ -274,10 +279,14 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     uint16_t* Wb = a.win ? reinterpret_cast<uint16_t*>(a.win) + (size_t)b * (kCW - 1 + K) * C : nullptr;
     uint16_t* Yb = a.y ? reinterpret_cast<uint16_t*>(a.y) + (size_t)b * K * C : nullptr;
 
-    // ---- v conv of the head's rows, every token; their window rows and conv outputs
-    if (v_wave) {
+    // ---- v conv of the head's rows (row block r: channel pair vch + r RPG), every token; their
+    // window rows and conv outputs
+    auto vconv = [&](int r) __attribute__((always_inline)) {
+        if (!v_wave) return;
         const float ta[kCW] = {vt0.x, vt0.y, vt0.z, vt0.w};
         const float tb[kCW] = {vt1.x, vt1.y, vt1.z, vt1.w};
+        const bool vl = vlive && vi0 + r * RPG < dv;
+        const size_t vc = vch + (size_t)r * RPG;
 #pragma unroll
         for (int n = 0; n < NVP; ++n) {
             const int t = (lane + 64 * n) / NPR;
@@ -290,21 +299,22 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
                 }
                 const uint32_t y0 = conv_silu_bf16(conv_pre<kCW>(ta, c0));
                 const uint32_t y1 = conv_silu_bf16(conv_pre<kCW>(tb, c1));
-                *reinterpret_cast<float2*>(&sm.V[rg][t][2 * vp]) = make_float2(bf16_to_f32(y0), bf16_to_f32(y1));
-                if (vlive) {
-                    if (Yb) *reinterpret_cast<uint32_t*>(Yb + (size_t)t * C + vch) = y0 | (y1 << 16);
+                *reinterpret_cast<float2*>(&sm.V[r & 1][rg][t][2 * vp]) = make_float2(bf16_to_f32(y0), bf16_to_f32(y1));
+                if (vl) {
+                    if (Yb) *reinterpret_cast<uint32_t*>(Yb + (size_t)t * C + vc) = y0 | (y1 << 16);
                     if (Wb) {
-                        *reinterpret_cast<uint32_t*>(Wb + (size_t)(t + kCW - 1) * C + vch) = vrow[n][kCW - 1];
+                        *reinterpret_cast<uint32_t*>(Wb + (size_t)(t + kCW - 1) * C + vc) = vrow[n][kCW - 1];
                         if (t == 0) {
 #pragma unroll
                             for (int m = 0; m < kCW - 1; ++m)
-                                *reinterpret_cast<uint32_t*>(Wb + (size_t)m * C + vch) = vrow[n][m];
+                                *reinterpret_cast<uint32_t*>(Wb + (size_t)m * C + vc) = vrow[n][m];
                         }
                     }
                 }
             }
         }
-    }
+    };
+    vconv(0);
 
     GDN_TL(7);
     // ---- the q|k conv of one chunk: this lane's item, its norm, LDS, window rows and outputs
@@ -356,81 +366,145 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
         if (qk_writer && Wb) *reinterpret_cast<uint4*>(Wb + (size_t)r * C + piece_chan(pc)) = hpc;
     }
     conv_chunk(0);
+    // stores through buffer resources whose range is empty when the output is not wanted (or, for
+    // o, past the window): one unconditional instruction each, so the compiler counts them
+    // exactly when it waits for the next row block's loads
+    constexpr int kNt = 2;                       // cache policy: non-temporal
+    const __amdgpu_buffer_rsrc_t rck = __builtin_amdgcn_make_buffer_rsrc(
+        a.S_ckpt ? a.S_ckpt + hb : nullptr, 0, a.S_ckpt ? (int)(SD * 4) : 0, 0x00020000);
+    constexpr int OE = O_BF16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        a.o ? reinterpret_cast<char*>(a.o) + (size_t)b * K * Hv * dv * OE : nullptr, 0,
+        a.o ? K * Hv * dv * OE : 0, 0x00020000);
     // the checkpoint: this window's start state
-    if (a.S_ckpt && live) store_f4<true>(a.S_ckpt + hb + (size_t)i * DK + c, S0);
+    auto store_ckpt = [&](int ir, f32x4_t v) __attribute__((always_inline)) {
+        typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), rck,
+                                               live ? ((ir * DK + c) * 4) : 0x7ffffff0, 0, kNt);
+    };
+    store_ckpt(i, S0);
     GDN_TL(1);
     __syncthreads();
     GDN_TL(2);
 
-    // ---- the token recurrence, chunk by chunk, state in registers; per token, with the row
-    // sums over the row's lanes (DPP):
+    // ---- per row block: the token recurrence, chunk by chunk, state in registers; per token, with
+    // the row sums over the row's lanes (DPP):
     //   p = S k^_t,  u = beta_t (v_t - gamma_t p),  S = gamma_t S + u k^_t,  o_t = S q^_t
     f32x4_t S = live ? S0 : f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float* Hrow = CAPTURE ? a.H + ((size_t)b * (K - 1) * Hv + h) * SD + (size_t)i * DK + c : nullptr;
-    float* Srow = a.S_out + hb + (size_t)i * DK + c;
     const size_t Hstep = (size_t)Hv * SD;
     constexpr int NO = (KMAX + LPR - 1) / LPR;   // outputs held per lane: lane j keeps o_{j + m LPR}
-    float ot[NO];
 #pragma unroll
-    for (int m = 0; m < NO; ++m) ot[m] = 0.f;
+    for (int r = 0; r < RB; ++r) {
+        const int ir = i + r * RPG;              // this lane's row in block r
+        float* Hrow = CAPTURE ? a.H + ((size_t)b * (K - 1) * Hv + h) * SD + (size_t)ir * DK + c : nullptr;
+        float* Srow = a.S_out + hb + (size_t)ir * DK + c;
+        // the next block's start state, taps and v rows, before this block's stores
+        f32x4_t Sn = S;
+        if (r + 1 < RB) {
+            Sn = load_f4(Sh + (size_t)(ir + RPG) * DK + c);
+            if (v_wave) {
+                const size_t vc = vch + (size_t)(r + 1) * RPG;
+                vt0 = *reinterpret_cast<const float4*>(a.w + vc * kCW);
+                vt1 = *reinterpret_cast<const float4*>(a.w + (vc + 1) * kCW);
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
+                for (int n = 0; n < NVP; ++n) {
+                    const int t = (lane + 64 * n) / NPR;
+                    const int tl = t < K ? t : K - 1;
 #pragma unroll
-        for (int tt0 = 0; tt0 < (cc == 0 ? T0 : TC); ++tt0) {
-            const int t = chunk_start(cc) + tt0;
-            if (t < KMAX && t < K) {
-                const float4 tk = sm.tok[g][t];          // beta, gamma, 1/|k|, 1/|q|
-                const float4 kx = lds4<true>(&sm.k[t][c]);
-                const float v = sm.V[g][t][rloc];
-                const float sk = group_sum<LPR>(S[0] * kx.x + S[1] * kx.y + S[2] * kx.z + S[3] * kx.w) * tk.z;
-                const float cu = tk.x * (v - tk.y * sk) * tk.z;   // u / |k_t|
-                S[0] = __builtin_fmaf(cu, kx.x, tk.y * S[0]);
-                S[1] = __builtin_fmaf(cu, kx.y, tk.y * S[1]);
-                S[2] = __builtin_fmaf(cu, kx.z, tk.y * S[2]);
-                S[3] = __builtin_fmaf(cu, kx.w, tk.y * S[3]);
-                if constexpr (CAPTURE) {
-                    float* dst = t < K - 1 ? Hrow + (size_t)t * Hstep : Srow;
-                    if (live) store_f4<true>(dst, S);
-                } else {
-                    if (live && t == K - 1) store_f4<true>(Srow, S);
-                }
-                if (t == 0) GDN_TL(3);
-                if (a.o) {
-                    const float4 qx = lds4<true>(&sm.q[t][c]);
-                    const float o = group_sum<LPR>(S[0] * qx.x + S[1] * qx.y + S[2] * qx.z + S[3] * qx.w) * tk.w;
-                    if (j == t % LPR) ot[t / LPR] = o;
+                    for (int m = 0; m < kCW; ++m)
+                        vrow[n][m] = *reinterpret_cast<const uint32_t*>(wrow(tl + m) + vc);
                 }
             }
         }
-        if (cc + 1 < NC) {
-            conv_chunk(cc + 1);
-            __syncthreads();
+        float ot[NO];
+#pragma unroll
+        for (int m = 0; m < NO; ++m) ot[m] = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+#pragma unroll
+            for (int tt0 = 0; tt0 < (cc == 0 ? T0 : TC); ++tt0) {
+                const int t = chunk_start(cc) + tt0;
+                if (t < KMAX && t < K) {
+                    const float4 tk = sm.tok[g][t];          // beta, gamma, 1/|k|, 1/|q|
+                    const float4 kx = lds4<true>(&sm.k[t][c]);
+                    const float v = sm.V[r & 1][g][t][rloc];
+                    const float sk = group_sum<LPR>(S[0] * kx.x + S[1] * kx.y + S[2] * kx.z + S[3] * kx.w) * tk.z;
+                    const float cu = tk.x * (v - tk.y * sk) * tk.z;   // u / |k_t|
+                    S[0] = __builtin_fmaf(cu, kx.x, tk.y * S[0]);
+                    S[1] = __builtin_fmaf(cu, kx.y, tk.y * S[1]);
+                    S[2] = __builtin_fmaf(cu, kx.z, tk.y * S[2]);
+                    S[3] = __builtin_fmaf(cu, kx.w, tk.y * S[3]);
+                    if constexpr (CAPTURE) {
+                        float* dst = t < K - 1 ? Hrow + (size_t)t * Hstep : Srow;
+                        if (live) store_f4<true>(dst, S);
+                    } else {
+                        if (live && t == K - 1) store_f4<true>(Srow, S);
+                    }
+                    if (r == 0 && t == 0) GDN_TL(3);
+                    if (a.o) {
+                        const float4 qx = lds4<true>(&sm.q[t][c]);
+                        const float o = group_sum<LPR>(S[0] * qx.x + S[1] * qx.y + S[2] * qx.z + S[3] * qx.w) * tk.w;
+                        if (j == t % LPR) ot[t / LPR] = o;
+                    }
+                }
+            }
+            if (r == 0 && cc + 1 < NC) {
+                conv_chunk(cc + 1);
+                __syncthreads();
+            }
         }
-    }
-    if (a.o && live) {
 #pragma unroll
         for (int m = 0; m < NO; ++m) {
             const int t = m * LPR + j;
-            if (t < K) store1<O_BF16>(a.o, (((size_t)b * K + t) * Hv + h) * dv + i, ot[m]);
+            const int off = live && t < K ? ((t * Hv + h) * dv + ir) * OE : 0x7ffffff0;
+            if constexpr (O_BF16)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(ot[m]), ro, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ot[m]), ro, off, 0, 0);
+        }
+        if (r + 1 < RB) {
+            // the next block: its checkpoint, then its v conv (v waves), then one barrier (V of the
+            // next block is written into the other buffer)
+            S = Sn;
+            store_ckpt(ir + RPG, S);
+            vconv(r + 1);
+            __syncthreads();
         }
     }
     GDN_TL(4);
 }
 
+template <int DK, int KMAX, bool O_BF16, bool CAPTURE, bool LIVE>
+hipError_t launch_rb(const VerifyArgs& a, int rb, hipStream_t s)
+{
+    constexpr int RPG = kWaves * (64 / (DK / 4));
+    const dim3 block(kStepThreads);
+    if constexpr (CAPTURE && LIVE && KMAX <= 16) {
+        if (rb == 4) {
+            const dim3 grid((a.dv + 4 * RPG - 1) / (4 * RPG), a.Hv / kGroups, a.B);
+            step_kernel<DK, KMAX, O_BF16, CAPTURE, LIVE, 4><<<grid, block, 0, s>>>(a);
+            return hipGetLastError();
+        }
+    }
+    const dim3 grid((a.dv + RPG - 1) / RPG, a.Hv / kGroups, a.B);
+    step_kernel<DK, KMAX, O_BF16, CAPTURE, LIVE, 1><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 template <int DK, bool O_BF16, bool CAPTURE, bool LIVE>
 hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
 {
+    // four row blocks per workgroup once the launch has at least eight workgroups per CU that way
     constexpr int RPG = kWaves * (64 / (DK / 4));
-    const dim3 grid((a.dv + RPG - 1) / RPG, a.Hv / kGroups, a.B);
-    const dim3 block(kStepThreads);
-    if (a.K <= 1) step_kernel<DK, 1, O_BF16, CAPTURE, LIVE><<<grid, block, 0, s>>>(a);
-    else if (a.K <= 2) step_kernel<DK, 2, O_BF16, CAPTURE, LIVE><<<grid, block, 0, s>>>(a);
-    else if (a.K <= 4) step_kernel<DK, 4, O_BF16, CAPTURE, LIVE><<<grid, block, 0, s>>>(a);
-    else if (a.K <= 8) step_kernel<DK, 8, O_BF16, CAPTURE, LIVE><<<grid, block, 0, s>>>(a);
-    else if (a.K <= 16) step_kernel<DK, 16, O_BF16, CAPTURE, LIVE><<<grid, block, 0, s>>>(a);
-    else if (a.K <= 32) step_kernel<DK, 32, O_BF16, CAPTURE, LIVE><<<grid, block, 0, s>>>(a);
-    else step_kernel<DK, 64, O_BF16, CAPTURE, LIVE><<<grid, block, 0, s>>>(a);
-    return hipGetLastError();
+    const long long wg4 = (long long)a.B * (a.Hv / kGroups) * (a.dv / (4 * RPG));
+    const int rb = (CAPTURE && LIVE && a.K <= 16 && a.dv % (4 * RPG) == 0 && wg4 >= 8 * 256) ? 4 : 1;
+    if (a.K <= 1) return launch_rb<DK, 1, O_BF16, CAPTURE, LIVE>(a, rb, s);
+    if (a.K <= 2) return launch_rb<DK, 2, O_BF16, CAPTURE, LIVE>(a, rb, s);
+    if (a.K <= 4) return launch_rb<DK, 4, O_BF16, CAPTURE, LIVE>(a, rb, s);
+    if (a.K <= 8) return launch_rb<DK, 8, O_BF16, CAPTURE, LIVE>(a, rb, s);
+    if (a.K <= 16) return launch_rb<DK, 16, O_BF16, CAPTURE, LIVE>(a, rb, s);
+    if (a.K <= 32) return launch_rb<DK, 32, O_BF16, CAPTURE, LIVE>(a, rb, s);
+    return launch_rb<DK, 64, O_BF16, CAPTURE, LIVE>(a, rb, s);
 }
 
 template <int DK, bool O_BF16>
@@ -459,7 +533,8 @@ hipError_t launch_step(const VerifyArgs& a, bool in_bf16, bool o_bf16, hipStream
 {
     // bf16 slabs whose value heads come in groups of three per key head take the pipelined
     // kernel; other shapes the verify kernel's fused-step mode (same results)
-    if (in_bf16 && (a.Hv / a.Hk) % kGroups == 0)
+    // (its buffer-resource offsets are 32-bit: an o plane of one sequence below 2 GiB)
+    if (in_bf16 && (a.Hv / a.Hk) % kGroups == 0 && (long long)a.K * a.Hv * a.dv * 4 < (1LL << 31))
         return o_bf16 ? launch_o<true>(a, s) : launch_o<false>(a, s);
     return launch_verify(a, in_bf16, o_bf16, s);
 }

@@ -1,7 +1,7 @@
 """Phase timeline of the fused verify step (gdn_verify_step) on the verify16 workload.
 
     python -m speculative_verify_gdn_amd.build --timeline
-    python -m speculative_verify_gdn_amd.timeline [--launches 6] [--sets 12]
+    python -m speculative_verify_gdn_amd.timeline [--launches 6] [--sets 12] [--workload verify16]
 
 Loads libgdn_timeline.so (the library built with the wall-clock marks of
 csrc/gdn_timeline.h) and runs the step chained over buffer sets as bench.py
@@ -47,12 +47,13 @@ def main():
     ap.add_argument("--launches", type=int, default=6)
     ap.add_argument("--sets", type=int, default=12)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="verify16", help="verify16 or batched (B=32, K=8)")
     args = ap.parse_args()
     lib = gdn.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn_timeline.so"))
     lib.gdn_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     lib.gdn_timeline_read.restype = ctypes.c_int
     lib.gdn_timeline_clear.restype = ctypes.c_int
-    wl = synth.WORKLOADS["verify16"]
+    wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
 
     def make_set(seed):
@@ -83,7 +84,7 @@ def main():
     for r in range(args.warmup):
         step(r)
     torch.cuda.synchronize()
-    grid = (wl.dv // 8) * (wl.Hv // 3) * wl.B
+    grid = min((wl.dv // 8) * (wl.Hv // 3) * wl.B, TL_GROUPS)   # workgroups with marks
     nw = 12
     buf = np.zeros(TL_GROUPS * TL_WAVES * TL_MARKS, dtype=np.uint64)
     for n in range(args.launches):
@@ -107,6 +108,9 @@ def main():
         out["entry_median_by_xcd"] = [round(float(np.nanmedian(ent[x::8])), 2) for x in range(8)]
         out["end_median_by_xcd"] = [round(float(np.nanmedian(end[x::8])), 2) for x in range(8)]
         out["last_end"] = round(float(np.nanmax(end)), 2)
+        # per workgroup: from its first wave's entry to its last wave's end
+        dur = end - ent
+        out["workgroup_span"] = [round(float(q), 2) for q in (np.nanmin(dur), np.nanmedian(dur), np.nanmax(dur))]
         print(json.dumps(out), flush=True)
 
 
