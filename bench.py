@@ -43,6 +43,9 @@ METRIC = "GDN verify tokens/s per layer (K=16) + achieved HBM GB/s vs peak"
 # the sources of the step's kernel (gdn_verify_step on bf16 slabs); the committed counter profile of
 # the kernel is used only while they hash to the value recorded with it
 STEP_SOURCES = ("gdn_step.hip", "gdn_verify_common.h", "gdn_device.h", "gdn_conv_math.h", "gdn_timeline.h")
+# the sources of gdn_verify with bf16 in and bf16 o (the instance the bench times)
+VERIFY_SOURCES = ("gdn_verify_impl.h", "gdn_verify_bf16_bf16.hip", "gdn_verify_common.h", "gdn_device.h",
+                  "gdn_conv_math.h", "gdn_timeline.h")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 O_DTYPE = [None]               # torch dtype of o, set in main (bf16 unless --o-f32)
 MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
@@ -785,13 +788,14 @@ def main():
 
     vb = verify_bytes(wl)
     sb = step_bytes(wl)
-    sha = source_sha(*STEP_SOURCES)
     cpk = copy_peak(torch, dev)
     if mode == "fused":
         # the dominant (and only) kernel of the step: gdn_verify_step
         dom, dom_bytes, dom_us = "gdn_verify_step", sb, t_fused
+        sha = source_sha(*STEP_SOURCES)
     else:
         dom, dom_bytes, dom_us = "gdn_verify", vb, t_ver
+        sha = source_sha(*VERIFY_SOURCES)
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     traffic = read_traffic(dom, wl.name, sha)
     mean_rb_bytes = sum(rollback_bytes(wl, [a]) for a in accepts) / len(accepts)

@@ -1,7 +1,8 @@
-"""Phase timeline of the fused verify step (gdn_verify_step) on the verify16 workload.
+"""Phase timelines of the fused verify step (gdn_verify_step) and of the chunked prefill.
 
     python -m speculative_verify_gdn_amd.build --timeline
-    python -m speculative_verify_gdn_amd.timeline [--launches 6] [--sets 12] [--workload verify16]
+    python -m speculative_verify_gdn_amd.timeline [--launches 6] [--sets 12] [--workload verify16|batched]
+    python -m speculative_verify_gdn_amd.timeline --workload prefill [--launches 2]
 
 Loads libgdn_timeline.so (the library built with the wall-clock marks of
 csrc/gdn_timeline.h) and runs the step chained over buffer sets as bench.py
@@ -21,6 +22,13 @@ Marks (lane 0 of every wave, 100 MHz real-time counter):
 Printed: one JSON line per launch with [min, p10, median, p90, max] of every
 mark in microseconds after the launch's earliest entry, the median entry and
 end per XCD (workgroup index mod 8) and the end of the slowest wave.
+
+With --workload prefill the marks are those of gdn_prefill_chunked's eleventh chunk
+(chunk index 10) in every workgroup, for the 8 state waves and the 4 preparation
+waves: 0 chunk start, 1 phase-1 work done, 2 past the phase-1 barrier, 3 phase-2
+work done, 4 past the phase-2 barrier.  Printed: per role and per preparation
+wave, the median and p90 over workgroups of each mark in nanoseconds after the
+wave's own chunk start.
 """
 from __future__ import annotations
 
@@ -42,14 +50,57 @@ TL_GROUPS, TL_WAVES, TL_MARKS = 2048, 16, 16
 NAMES = {8: "entry", 0: "start", 5: "accept", 6: "state", 7: "gates_v", 1: "conv0", 2: "barrier", 3: "store0", 4: "end"}
 
 
+def prefill_timeline(lib, launches):
+    lib.gdn_timeline_prefill_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.gdn_timeline_prefill_read.restype = ctypes.c_int
+    lib.gdn_timeline_prefill_clear.restype = ctypes.c_int
+    wl = synth.WORKLOADS["prefill"]
+    dev = torch.device("cuda", 0)
+    inp = synth.make_inputs(wl, seed=0)
+    d = {k: v.to(dev) for k, v in inp.items()}
+    d["qkv"] = synth.make_qkv(wl, seed=0).to(dev)
+    d["S_out"] = torch.empty_like(d["S_in"])
+    d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev, dtype=torch.bfloat16)
+
+    def pre():
+        gdn.prefill_chunked(d["qkv"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], d["S_out"],
+                            d["o"], wl.Hk, chunk=wl.chunk)
+
+    for _ in range(3):
+        pre()
+    torch.cuda.synchronize()
+    grid = wl.B * wl.Hv
+    buf = np.zeros(TL_GROUPS * TL_WAVES * TL_MARKS, dtype=np.uint64)
+    names = ("start", "p1_work", "p1_barrier", "p2_work", "p2_barrier")
+    for n in range(launches):
+        assert lib.gdn_timeline_prefill_clear() == 0
+        torch.cuda.synchronize()
+        pre()
+        torch.cuda.synchronize()
+        assert lib.gdn_timeline_prefill_read(buf.ctypes.data, buf.nbytes) == 0
+        t = buf.reshape(TL_GROUPS, TL_WAVES, TL_MARKS)[:grid, :12, :5].astype(np.int64)
+        rel = (t - t[:, :, :1]) * 10   # 100 MHz ticks -> ns after the wave's own chunk start
+        out = {"launch": n, "chunk": 10}
+        for role, ws in (("state_waves", slice(0, 8)), ("prep_waves", slice(8, 12))):
+            x = rel[:, ws, :]
+            out[role] = {nm: [int(np.median(x[:, :, k])), int(np.percentile(x[:, :, k], 90))]
+                         for k, nm in enumerate(names) if k}
+        out["prep_wave_p1_work_median"] = [int(np.median(rel[:, 8 + w, 1])) for w in range(4)]
+        out["prep_wave_p2_work_median"] = [int(np.median(rel[:, 8 + w, 3] - rel[:, 8 + w, 2])) for w in range(4)]
+        print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--launches", type=int, default=6)
     ap.add_argument("--sets", type=int, default=12)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", default="verify16", help="verify16 or batched (B=32, K=8)")
+    ap.add_argument("--workload", default="verify16", help="verify16, batched (B=32, K=8) or prefill")
     args = ap.parse_args()
     lib = gdn.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn_timeline.so"))
+    if args.workload == "prefill":
+        prefill_timeline(lib, args.launches)
+        return
     lib.gdn_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     lib.gdn_timeline_read.restype = ctypes.c_int
     lib.gdn_timeline_clear.restype = ctypes.c_int
