@@ -113,7 +113,7 @@ def main():
         d["win"] = torch.empty(wl.B, wl.W - 1 + wl.T, wl.C, dtype=d["x"].dtype, device=dev)
         d["S_out"] = torch.empty_like(d["S_in"])
         d["H"] = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device=dev)
-        d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev)
+        d["o"] = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device=dev, dtype=torch.bfloat16)
         d["S_ckpt"] = torch.empty_like(d["S_in"])
         return d
 
