@@ -15,6 +15,18 @@ then linked into speculative_verify_gdn_amd/libgdn.so.  Flags:
                                  IEEE float division and denormals (the conv
                                  step is bit-exact by construction)
   -target-feature -packed-fp32-ops   no packed fp32 VALU instructions
+  -mllvm -amdgpu-mfma-padding-ratio=100
+                                 s_nops cover the latency between neighbouring
+                                 MFMAs (only MFMA code changes).  Without them the
+                                 chunked prefill gave wrong outputs in two elements
+                                 of one accumulator tile, depending on timing: an
+                                 MFMA that takes its accumulator from the MFMA
+                                 just before it (into another register) read it
+                                 after a later LDS load had refilled the register
+                                 the compiler had freed.  With the same
+                                 instructions and registers and the latency padded
+                                 the outputs are right; the padding costs nothing
+                                 measurable on the MFMA kernels here.
 """
 from __future__ import annotations
 
@@ -37,14 +49,16 @@ FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-padding-ratio=100",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
     "-I" + os.path.join(ROOT, "include"),
 ]
+SOURCE_FLAGS: dict = {}
 
 
 def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(os.path.basename(src), ()), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -127,6 +127,8 @@ hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s);
 hipError_t launch_rollback_conv(const RollConvArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, bool o_bf16, hipStream_t s);
 hipError_t launch_prefill_wy(const PrefillArgs& a, bool o_bf16, hipStream_t s);
+// the chunkwise kernel for dk = 128 and chunks of 64 tokens (hipErrorInvalidValue for other shapes)
+hipError_t launch_prefill_c64(const PrefillArgs& a, bool o_bf16, hipStream_t s);
 hipError_t launch_conv_tree(const ConvTreeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_tree_rollback(const TreeRollbackArgs& a, hipStream_t s);
 

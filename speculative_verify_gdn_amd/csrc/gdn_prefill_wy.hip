@@ -43,19 +43,18 @@
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_timeline.h"
+#include "gdn_wy_mfma.h"
 
 namespace gdn {
 namespace {
 
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short bf16x4_t;
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+using namespace wy;
 
 constexpr int kStateWaves = 8;                           // waves holding state rows (16 each)
 constexpr int kPrepWaves = 4;                            // waves preparing the next chunk
 constexpr int kThreads = 64 * (kStateWaves + kPrepWaves);
 constexpr int kPrepThreads = 64 * kPrepWaves;
 constexpr int kRows = 16 * kStateWaves;                  // state rows per workgroup
-constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: raw dword access on CDNA
 
 template <int DK, int L>
 struct WyShape {
@@ -105,71 +104,8 @@ struct WySmem {
     float E[S::NT][L];               // e^{G_t - G_end(k)} for blocks k before t's block
 };
 
-// A 32-wide slice of a contraction index is spread over the four lane groups
-// g of an MFMA operand as pi(g, s) = 4g + s (s < 4) and 16 + 4g + (s - 4)
-// (s >= 4): the order in which a 16x16 accumulator tile holds its rows, so
-// two accumulator tiles feed the next product directly.
-__device__ __forceinline__ int pi_group(int x) { return (x & 15) >> 2; }
-__device__ __forceinline__ int pi_slot(int x) { return ((x >> 4) << 2) | (x & 3); }
-
-// record swizzle of q/k operand tiles (a permutation of the 64 records; it
-// spreads the staging writes over the banks), and the record of K^T operand
-// (jt, slice, lane): one pad record per key tile does the same for K^T
-__device__ __forceinline__ int qk_rec(int lane, int m) { return lane ^ ((m & 3) << 2); }
 template <int NS>
 __device__ __forceinline__ int kt_rec(int jt, int ms, int lane) { return jt * (NS * 64 + 1) + ms * 64 + lane; }
-
-// gates of one token for value head h
-__device__ __forceinline__ void wy_gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
-                                        float& beta, float& g)
-{
-    if (dt_bias != nullptr) {
-        beta = __frcp_rn(1.0f + __expf(-braw));
-        const float a = al + dt_bias[h];
-        const float sp = a > 20.0f ? a : __logf(1.0f + __expf(a));
-        g = -sp * __expf(A_log[h]);
-    } else {
-        beta = braw;
-        g = al;
-    }
-}
-
-// bf16 hi (round to nearest) and lo (the rounded remainder) of 2 floats, packed
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo)
-{
-    const bf16x2_t hb = {(__bf16)x0, (__bf16)x1};
-    const uint32_t hu = __builtin_bit_cast(uint32_t, hb);
-    const float r0 = x0 - __uint_as_float(hu << 16);
-    const float r1 = x1 - __uint_as_float(hu & 0xffff0000u);
-    const bf16x2_t lb = {(__bf16)r0, (__bf16)r1};
-    hi = hu;
-    lo = __builtin_bit_cast(uint32_t, lb);
-}
-
-__device__ __forceinline__ void split4(const f32x4_t x, uint2& hi, uint2& lo)
-{
-    split2(x[0], x[1], hi.x, lo.x);
-    split2(x[2], x[3], hi.y, lo.y);
-}
-
-__device__ __forceinline__ bf16x4_t as4(uint2 u) { return __builtin_bit_cast(bf16x4_t, u); }
-
-__device__ __forceinline__ bf16x8_t as8(uint2 a, uint2 b)
-{
-    return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
-}
-
-__device__ __forceinline__ f32x4_t mfma16(uint2 a, uint2 b, f32x4_t c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as4(a), as4(b), c, 0, 0, 0);
-}
-
-__device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float4 lds_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 // sum over each aligned group of N lanes (N = 4, 8 or 16), every lane gets it
 template <int N>
@@ -180,19 +116,6 @@ __device__ __forceinline__ float group_sum(float v)
     if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
     if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
     return v;
-}
-
-// sum of squares of 8 bf16 (exact products, fp32 sums)
-__device__ __forceinline__ float sq8(const uint4 u)
-{
-    float s = 0.f;
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16x2_t v = __builtin_bit_cast(bf16x2_t, w[e]);
-        s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
-    }
-    return s;
 }
 
 // linear index of a gram tile other than the diagonal blocks of A ->
@@ -216,17 +139,6 @@ __device__ __forceinline__ void other_tile(int i, bool& is_m, int& ib, int& kb)
     kb = r;
 }
 
-// value head of workgroup row y: the value heads of key head kh sit at rows congruent mod 8
-// (each block of 8 G rows holds 8 key heads, G = Hv / Hk), so with one workgroup per head and
-// sequence they are dispatched to one XCD; other shapes keep the identity
-__device__ __forceinline__ int wy_head(int y, int Hv, int Hk, int gx)
-{
-    const int G = Hv / Hk;
-    if (gx != 1 || Hv % (8 * G) != 0) return y;
-    const int k = y / (8 * G), r = y % (8 * G);
-    return (8 * k + r % 8) * G + r / 8;
-}
-
 template <int DK, int L, bool O_BF16>
 __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
 {
@@ -241,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
     const bool prep = wave >= kStateWaves;
     const int b = blockIdx.z;
     const int T = a.T, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
-    const int h = wy_head(blockIdx.y, Hv, Hk, gridDim.x);
+    const int h = head_of_row(blockIdx.y, Hv, Hk, gridDim.x);
     const int C = 2 * Hk * DK + Hv * dv;
     const int hk = h / (Hv / Hk);
     const uint16_t* qkv = reinterpret_cast<const uint16_t*>(a.qkv);
@@ -315,8 +227,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
                     dst[8 * e] = (uint16_t)((e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu));
             }
             // norms: every token row is CPR consecutive lanes
-            const float sq = group_sum<CPR>(sq8(q));
-            const float sk = group_sum<CPR>(sq8(k));
+            const float sq = group_sum<CPR>(sq8(q, 0.f));
+            const float sk = group_sum<CPR>(sq8(k, 0.f));
             if (sr == 0 && in_chunk) {
                 const bool valid = t < Lv;
                 x.rk[t] = valid ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.f;
@@ -326,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
         if (pwave == 0) {
             // gates, their running sum and the decay factors; lane = token
             float beta = 0.f, g = 0.f;
-            if (lane < Lv) wy_gate(bf16_lo(graw), bf16_hi(graw), a.dt_bias, a.A_log, h, beta, g);
+            if (lane < Lv) gate(bf16_lo(graw), bf16_hi(graw), a.dt_bias, a.A_log, h, beta, g);
             float G = g;
 #pragma unroll
             for (int d = 1; d < L; d <<= 1) {
@@ -732,6 +644,8 @@ hipError_t launch_o(const PrefillArgs& a, hipStream_t s)
 
 hipError_t launch_prefill_wy(const PrefillArgs& a, bool o_bf16, hipStream_t s)
 {
+    // dk = 128 with chunks of 64 tokens: the kernel with 32-row state waves
+    if (a.dk == 128 && a.chunk == 64) return launch_prefill_c64(a, o_bf16, s);
     return o_bf16 ? launch_o<true>(a, s) : launch_o<false>(a, s);
 }
 

@@ -24,9 +24,9 @@ mark in microseconds after the launch's earliest entry, the median entry and
 end per XCD (workgroup index mod 8) and the end of the slowest wave.
 
 With --workload prefill the marks are those of gdn_prefill_chunked's eleventh chunk
-(chunk index 10) in every workgroup, for the 8 state waves and the 4 preparation
-waves: 0 chunk start, 1 phase-1 work done, 2 past the phase-1 barrier, 3 phase-2
-work done, 4 past the phase-2 barrier.  Printed: per role and per preparation
+(chunk index 10) in every workgroup (the dk = 128, chunk 64 kernel), for the 4 state
+waves and the 4 preparation waves: 0 chunk start, 1 phase-1 work done, 2 past the
+phase-1 barrier, 3 phase-2 work done, 4 past the phase-2 barrier.  Printed: per role and per preparation
 wave, the median and p90 over workgroups of each mark in nanoseconds after the
 wave's own chunk start.
 """
@@ -51,9 +51,9 @@ NAMES = {8: "entry", 0: "start", 5: "accept", 6: "state", 7: "gates_v", 1: "conv
 
 
 def prefill_timeline(lib, launches):
-    lib.gdn_timeline_prefill_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
-    lib.gdn_timeline_prefill_read.restype = ctypes.c_int
-    lib.gdn_timeline_prefill_clear.restype = ctypes.c_int
+    lib.gdn_timeline_c64_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.gdn_timeline_c64_read.restype = ctypes.c_int
+    lib.gdn_timeline_c64_clear.restype = ctypes.c_int
     wl = synth.WORKLOADS["prefill"]
     dev = torch.device("cuda", 0)
     inp = synth.make_inputs(wl, seed=0)
@@ -73,20 +73,29 @@ def prefill_timeline(lib, launches):
     buf = np.zeros(TL_GROUPS * TL_WAVES * TL_MARKS, dtype=np.uint64)
     names = ("start", "p1_work", "p1_barrier", "p2_work", "p2_barrier")
     for n in range(launches):
-        assert lib.gdn_timeline_prefill_clear() == 0
+        assert lib.gdn_timeline_c64_clear() == 0
         torch.cuda.synchronize()
         pre()
         torch.cuda.synchronize()
-        assert lib.gdn_timeline_prefill_read(buf.ctypes.data, buf.nbytes) == 0
-        t = buf.reshape(TL_GROUPS, TL_WAVES, TL_MARKS)[:grid, :12, :5].astype(np.int64)
+        assert lib.gdn_timeline_c64_read(buf.ctypes.data, buf.nbytes) == 0
+        t = buf.reshape(TL_GROUPS, TL_WAVES, TL_MARKS)[:grid, :8, :].astype(np.int64)
         rel = (t - t[:, :, :1]) * 10   # 100 MHz ticks -> ns after the wave's own chunk start
         out = {"launch": n, "chunk": 10}
-        for role, ws in (("state_waves", slice(0, 8)), ("prep_waves", slice(8, 12))):
+        for role, ws in (("state_waves", slice(0, 4)), ("prep_waves", slice(4, 8))):
             x = rel[:, ws, :]
             out[role] = {nm: [int(np.median(x[:, :, k])), int(np.percentile(x[:, :, k], 90))]
                          for k, nm in enumerate(names) if k}
-        out["prep_wave_p1_work_median"] = [int(np.median(rel[:, 8 + w, 1])) for w in range(4)]
-        out["prep_wave_p2_work_median"] = [int(np.median(rel[:, 8 + w, 3] - rel[:, 8 + w, 2])) for w in range(4)]
+        out["prep_wave_p1_work_median"] = [int(np.median(rel[:, 4 + w, 1])) for w in range(4)]
+        out["prep_wave_p2_work_median"] = [int(np.median(rel[:, 4 + w, 3] - rel[:, 4 + w, 2])) for w in range(4)]
+        out["state_wave_p2_work_median"] = [int(np.median(rel[:, w, 3] - rel[:, w, 2])) for w in range(4)]
+        # finer marks (ns after the chunk start, median over workgroups and waves of the role)
+        fine = {"prep": {5: "q|k arrived", 6: "operands + K^T written", 7: "norms written", 8: "gates scanned",
+                         9: "gate factors written", 10: "diagonal block scaled", 11: "inverse written",
+                         12: "gram tiles written"},
+                "state": {15: "P, R done", 13: "U_0, U_1, O_0, O_1, first S update", 14: "phase 2 done"}}
+        for role, ws in (("state", slice(0, 4)), ("prep", slice(4, 8))):
+            x = rel[:, ws, :]
+            out[role + "_marks"] = {nm: int(np.median(x[:, :, k])) for k, nm in fine[role].items()}
         print(json.dumps(out), flush=True)
 
 

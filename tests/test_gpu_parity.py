@@ -550,6 +550,12 @@ WY_CASES = [
     (dict(B=1, T=129, Hk=1, Hv=2), 32, dict(weak=True, o_bf16=True)),
     (dict(B=1, T=47, Hk=1, Hv=2), 16, dict()),
     (dict(B=3, T=96, Hk=2, Hv=2, dk=64, dv=64), 64, dict(activated=True, weak=True)),
+    # dk = 128 with chunks of 64 (32-row state waves): rows past dv inside a wave and whole waves
+    # past it, two row blocks per head, one token, a one-token last chunk
+    (dict(B=1, T=200, Hk=1, Hv=2, dv=48), 64, dict(weak=True)),
+    (dict(B=2, T=150, Hk=1, Hv=1, dv=160), 64, dict(o_bf16=True, inplace=True)),
+    (dict(B=1, T=1, Hk=1, Hv=1), 64, dict()),
+    (dict(B=1, T=65, Hk=2, Hv=4), 64, dict(activated=True)),
 ]
 
 
