@@ -15,8 +15,8 @@
 // Workgroup: 8 waves for 128 state rows of one (sequence, value head), one
 // workgroup per CU, two waves per SIMD:
 //   state waves (4): each owns 32 state rows for the whole prompt, kept in
-//     registers as MFMA accumulator tiles of S^T (lane <-> state row, two
-//     16-row tiles, 8 key tiles each).  Per chunk: P = K S^T and R = Q S^T
+//     registers as MFMA accumulator tiles of S^T (lane r <-> state rows 2r and
+//     2r + 1, one per 16-row tile, 8 key tiles each).  Per chunk: P = K S^T and R = Q S^T
 //     with the state split into bf16 hi + lo (one read of each K and Q
 //     operand serves both row tiles), the right-hand sides and the state part
 //     of O; then block forward substitution for U, O += M U and
@@ -24,7 +24,8 @@
 //     16-token blocks use the 16x16x32 MFMA (on gfx950 the 16x16x16 form takes
 //     as long for half the work).
 //   prep waves (4): for the next chunk meanwhile.  Phase 1: prep wave p stages
-//     token tile p (raw q, k in operand order, K^T for the state update) and
+//     token tile p (raw q, k in operand order; the state update reads its K^T
+//     operands from the same k tiles with transposing LDS reads) and
 //     the tile's norms, and the gates of all 64 tokens (every prep wave forms
 //     them; a wave-wide DPP scan gives the running sums).  Phase 2: five gram
 //     tiles per wave (K K^T and K Q^T scaled to -A and M, stored as bf16 hi/lo
@@ -52,14 +53,13 @@ constexpr int kSW = 4;                           // state waves (32 rows each)
 constexpr int kPW = 4;                           // prep waves
 constexpr int kC64Threads = 64 * (kSW + kPW);
 constexpr int kC64Rows = 32 * kSW;
-constexpr int kKTS = 2 * 64 + 1;                 // K^T records per key tile: two 32-token slices + pad
 
 struct C64Chunk {
     bf16x8_t qop[4][4][64];      // raw q: [token tile][32-key slice][record]; record of lane (r, g):
                                  // token 16 tile + r, keys 32 slice + pi(g, 0..7)
-    bf16x8_t kop[4][4][64];      // raw k, same order
-    bf16x8_t ktop[8 * kKTS];     // raw k^T: [key tile jt][32-token slice][record]; record of lane
-                                 // (r, g): key 16 jt + r, tokens 32 slice + pi(g, 0..7)
+    bf16x8_t kop[4][4][64];      // raw k, same order (any 4 consecutive keys of a token, aligned to 4,
+                                 // are 8 contiguous bytes: the K^T operands are read from here with
+                                 // transposing reads)
     uint2 Ah[6][64], Al[6][64];  // -A tiles (ib > kb, row order), 16x16x16 A-operand order, bf16 hi / lo
     uint2 Th[4][64], Tl[4][64];  // (I + A_ii)^-1
     uint2 Mh[10][64], Ml[10][64];  // M tiles (kb <= ib, row order)
@@ -110,6 +110,15 @@ __device__ __forceinline__ float wave_scan(float x)
     x += dpp0<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
     x += dpp0<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
     return x;
+}
+
+// transposing LDS read of 4 bf16 (see the K^T operand in the state update for the lane mapping)
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 tr16(const char* p)
+{
+    typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
+    return __builtin_bit_cast(uint2, v);
 }
 
 // hi/lo pair of a 16x16 tile in one operand order
@@ -168,7 +177,9 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
         const int p = __builtin_amdgcn_readfirstlane(wave - kSW);
         const int j = g;                          // piece group: keys 32 i + 8 j .. +7 of slice i
         uint4 qreg[4], kreg[4];                   // token 16 p + r, slices 0..3, piece j
-        uint32_t graw = 0;                        // lane t: raw beta | raw alpha << 16 of token t
+        // lane t: raw beta and raw alpha of token t, each in its own register (combining them at load
+        // time would wait for the prefetch right away)
+        uint32_t gbr = 0, gal = 0;
         float gbeta = 0.f, gG = 0.f;              // lane t: beta_t and G_t of the chunk staged last
         const int qoff = ((16 * p + r) * C + hk * kDK + 8 * j) * 2;
         auto prefetch = [&](int c0) __attribute__((always_inline)) {
@@ -187,8 +198,8 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.alpha) + g0), 0, Lv * Hv * 2, kBufferFlags);
             const int goff = (lane * Hv + h) * 2;
-            graw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, goff, 0, 0) |
-                   ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ra, goff, 0, 0) << 16);
+            gbr = __builtin_amdgcn_raw_buffer_load_b16(rb, goff, 0, 0);
+            gal = __builtin_amdgcn_raw_buffer_load_b16(ra, goff, 0, 0);
         };
 
         // phase 1: token tile p of the chunk at c0 into buffer x, and its norms
@@ -197,7 +208,6 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             if (mk) GDN_TLV(5, qreg[3].w);
             const int t = 16 * p + r;
             const int hf = j >> 1, g0 = (j & 1) << 1;
-            const int ms = t >> 5, tg = pi_group(t & 31), ts = pi_slot(t & 31);
             float sq = 0.f, sk = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -210,13 +220,6 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
                 *reinterpret_cast<uint2*>(qd + r1) = make_uint2(q.z, q.w);
                 *reinterpret_cast<uint2*>(kd + r0) = make_uint2(k.x, k.y);
                 *reinterpret_cast<uint2*>(kd + r1) = make_uint2(k.z, k.w);
-                // k^T: key 32 i + 8 j + e is row 8 (j & 1) + e of key tile 2 i + (j >> 1)
-                uint16_t* dst = reinterpret_cast<uint16_t*>(
-                                    &x.ktop[(2 * i + (j >> 1)) * kKTS + ms * 64 + 8 * (j & 1) + 16 * tg]) + ts;
-                const uint32_t kw[4] = {k.x, k.y, k.z, k.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    dst[8 * e] = (uint16_t)((e & 1) ? (kw[e >> 1] >> 16) : (kw[e >> 1] & 0xffffu));
                 sq = sq8(q, sq);
                 sk = sq8(k, sk);
             }
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             // the gates (lane = token) and their running sum, from the raw bits loaded with the chunk
             // (the next prefetch overwrites them)
             float beta = 0.f, gg = 0.f;
-            if (lane < Lv) gate(bf16_lo(graw), bf16_hi(graw), a.dt_bias, a.A_log, h, beta, gg);
+            if (lane < Lv) gate(bf16_lo(gbr), bf16_lo(gal), a.dt_bias, a.A_log, h, beta, gg);
             gbeta = beta;
             gG = wave_scan(gg);
             if (mk) GDN_TLV(8, gG);
@@ -396,15 +399,16 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
     }
 
     // ================================================================ state waves
-    // rows of this lane: 32 wave + 16 rt + r of the workgroup's block; rows past dv carry zeros and
-    // store nothing
-    const int row0 = blockIdx.x * kC64Rows + 32 * wave + r;
-    const bool live0 = row0 < dv, live1 = row0 + 16 < dv;
+    // rows of this lane: 32 wave + 2 r + rt of the workgroup's block (two adjacent rows, so each v
+    // load and o store covers both); rows past dv carry zeros and store nothing (dv is even: both
+    // rows or neither)
+    const int row0 = blockIdx.x * kC64Rows + 32 * wave + 2 * r;
+    const bool live0 = row0 < dv, live1 = row0 + 1 < dv;
     f32x4_t S[8][2];                 // S^T tiles: S[jt][rt] lane (r, g) e = S[row][16 jt + 4 g + e]
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         const bool lv = rt ? live1 : live0;
-        const float* sp = a.S_in + (((size_t)b * Hv + h) * dv + (lv ? row0 + 16 * rt : 0)) * kDK + 4 * g;
+        const float* sp = a.S_in + (((size_t)b * Hv + h) * dv + (lv ? row0 + rt : 0)) * kDK + 4 * g;
 #pragma unroll
         for (int jt = 0; jt < 8; ++jt) {
             const f32x4_t v = load_f4(sp + 16 * jt);
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
         }
     }
     // v[token 16 tt + 4 g + e][row of rt] of the chunk to process next (raw bf16)
-    uint32_t vreg[4][4][2];
+    uint32_t vreg[4][4];             // v of rows row0, row0 + 1 (bf16 pair) for token 16 tt + 4 g + e
     const int voff = ((4 * g) * C + 2 * Hk * kDK + h * dv + row0) * 2;
     auto prefetch_v = [&](int c0) __attribute__((always_inline)) {
         // rows past dv read another channel or past the chunk (zero): unused
@@ -422,8 +426,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int so = __builtin_amdgcn_readfirstlane((16 * tt + e) * C * 2);
-                vreg[tt][e][0] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff, so, 0);
-                vreg[tt][e][1] = __builtin_amdgcn_raw_buffer_load_b16(rv, voff + 32, so, 0);
+                vreg[tt][e] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, so, 0);
             }
     };
     prefetch_v(0);
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
                     const bool lv = rt ? live1 : live0;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float v = lv ? bf16_lo(vreg[tt][e][rt]) : 0.f;
+                        const float v = lv ? (rt ? bf16_hi(vreg[tt][e]) : bf16_lo(vreg[tt][e])) : 0.f;
                         X[tt][rt][e] = __builtin_fmaf(-av[e], P[tt][rt][e], bv[e] * v);
                         O[tt][rt][e] = ev[e] * R[tt][rt][e];
                     }
@@ -511,8 +514,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             // rows past dv and tokens past the prompt fall outside the resource: dropped
             const int ostride = Hv * dv * OE;
             const int obase = ((4 * g * Hv + h) * dv + row0) * OE;
-            const int ooff0 = live0 ? obase : 0x7ffffff0;
-            const int ooff1 = live1 ? obase + 16 * OE : 0x7ffffff0;
+            const int ooff = live0 ? obase : 0x7ffffff0;
             HL U[4][2], CU[4][2];
             auto tileA = [&](int ib, int kb) __attribute__((always_inline)) {
                 const int ia = ib * (ib - 1) / 2 + kb;
@@ -555,6 +557,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
                 }
                 if (ib >= 2) M2 = tileM(ib, 2);
                 if (ib == 3) M3 = tileM(3, 3);
+                f32x4_t o2[2];
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
                     f32x4_t o = O[ib][rt];
@@ -562,21 +565,34 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
                     if (ib >= 1) o = mm32(M0, M1, U[0][rt], U[1][rt], o);
                     if (ib == 2) o = mm16(M2, U[2][rt], o);
                     if (ib == 3) o = mm32(M2, M3, U[2][rt], U[3][rt], o);
+                    o2[rt] = o;
+                }
+                // both rows of the lane in one store per token
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int so = __builtin_amdgcn_readfirstlane((16 * ib + e) * ostride);   // the token's
-                        const int off = rt ? ooff1 : ooff0;
-                        if constexpr (O_BF16)
-                            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)o[e]), ro, off, so, 0);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[e]), ro, off, so, 0);
+                for (int e = 0; e < 4; ++e) {
+                    const int so = __builtin_amdgcn_readfirstlane((16 * ib + e) * ostride);   // the token's
+                    if constexpr (O_BF16) {
+                        const bf16x2_t pr = {(__bf16)o2[0][e], (__bf16)o2[1][e]};
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, pr), ro, ooff, so, 0);
+                    } else {
+                        typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+                        const u32x2_t pr = {__float_as_uint(o2[0][e]), __float_as_uint(o2[1][e])};
+                        __builtin_amdgcn_raw_buffer_store_b64(pr, ro, ooff, so, 0);
                     }
                 }
                 if (ib & 1) {
-                    // tiles ib-1, ib form the 32-token slice ib/2
+                    // tiles ib-1, ib form the 32-token slice ib/2.  The K^T operand of key tile jt: lane
+                    // (r, g) needs k[32 s + pi(g, 0..7)][16 jt + r]; a transposing read hands lane r of
+                    // each 16-lane group element r mod 4 of the 4-vector addressed by lane
+                    // 4 s' + r / 4 of that group, so lane (j, g) addresses keys 16 jt + 4 (j mod 4) ..
+                    // + 3 of token 32 s + 4 g + j / 4 (and + 16 for the second half)
 #pragma unroll
                     for (int jt = 0; jt < 8; ++jt) {
-                        const bf16x8_t ka = cur.ktop[jt * kKTS + (ib >> 1) * 64 + lane];
+                        const int m = jt >> 1, hb = 8 * (jt & 1);
+                        const int rec = qk_rec(4 * g + (r >> 2) + 16 * (r & 3), m);
+                        const char* k0 = reinterpret_cast<const char*>(&cur.kop[ib - 1][m][rec]) + hb;
+                        const char* k1 = reinterpret_cast<const char*>(&cur.kop[ib][m][rec]) + hb;
+                        const bf16x8_t ka = as8(tr16(k0), tr16(k1));
 #pragma unroll
                         for (int rt = 0; rt < 2; ++rt) {
                             S[jt][rt] = mfma32(ka, as8(CU[ib - 1][rt].h, CU[ib][rt].h), S[jt][rt]);
@@ -600,7 +616,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         if (rt ? live1 : live0) {
-            float* sp = a.S_out + (((size_t)b * Hv + h) * dv + row0 + 16 * rt) * kDK + 4 * g;
+            float* sp = a.S_out + (((size_t)b * Hv + h) * dv + row0 + rt) * kDK + 4 * g;
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) store_f4<false>(sp + 16 * jt, S[jt][rt]);
         }

@@ -166,7 +166,9 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
     // ---------------------------------------------------------------- prep waves
     const int ptid = tid - kStateWaves * 64, pwave = wave - kStateWaves;
     uint4 qreg[NP], kreg[NP];  // the q|k pieces of the chunk to stage next
-    uint32_t graw = 0;         // prep wave 0, lane t: raw beta | raw alpha << 16
+    // prep wave 0, lane t: raw beta and raw alpha, each in its own register (combining them at load
+    // time would wait for the prefetch right away)
+    uint32_t gbr = 0, gal = 0;
     // staging role: piece sr of token row stp (+ TPP per pass)
     const int qoff = ((ptid / CPR) * C + hk * DK + 8 * (ptid % CPR)) * 2;
     const int goff = (lane0 * Hv + h) * 2;
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
             const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<uint16_t*>(reinterpret_cast<const uint16_t*>(a.alpha) + g0), 0, Lv * Hv * 2,
                 kBufferFlags);
-            graw = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, goff, 0, 0) |
-                   ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ra, goff, 0, 0) << 16);
+            gbr = __builtin_amdgcn_raw_buffer_load_b16(rb, goff, 0, 0);
+            gal = __builtin_amdgcn_raw_buffer_load_b16(ra, goff, 0, 0);
         }
     };
 
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
         if (pwave == 0) {
             // gates, their running sum and the decay factors; lane = token
             float beta = 0.f, g = 0.f;
-            if (lane < Lv) gate(bf16_lo(graw), bf16_hi(graw), a.dt_bias, a.A_log, h, beta, g);
+            if (lane < Lv) gate(bf16_lo(gbr), bf16_lo(gal), a.dt_bias, a.A_log, h, beta, g);
             float G = g;
 #pragma unroll
             for (int d = 1; d < L; d <<= 1) {
