@@ -25,13 +25,14 @@
 //     as long for half the work).
 //   prep waves (4): for the next chunk meanwhile.  Phase 1: prep wave p stages
 //     token tile p (raw q, k in operand order; the state update reads its K^T
-//     operands from the same k tiles with transposing LDS reads) and
-//     the tile's norms, and the gates of all 64 tokens (every prep wave forms
-//     them; a wave-wide DPP scan gives the running sums).  Phase 2: five gram
-//     tiles per wave (K K^T and K Q^T scaled to -A and M, stored as bf16 hi/lo
-//     pairs) and the inverse of one diagonal block, (I + N)^-1 =
+//     operands from the same k tiles with transposing LDS reads) and the
+//     tile's norms (a token's pieces are one row of 16 lanes: DPP sums), the
+//     gates of all 64 tokens (every prep wave forms them; a wave-wide DPP scan
+//     gives the running sums) and the diagonal block p of A, which needs this
+//     tile only.  Phase 2: the inverse of that block, (I + N)^-1 =
 //     (I - N)(I + N^2)(I + N^4)(I + N^8) for the strictly lower 16x16 block N,
-//     on MFMA.
+//     on MFMA, and four more gram tiles (K K^T and K Q^T scaled to -A and M,
+//     stored as bf16 hi/lo pairs).
 // Two LDS buffers hold the chunk operands (chunk c read by the state waves,
 // chunk c+1 written by the prep waves); two barriers per chunk separate the
 // phases: [state: P, R, X | prep: stage c+1, its gates] [state: solve, O, S |
@@ -175,21 +176,24 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
     if (wave >= kSW) {
         // ============================================================ prep waves
         const int p = __builtin_amdgcn_readfirstlane(wave - kSW);
-        const int j = g;                          // piece group: keys 32 i + 8 j .. +7 of slice i
-        uint4 qreg[4], kreg[4];                   // token 16 p + r, slices 0..3, piece j
+        // staging: lane (u, jp) = (lane / 16, lane mod 16) takes piece jp (keys 8 jp .. 8 jp + 7) of token
+        // 16 p + 4 i + u in pass i, so a token's 16 pieces sit in one row of 16 lanes (DPP sums)
+        const int jp = lane & 15, u = lane >> 4;
+        uint4 qreg[4], kreg[4];
         // lane t: raw beta and raw alpha of token t, each in its own register (combining them at load
         // time would wait for the prefetch right away)
         uint32_t gbr = 0, gal = 0;
         float gbeta = 0.f, gG = 0.f;              // lane t: beta_t and G_t of the chunk staged last
-        const int qoff = ((16 * p + r) * C + hk * kDK + 8 * j) * 2;
+        f32x4_t gNa, gNb;                         // diagonal block p of A of the chunk staged last, A and B order
+        const int qoff = ((16 * p + u) * C + hk * kDK + 8 * jp) * 2;
         auto prefetch = [&](int c0) __attribute__((always_inline)) {
             const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(c0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                qreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        rq, qoff, __builtin_amdgcn_readfirstlane(64 * i), 0));
+                const int so = __builtin_amdgcn_readfirstlane(8 * i * C);   // 4 i tokens further
+                qreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, qoff, so, 0));
                 kreg[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        rq, qoff, __builtin_amdgcn_readfirstlane(64 * i + Hk * kDK * 2), 0));
+                                                        rq, qoff, __builtin_amdgcn_readfirstlane(so + Hk * kDK * 2), 0));
             }
             const int Lv = min(kL, T - c0);
             const size_t g0 = ((size_t)b * T + c0) * Hv;
@@ -202,36 +206,45 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             gal = __builtin_amdgcn_raw_buffer_load_b16(ra, goff, 0, 0);
         };
 
-        // phase 1: token tile p of the chunk at c0 into buffer x, and its norms
+        // raw gram tile of buffer x: lane (r, g) element e holds k_{16 kb + 4 g + e} . (q or k)_{16 ib + r}
+        auto gram = [&](const C64Chunk& x, int ib, int kb, bool ism) __attribute__((always_inline)) {
+            f32x4_t D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int rec = qk_rec(lane, m);
+                const bf16x8_t* xs = ism ? &x.qop[ib][m][0] : &x.kop[ib][m][0];
+                D = mfma32(x.kop[kb][m][rec], xs[rec], D);
+            }
+            return D;
+        };
+
+        // phase 1: token tile p of the chunk at c0 into buffer x, its norms, the gates of all tokens, and
+        // the diagonal block p of A (it needs this tile only)
         auto stage = [&](int c0, C64Chunk& x, bool mk) __attribute__((always_inline)) {
             const int Lv = min(kL, T - c0);
             if (mk) GDN_TLV(5, qreg[3].w);
-            const int t = 16 * p + r;
-            const int hf = j >> 1, g0 = (j & 1) << 1;
-            float sq = 0.f, sk = 0.f;
+            const int m = jp >> 2, hf = (jp & 3) >> 1, g0 = (jp & 1) << 1;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint4 q = qreg[i], k = kreg[i];
-                // keys 32 i + 8 j + 0..3 -> group g0 (slots 4 hf ..), keys + 4..7 -> group g0 + 1
-                char* qd = reinterpret_cast<char*>(&x.qop[p][i][0]) + 8 * hf;
-                char* kd = reinterpret_cast<char*>(&x.kop[p][i][0]) + 8 * hf;
-                const int r0 = qk_rec(r + 16 * g0, i) * 16, r1 = qk_rec(r + 16 * (g0 + 1), i) * 16;
+                const int row = 4 * i + u, t = 16 * p + row;
+                // keys 8 jp + 0..3 -> group g0 (slots 4 hf ..), keys + 4..7 -> group g0 + 1
+                char* qd = reinterpret_cast<char*>(&x.qop[p][m][0]) + 8 * hf;
+                char* kd = reinterpret_cast<char*>(&x.kop[p][m][0]) + 8 * hf;
+                const int r0 = qk_rec(row + 16 * g0, m) * 16, r1 = qk_rec(row + 16 * (g0 + 1), m) * 16;
                 *reinterpret_cast<uint2*>(qd + r0) = make_uint2(q.x, q.y);
                 *reinterpret_cast<uint2*>(qd + r1) = make_uint2(q.z, q.w);
                 *reinterpret_cast<uint2*>(kd + r0) = make_uint2(k.x, k.y);
                 *reinterpret_cast<uint2*>(kd + r1) = make_uint2(k.z, k.w);
-                sq = sq8(q, sq);
-                sk = sq8(k, sk);
+                // norms: the token's 16 pieces are one row of lanes
+                const float sq = group_sum<16>(sq8(q, 0.f)), sk = group_sum<16>(sq8(k, 0.f));
+                if (jp == 0) {
+                    const bool valid = t < Lv;
+                    sm.rk[t] = valid ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.f;
+                    sm.rq[t] = valid ? __builtin_amdgcn_rsqf(sq + a.eps) : 0.f;
+                }
             }
             if (mk) GDN_TL(6);
-            // the token's four piece groups are lanes r, r + 16, r + 32, r + 48
-            sq = sum_xor16_32(sq);
-            sk = sum_xor16_32(sk);
-            if (j == 0) {
-                const bool valid = t < Lv;
-                sm.rk[t] = valid ? __builtin_amdgcn_rsqf(sk + a.eps) : 0.f;
-                sm.rq[t] = valid ? __builtin_amdgcn_rsqf(sq + a.eps) : 0.f;
-            }
             if (mk) GDN_TL(7);
             // the gates (lane = token) and their running sum, from the raw bits loaded with the chunk
             // (the next prefetch overwrites them)
@@ -240,6 +253,26 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             gbeta = beta;
             gG = wave_scan(gg);
             if (mk) GDN_TLV(8, gG);
+            // the diagonal block p of A in both operand orders (its tokens, norms and gates are this
+            // wave's own)
+            if ((lane >> 4) == p) {
+                sm.Gv[p][lane] = gG;
+                sm.bk[p][lane] = gbeta * sm.rk[lane];
+            }
+            const f32x4_t D = gram(x, p, p, false);   // symmetric: k_{4g+e} . k_r of block p
+            const int t = 16 * p + r, s0 = 16 * p + 4 * g;
+            const float bkt = sm.bk[p][t], Gt = sm.Gv[p][t], rkr = sm.rk[t];
+            const float4 bks = lds_f4(&sm.bk[p][s0]), Gs = lds_f4(&sm.Gv[p][s0]), rks = lds_f4(&sm.rk[s0]);
+            const float bk4[4] = {bks.x, bks.y, bks.z, bks.w}, G4[4] = {Gs.x, Gs.y, Gs.z, Gs.w};
+            const float rk4[4] = {rks.x, rks.y, rks.z, rks.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int sc = 4 * g + e;
+                // A order: N[r][sc]; B order: N[sc][r]
+                gNa[e] = sc < r ? bkt * rk4[e] * __expf(fminf(Gt - G4[e], 0.f)) * D[e] : 0.f;
+                gNb[e] = r < sc ? bk4[e] * rkr * __expf(fminf(G4[e] - Gt, 0.f)) * D[e] : 0.f;
+            }
+            if (mk) GDN_TLV(10, gNb[0]);
         };
 
         // phase 2: the gate factors, this wave's gram tiles and its diagonal block's inverse, for
@@ -269,35 +302,9 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             }
 
             if (mk) GDN_TL(9);
-            // raw gram tile: lane (r, g) element e holds k_{16 kb + 4 g + e} . (q or k)_{16 ib + r}
-            auto gram = [&](int ib, int kb, bool ism) __attribute__((always_inline)) {
-                f32x4_t D = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int rec = qk_rec(lane, m);
-                    const bf16x8_t* xs = ism ? &x.qop[ib][m][0] : &x.kop[ib][m][0];
-                    D = mfma32(x.kop[kb][m][rec], xs[rec], D);
-                }
-                return D;
-            };
-
-            // the diagonal block p of A in both operand orders, and its inverse
+            // the inverse of the diagonal block p (formed at staging)
             {
-                const f32x4_t D = gram(p, p, false);   // symmetric: k_{4g+e} . k_r of block p
-                const int t = 16 * p + r, s0 = 16 * p + 4 * g;
-                const float bkt = sm.bk[p][t], Gt = sm.Gv[p][t], rkr = sm.rk[t];
-                const float4 bks = lds_f4(&sm.bk[p][s0]), Gs = lds_f4(&sm.Gv[p][s0]), rks = lds_f4(&sm.rk[s0]);
-                const float bk4[4] = {bks.x, bks.y, bks.z, bks.w}, G4[4] = {Gs.x, Gs.y, Gs.z, Gs.w};
-                const float rk4[4] = {rks.x, rks.y, rks.z, rks.w};
-                f32x4_t Na, Nb;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int s = 4 * g + e;
-                    // A order: N[r][s]; B order: N[s][r]
-                    Na[e] = s < r ? bkt * rk4[e] * __expf(fminf(Gt - G4[e], 0.f)) * D[e] : 0.f;
-                    Nb[e] = r < s ? bk4[e] * rkr * __expf(fminf(G4[e] - Gt, 0.f)) * D[e] : 0.f;
-                }
-                if (mk) GDN_TLV(10, Nb[0]);
+                const f32x4_t Na = gNa, Nb = gNb;
                 // (I + N)^-1 in A order is (I + M)^-1 of M = N^T in accumulator order:
                 // (I - M)(I + M^2)(I + M^4)(I + M^8), M^16 = 0.  The A order of M is N's B order and
                 // the B order of M is N's A order; a product's accumulator order is the B order of
@@ -332,7 +339,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
                 const int ent = kC64Tiles[4 * p + i];
                 const bool ism = ent & 1;
                 const int ib = (ent >> 1) & 3, kb = (ent >> 3) & 3;
-                const f32x4_t D = gram(ib, kb, ism);
+                const f32x4_t D = gram(x, ib, kb, ism);
                 // lane: row t of tile (ib, kb), columns s = 16 kb + 4 g + e
                 const int t = 16 * ib + r, s0 = 16 * kb + 4 * g;
                 float y[4];

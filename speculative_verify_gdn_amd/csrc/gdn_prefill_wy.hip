@@ -107,17 +107,6 @@ struct WySmem {
 template <int NS>
 __device__ __forceinline__ int kt_rec(int jt, int ms, int lane) { return jt * (NS * 64 + 1) + ms * 64 + lane; }
 
-// sum over each aligned group of N lanes (N = 4, 8 or 16), every lane gets it
-template <int N>
-__device__ __forceinline__ float group_sum(float v)
-{
-    v += dpp_mov<kDppQuadXor1>(v);
-    v += dpp_mov<kDppQuadXor2>(v);
-    if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
-    if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
-    return v;
-}
-
 // linear index of a gram tile other than the diagonal blocks of A ->
 // (M tile?, row block ib, column block kb): first the strictly lower A tiles
 // in row order, then the lower M tiles with the diagonal in row order

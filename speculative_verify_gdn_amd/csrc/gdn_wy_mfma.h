@@ -91,6 +91,17 @@ __device__ __forceinline__ f32x4_t mfma32(bf16x8_t a, bf16x8_t b, f32x4_t c)
 
 __device__ __forceinline__ float4 lds_f4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
+// sum over each aligned group of N lanes (N = 4, 8 or 16), every lane gets it
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v += dpp_mov<kDppQuadXor1>(v);
+    v += dpp_mov<kDppQuadXor2>(v);
+    if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
+    return v;
+}
+
 // acc + sum of squares of 8 bf16 (exact products, fp32 sums)
 __device__ __forceinline__ float sq8(const uint4 u, float acc)
 {
