@@ -157,6 +157,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
 {
     constexpr int OE = O_BF16 ? 2 : 4;
     __shared__ C64Smem sm;
+    GDN_TL_BEGIN();
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -402,6 +403,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             __syncthreads();
             if (it == 10) GDN_TL(4);
         }
+        GDN_TL_END();
         return;
     }
 
@@ -628,6 +630,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             for (int jt = 0; jt < 8; ++jt) store_f4<false>(sp + 16 * jt, S[jt][rt]);
         }
     }
+    GDN_TL_END();
 }
 
 }  // namespace

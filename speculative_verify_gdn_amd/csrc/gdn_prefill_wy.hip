@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
     constexpr int CPR = Sh::CPR, TPP = Sh::TPP, NP = Sh::NP;
     constexpr int OE = O_BF16 ? 2 : 4;
     __shared__ WySmem<DK, L> sm;
+    GDN_TL_BEGIN();
 
     const int tid = threadIdx.x;
     const int lane0 = tid & 63, wave = tid >> 6;
@@ -432,6 +433,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
             __syncthreads();
             if (it == 10) GDN_TL(4);
         }
+        GDN_TL_END();
         return;
     }
 
@@ -599,6 +601,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
 #pragma unroll
         for (int jt = 0; jt < JT; ++jt) store_f4<false>(sp + 16 * jt, S[jt]);
     }
+    GDN_TL_END();
 }
 
 template <int DK, int L, bool O_BF16>

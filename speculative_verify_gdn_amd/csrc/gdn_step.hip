@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
 
     GDN_TL(8);
     const int b = blockIdx.z;
-    const int gtid = threadIdx.x, g = gtid / kThreads;
+    const int gtid = threadIdx.x, g = __builtin_amdgcn_readfirstlane(gtid / kThreads);
     const int tid = gtid % kThreads, lane = tid & 63, wave = tid >> 6;
     // the previous window's accept length first: the start state and the history rows wait for
     // it.  It is read as a vector load (index zero, but lane-dependent: eps >= 0 is checked on the

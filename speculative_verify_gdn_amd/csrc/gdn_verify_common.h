@@ -19,7 +19,14 @@ __device__ __forceinline__ float group_sum(float v)
     v += dpp_mov<kDppQuadXor2>(v);
     if constexpr (N >= 8) v += dpp_mov<kDppRowHalfMirror>(v);
     if constexpr (N >= 16) v += dpp_mov<kDppRowMirror>(v);
-    if constexpr (N >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (N >= 32) {
+        // the two rows of 16 lanes exchanged in one VALU instruction (each row now holds its sum in
+        // every lane): the first result holds row 2m in both rows, the second row 2m+1, so their sum
+        // is row 2m + row 2m+1 in every lane, the same bits as v + partner in either row
+        const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    }
+    static_assert(N <= 32, "groups of at most 32 lanes");
     return v;
 }
 

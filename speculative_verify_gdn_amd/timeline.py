@@ -168,6 +168,14 @@ def main():
         out["entry_median_by_xcd"] = [round(float(np.nanmedian(ent[x::8])), 2) for x in range(8)]
         out["end_median_by_xcd"] = [round(float(np.nanmedian(end[x::8])), 2) for x in range(8)]
         out["last_end"] = round(float(np.nanmax(end)), 2)
+        # per wave role (waves 0-3 the first chunk's q|k conv, 4-6 the gates, 7-9 the v conv, 10-11
+        # none): the median of each mark before the first barrier
+        roles = (("conv0", slice(0, 4)), ("gates", slice(4, 7)), ("v", slice(7, 10)), ("idle", slice(10, 12)))
+        out["by_role"] = {}
+        for rn, ws in roles:
+            x = t[:, ws, :]
+            out["by_role"][rn] = {NAMES[k]: round(float(np.median((x[:, :, k][x[:, :, k] > 0] - t0) * 0.01)), 2)
+                                  for k in (5, 6, 7, 1, 2) if (x[:, :, k] > 0).any()}
         # per workgroup: from its first wave's entry to its last wave's end
         dur = end - ent
         out["workgroup_span"] = [round(float(q), 2) for q in (np.nanmin(dur), np.nanmedian(dur), np.nanmax(dur))]
