@@ -140,6 +140,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     using Smem = StepSmem<DK, KP, RPG>;
     __shared__ Smem sm;
 
+    GDN_TL_BEGIN();
     GDN_TL(8);
     const int b = blockIdx.z;
     const int gtid = threadIdx.x, g = __builtin_amdgcn_readfirstlane(gtid / kThreads);
@@ -472,6 +473,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
         }
     }
     GDN_TL(4);
+    GDN_TL_END();
 }
 
 template <int DK, int KMAX, bool O_BF16, bool CAPTURE, bool LIVE>
