@@ -58,12 +58,17 @@ __device__ __forceinline__ int head_of_row(int y, int Hv, int Hk, int gx)
 __device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo)
 {
     const bf16x2_t hb = {(__bf16)x0, (__bf16)x1};
-    const uint32_t hu = __builtin_bit_cast(uint32_t, hb);
+    uint32_t hu = __builtin_bit_cast(uint32_t, hb);
+    // both packed words opaque: otherwise the compiler converts each value on its own (a convert with a
+    // zero partner per value, then a byte permute to pack them), 8 instructions a pair instead of 6
+    asm("" : "+v"(hu));
     const float r0 = x0 - __uint_as_float(hu << 16);
     const float r1 = x1 - __uint_as_float(hu & 0xffff0000u);
     const bf16x2_t lb = {(__bf16)r0, (__bf16)r1};
+    uint32_t lu = __builtin_bit_cast(uint32_t, lb);
+    asm("" : "+v"(lu));
     hi = hu;
-    lo = __builtin_bit_cast(uint32_t, lb);
+    lo = lu;
 }
 
 __device__ __forceinline__ void split4(const f32x4_t x, uint2& hi, uint2& lo)
