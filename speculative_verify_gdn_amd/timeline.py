@@ -9,7 +9,8 @@ csrc/gdn_timeline.h) and runs the step chained over buffer sets as bench.py
 does (set r continues from set r-1's window; the sets together exceed the
 Infinity Cache).  After warm-up, each measured launch runs alone: the marks
 are cleared, one step is launched and synchronised, and the marks are read.
-Marks (lane 0 of every wave, 100 MHz real-time counter):
+Marks (every wave, 100 MHz real-time counter; a wave keeps its marks in registers and writes
+them once at its end, so the marks add no memory operations to the waits they measure):
   8 entry      the wave's first instruction (before the kernel arguments are read)
   0 start      the accept-length load issued
   5 accept     the accept length has arrived
@@ -21,7 +22,9 @@ Marks (lane 0 of every wave, 100 MHz real-time counter):
   4 end        the wave's last store issued
 Printed: one JSON line per launch with [min, p10, median, p90, max] of every
 mark in microseconds after the launch's earliest entry, the median entry and
-end per XCD (workgroup index mod 8) and the end of the slowest wave.
+end per XCD (workgroup index mod 8), the end of the slowest wave, and per wave
+role (waves 0-3 the first chunk's q|k conv, 4-6 the gates, 7-9 the v conv,
+10-11 none) the medians of the marks before the first barrier.
 
 With --workload prefill the marks are those of gdn_prefill_chunked's eleventh chunk
 (chunk index 10) in every workgroup (the dk = 128, chunk 64 kernel), for the 4 state
