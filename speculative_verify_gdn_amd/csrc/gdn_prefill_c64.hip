@@ -37,7 +37,10 @@
 // chunk c+1 written by the prep waves); two barriers per chunk separate the
 // phases: [state: P, R, X | prep: stage c+1, its gates] [state: solve, O, S |
 // prep: grams and inverses of c+1].  The v values go straight from memory into
-// the state waves' registers, a chunk ahead.
+// the state waves' registers, a chunk ahead.  The prep waves run at a higher
+// wave priority: each SIMD holds one wave of each role, the preparation was the
+// longer of the two in both phases, and its instructions now go first whenever
+// both waves are ready.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_timeline.h"
