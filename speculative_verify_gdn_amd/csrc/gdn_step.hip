@@ -143,6 +143,14 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     GDN_TL_BEGIN();
     GDN_TL(8);
     const int b = blockIdx.z;
+    // the row blocks of one group of value heads on one XCD (workgroup i runs on XCD i mod 8): they
+    // share the key head's q|k rows and taps through that XCD's L2
+    int bx = blockIdx.x, by = blockIdx.y;
+    if ((gridDim.y & 7) == 0) {
+        const int wi = blockIdx.x + gridDim.x * blockIdx.y, slot = wi >> 3;
+        by = (wi & 7) + 8 * (slot / gridDim.x);
+        bx = slot % gridDim.x;
+    }
     const int gtid = threadIdx.x, g = __builtin_amdgcn_readfirstlane(gtid / kThreads);
     const int tid = gtid % kThreads, lane = tid & 63, wave = tid >> 6;
     // the previous window's accept length first: the start state and the history rows wait for
@@ -156,9 +164,9 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     const int gw = gtid >> 6;                    // wave of the workgroup, 0..11
     const int j = lane % LPR, c = 4 * j;
     const int rloc = wave * RPW + lane / LPR;
-    const int h = blockIdx.y * kGroups + g;
+    const int h = by * kGroups + g;
     static_assert(RB == 1 || (CAPTURE && LIVE), "several row blocks per workgroup need capture and live rows");
-    const int blk0 = blockIdx.x * RB;            // the workgroup's first row block
+    const int blk0 = bx * RB;                    // the workgroup's first row block
     const int i = blk0 * RPG + rloc;             // this lane's row in the first block
     const int K = a.K, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
     const bool live = LIVE || i < dv;
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x) + (size_t)b * K * C;
     const uint16_t* HS0 = reinterpret_cast<const uint16_t*>(a.hsrc) + (size_t)b * a.hrows * C;
     // one workgroup per key head writes the q|k window rows and conv outputs
-    const bool qk_writer = blockIdx.x == 0 && (blockIdx.y * kGroups) % (Hv / Hk) == 0;
+    const bool qk_writer = bx == 0 && (by * kGroups) % (Hv / Hk) == 0;
 
     // roles: waves 0..3 convolve chunk 0's q|k items (tokens 0 and 1); waves 4..6 form the gates of
     // head rg = gw - 4 and waves 7..9 the v conv of head rg = gw - 7's rows (waves of the
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     const bool gate_wave = gw >= 4 && gw < 4 + kGroups;
     const bool v_wave = gw >= 7 && gw < 7 + kGroups;
     const int rg = gate_wave ? gw - 4 : (v_wave ? gw - 7 : g);   // the head of the role
-    const int hr = blockIdx.y * kGroups + rg;
+    const int hr = by * kGroups + rg;
 
     // ---- loads that do not depend on the accept length
     // conv item of this lane: slot q of every chunk (token chunk_start(cc) + q/2; q even: q, odd: k;
