@@ -151,6 +151,8 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
         by = (wi & 7) + 8 * (slot / gridDim.x);
         bx = slot % gridDim.x;
     }
+    // the wave's value head (uniform: the checkpoint's buffer resource, built from it, is then a scalar
+    // one; otherwise the compiler wraps each checkpoint store in a loop over the lanes' resources)
     const int gtid = threadIdx.x, g = __builtin_amdgcn_readfirstlane(gtid / kThreads);
     const int tid = gtid % kThreads, lane = tid & 63, wave = tid >> 6;
     // the previous window's accept length first: the start state and the history rows wait for
