@@ -46,7 +46,13 @@
  *     argument returns a negative code, launches nothing and leaves every
  *     buffer untouched.  gdn_last_error() gives a message (thread-local).
  *   - B == 0 is a valid empty call: GDN_OK, nothing launched.
- *   - Thread-safe: the only global state is the thread-local error message.
+ *   - Thread-safe: the only global state is the thread-local error message
+ *     (and, in the debug build only, the device-side count read by
+ *     gdn_debug_clamped_accepts).
+ *   - Accept lengths outside the range of the window they refer to are
+ *     clamped into it by the kernels (the rollback to an accepted prefix:
+ *     strix-llama.cpp PR #14, commit messages on recurrent snapshot rollback);
+ *     the debug build also counts them.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -73,6 +79,20 @@ int gdn_version(void);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *gdn_last_error(void);
+
+/*
+ * gdn_debug_clamped_accepts -- debug build only (libgdn_debug.so, compiled
+ * with GDN_DEBUG): the number of accept lengths that kernels of this library
+ * found outside 0..K of their window and clamped, on the current device,
+ * since the library was loaded or last reset -- one count per sequence and
+ * call of gdn_rollback(_ex), gdn_rollback_conv_step, gdn_replay and
+ * gdn_verify_step (accept_prev).  Reads device memory, so it waits for the
+ * device's work to finish: for tests and debugging, not a serving loop.
+ *   count  host pointer, receives the count
+ *   reset  non-zero: the count is set to zero after it is read
+ * The release build (libgdn.so) counts nothing and returns GDN_EUNSUPPORTED.
+ */
+int gdn_debug_clamped_accepts(long long *count, int reset);
 
 /*
  * gdn_conv_step -- fused causal depthwise conv1d decode / verify step.

@@ -1,11 +1,14 @@
 """Build libgdn.so (the HIP library behind include/gdn.h) for gfx950.
 
-    python -m speculative_verify_gdn_amd.build [--timeline]
+    python -m speculative_verify_gdn_amd.build [--timeline | --debug]
 
 --timeline builds libgdn_timeline.so instead: the same library with the
 wall-clock marks of csrc/gdn_timeline.h compiled into the fused verify step
 (-DGDN_TIMELINE, objects in _build_timeline/), read back by
 speculative_verify_gdn_amd/timeline.py.  The product library never has them.
+--debug builds libgdn_debug.so (-DGDN_DEBUG, objects in _build_debug/): the
+same library with the count of clamped accept lengths of csrc/gdn_debug.h,
+read by gdn_debug_clamped_accepts.
 
 Each .hip file under csrc/ is compiled to an object in _build/ (in parallel),
 then linked into speculative_verify_gdn_amd/libgdn.so.  Flags:
@@ -65,11 +68,14 @@ def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, timeline: bool = False) -> str:
-    """Compile every HIP source and link libgdn.so (or, with timeline, libgdn_timeline.so); returns its path."""
-    build_dir = os.path.join(PKG, "_build_timeline") if timeline else BUILD
-    lib = os.path.join(PKG, "libgdn_timeline.so") if timeline else LIB
-    extra = ("-DGDN_TIMELINE",) if timeline else ()
+def build(verbose: bool = False, timeline: bool = False, debug: bool = False) -> str:
+    """Compile every HIP source and link libgdn.so (with timeline libgdn_timeline.so, with debug
+    libgdn_debug.so); returns its path."""
+    assert not (timeline and debug), "one variant at a time"
+    variant = "_timeline" if timeline else ("_debug" if debug else "")
+    build_dir = os.path.join(PKG, "_build" + variant)
+    lib = os.path.join(PKG, "libgdn%s.so" % variant)
+    extra = ("-DGDN_TIMELINE",) if timeline else (("-DGDN_DEBUG",) if debug else ())
     os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")), key=lambda f: -os.path.getsize(f))  # largest first
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
@@ -86,5 +92,5 @@ def build(verbose: bool = False, timeline: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True, timeline="--timeline" in sys.argv[1:])
+    build(verbose=True, timeline="--timeline" in sys.argv[1:], debug="--debug" in sys.argv[1:])
     sys.exit(0)

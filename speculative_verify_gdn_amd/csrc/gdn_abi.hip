@@ -87,6 +87,33 @@ int gdn_version(void) { return GDN_VERSION; }
 
 const char* gdn_last_error(void) { return g_err; }
 
+int gdn_debug_clamped_accepts(long long* count, int reset)
+{
+    const char* fn = "gdn_debug_clamped_accepts";
+#ifdef GDN_DEBUG
+    REQUIRE(count, GDN_EINVAL, "%s: null count", fn);
+    // one counter per translation unit that clamps accept lengths
+    hipError_t (*const readers[])(unsigned long long*, bool) = {
+        gdn::clamped_accepts_rollback,          gdn::clamped_accepts_conv,
+        gdn::clamped_accepts_step,              gdn::clamped_accepts_verify_bf16_bf16,
+        gdn::clamped_accepts_verify_bf16_f32,   gdn::clamped_accepts_verify_f32_bf16,
+        gdn::clamped_accepts_verify_f32_f32};
+    unsigned long long total = 0;
+    for (auto rd : readers) {
+        unsigned long long n = 0;
+        const hipError_t e = rd(&n, reset != 0);
+        if (e != hipSuccess) return fail(GDN_EHIP, "%s: %s", fn, hipGetErrorString(e));
+        total += n;
+    }
+    *count = (long long)total;
+    return ok();
+#else
+    (void)count;
+    (void)reset;
+    return fail(GDN_EUNSUPPORTED, "%s: counted only in the debug build (libgdn_debug.so)", fn);
+#endif
+}
+
 int gdn_conv_step(const void* x, const float* w, void* hist, void* y, void* win_out, int B, int T, int C, int W,
                   int io_dtype, void* stream)
 {

@@ -22,6 +22,7 @@
 // threads of that tile that rewrite the history load their new rows first,
 // wait at a workgroup barrier for every read of the old history, then store.
 #include "gdn_conv_math.h"
+#include "gdn_debug.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(kThreads) void rollback_conv_kernel(RollConvArgs a,
 {
     const int b = blockIdx.y;
     int acc = a.accept[b];
+    GDN_COUNT_CLAMP(blockIdx.x == 0 && threadIdx.x == 0 && (acc < 0 || acc > a.Kp));
     acc = acc < 0 ? 0 : (acc > a.Kp ? a.Kp : acc);
 
     if ((int)blockIdx.x < state_blocks) {
@@ -377,3 +379,5 @@ hipError_t launch_conv_tree(const ConvTreeArgs& a, bool bf16, hipStream_t s)
 }
 
 }  // namespace gdn
+
+GDN_CLAMP_READER(clamped_accepts_conv)

@@ -132,4 +132,15 @@ hipError_t launch_prefill_c64(const PrefillArgs& a, bool o_bf16, hipStream_t s);
 hipError_t launch_conv_tree(const ConvTreeArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_tree_rollback(const TreeRollbackArgs& a, hipStream_t s);
 
+#ifdef GDN_DEBUG
+// the debug build's counts of clamped accept lengths, one per translation unit (gdn_debug.h)
+hipError_t clamped_accepts_rollback(unsigned long long* n, bool reset);
+hipError_t clamped_accepts_conv(unsigned long long* n, bool reset);
+hipError_t clamped_accepts_step(unsigned long long* n, bool reset);
+hipError_t clamped_accepts_verify_bf16_bf16(unsigned long long* n, bool reset);
+hipError_t clamped_accepts_verify_bf16_f32(unsigned long long* n, bool reset);
+hipError_t clamped_accepts_verify_f32_bf16(unsigned long long* n, bool reset);
+hipError_t clamped_accepts_verify_f32_f32(unsigned long long* n, bool reset);
+#endif
+
 }  // namespace gdn

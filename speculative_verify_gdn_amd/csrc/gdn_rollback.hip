@@ -15,6 +15,7 @@
 // sequence.  State workgroups of sequences with a == K return at once; the conv
 // rows are copied for every a (for a == K they already hold win[K..] after an
 // in-place conv step, so the copy is a no-op there).
+#include "gdn_debug.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -30,6 +31,8 @@ __global__ __launch_bounds__(kThreads) void rollback_kernel(RollbackArgs a, int 
     const int Kb = a.K;                                        // window of the buffers
     const int K = a.lens ? min(max(a.lens[b], 1), Kb) : Kb;   // this sequence's window
     int acc = a.accept[b];
+    // (the replay's launch has no state blocks: its verify launch counts)
+    GDN_COUNT_CLAMP(state_blocks > 0 && blockIdx.x == 0 && threadIdx.x == 0 && (acc < 0 || acc > K));
     acc = acc < 0 ? 0 : (acc > K ? K : acc);
 
     if ((int)blockIdx.x < state_blocks) {
@@ -185,3 +188,5 @@ hipError_t launch_rollback(const RollbackArgs& a, hipStream_t s)
 }
 
 }  // namespace gdn
+
+GDN_CLAMP_READER(clamped_accepts_rollback)

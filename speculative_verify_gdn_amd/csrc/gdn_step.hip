@@ -43,6 +43,7 @@
 // at kernel start every wave of the chip loads at once, and the number of load
 // instructions sets how long the round trips take.
 #include "gdn_conv_math.h"
+#include "gdn_debug.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_timeline.h"
@@ -246,7 +247,9 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(VerifyArgs a)
     }
 
     // ---- the start state and the rows that the accept length picks
-    const int ap = a.acc_prev ? min(max(__builtin_amdgcn_readfirstlane(ap_raw), 0), a.Kp) : 0;
+    const int ap_u = __builtin_amdgcn_readfirstlane(ap_raw);
+    GDN_COUNT_CLAMP(a.acc_prev && gtid == 0 && blockIdx.x == 0 && blockIdx.y == 0 && (ap_u < 0 || ap_u > a.Kp));
+    const int ap = a.acc_prev ? min(max(ap_u, 0), a.Kp) : 0;
     GDN_TLV(5, ap);
     const float* Sh;
     if (a.acc_prev)
@@ -552,6 +555,8 @@ hipError_t launch_step(const VerifyArgs& a, bool in_bf16, bool o_bf16, hipStream
 }
 
 }  // namespace gdn
+
+GDN_CLAMP_READER(clamped_accepts_step)
 
 #ifdef GDN_TIMELINE
 // the marks of the last launches: [workgroup][wave][mark] 100 MHz counter values (0: not reached)

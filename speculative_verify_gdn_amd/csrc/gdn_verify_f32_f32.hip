@@ -7,3 +7,5 @@ namespace gdn {
 hipError_t launch_verify_f32_f32(const VerifyArgs& a, hipStream_t s) { return launch_io<false, false>(a, s); }
 
 }  // namespace gdn
+
+GDN_CLAMP_READER(clamped_accepts_verify_f32_f32)

@@ -56,6 +56,7 @@
 #pragma once
 
 #include "gdn_conv_math.h"
+#include "gdn_debug.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_verify_common.h"
@@ -186,7 +187,9 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     if (a.replay) {
         // replay of the accepted prefix from the checkpoint S_in: nothing to do when the
         // whole window was kept (S_out holds its final state), a copy when none was
-        const int acc = min(max(a.replay[b], 0), Kb);
+        const int acc_raw = a.replay[b];
+        GDN_COUNT_CLAMP(threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && (acc_raw < 0 || acc_raw > Kb));
+        const int acc = min(max(acc_raw, 0), Kb);
         if (acc >= Kb) return;
         if (acc == 0) {
             const int rl = blockIdx.x * RPG + wave * RPW + lane / LPR;
@@ -220,7 +223,9 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
         if constexpr (STEP) {
             int ap = 0;
             if (a.acc_prev) {
-                ap = min(max(a.acc_prev[b], 0), a.Kp);
+                const int ap_raw = a.acc_prev[b];
+                GDN_COUNT_CLAMP(threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0 && (ap_raw < 0 || ap_raw > a.Kp));
+                ap = min(max(ap_raw, 0), a.Kp);
                 const size_t hb = ((size_t)b * Hv + h) * SD;
                 Sh = ap == 0 ? a.Sp_ckpt + hb
                              : (ap == a.Kp ? a.Sp_out + hb : a.Sp_H + (((size_t)b * (a.Kp - 1) + ap - 1) * Hv + h) * SD);

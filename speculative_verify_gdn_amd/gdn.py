@@ -9,6 +9,7 @@ call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -17,12 +18,15 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("GDN_LIB", os.path.join(_PKG, "libgdn.so"))
+# the debug build (also counts clamped accept lengths: debug_clamped_accepts)
+DEBUG_LIB_PATH = os.path.join(_PKG, "libgdn_debug.so")
 
 GDN_OK, GDN_EINVAL, GDN_EUNSUPPORTED, GDN_EHIP = 0, -1, -2, -3
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked",
            "gdn_rollback_conv_step", "gdn_conv_step_ex", "gdn_verify_ex", "gdn_rollback_ex", "gdn_replay",
-           "gdn_conv_tree", "gdn_verify_tree", "gdn_rollback_tree", "gdn_verify_step")
+           "gdn_conv_tree", "gdn_verify_tree", "gdn_rollback_tree", "gdn_verify_step",
+           "gdn_debug_clamped_accepts")
 
 
 class GdnError(RuntimeError):
@@ -33,44 +37,74 @@ class GdnError(RuntimeError):
 
 _lib = None
 _lock = threading.Lock()
+_using = threading.local()
 
 
 def load(path: str = LIB_PATH):
     """Load libgdn.so (once) and declare the C signatures."""
     global _lib
     with _lock:
-        if _lib is not None:
-            return _lib
-        if not os.path.exists(path):
-            raise FileNotFoundError("libgdn.so not built (%s); run python -m speculative_verify_gdn_amd.build"
-                                    % path)
-        lib = ctypes.CDLL(path)
-        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-        lib.gdn_version.restype = I
-        lib.gdn_last_error.restype = ctypes.c_char_p
-        lib.gdn_conv_step.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
-        lib.gdn_verify.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
-        lib.gdn_rollback.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
-        lib.gdn_prefill_chunked.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P]
-        lib.gdn_rollback_conv_step.argtypes = [P, I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
-        lib.gdn_conv_step_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
-        lib.gdn_verify_ex.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
-        lib.gdn_rollback_ex.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
-        lib.gdn_replay.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
-        lib.gdn_verify_step.argtypes = [P, I, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P,
-                                        I, I, I, I, I, I, I, I, I, F, P]
-        lib.gdn_conv_tree.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
-        lib.gdn_verify_tree.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
-        lib.gdn_rollback_tree.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
-        for name in EXPORTS:
-            getattr(lib, name).restype = ctypes.c_char_p if name == "gdn_last_error" else I
-        _lib = lib
-        return lib
+        if _lib is None:
+            _lib = open_library(path)
+        return _lib
+
+
+def _L():
+    """The library the calls of this thread go to: load()'s, or the one a `using` block names."""
+    lib = getattr(_using, "lib", None)
+    return lib if lib is not None else load()
+
+
+@contextlib.contextmanager
+def using(lib):
+    """Route this thread's calls to another build of the library (e.g. open_library(DEBUG_LIB_PATH))."""
+    prev = getattr(_using, "lib", None)
+    _using.lib = lib
+    try:
+        yield lib
+    finally:
+        _using.lib = prev
+
+
+def debug_clamped_accepts(reset: bool = False) -> int:
+    """gdn_debug_clamped_accepts: clamped accept lengths counted by the debug build (raises GdnError
+    GDN_EUNSUPPORTED on the release build)."""
+    n = ctypes.c_longlong(0)
+    _check(_L().gdn_debug_clamped_accepts(ctypes.byref(n), int(bool(reset))))
+    return n.value
+
+
+def open_library(path: str):
+    """Open a build of libgdn at `path` and declare the C signatures (no caching)."""
+    if not os.path.exists(path):
+        raise FileNotFoundError("libgdn not built (%s); run python -m speculative_verify_gdn_amd.build" % path)
+    lib = ctypes.CDLL(path)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.gdn_version.restype = I
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    lib.gdn_conv_step.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+    lib.gdn_verify.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    lib.gdn_rollback.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.gdn_prefill_chunked.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, P]
+    lib.gdn_rollback_conv_step.argtypes = [P, I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.gdn_conv_step_ex.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P]
+    lib.gdn_verify_ex.argtypes = [P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    lib.gdn_rollback_ex.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.gdn_replay.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    lib.gdn_verify_step.argtypes = [P, I, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P, P,
+                                    I, I, I, I, I, I, I, I, I, F, P]
+    lib.gdn_conv_tree.argtypes = [P, P, P, P, P, I, I, I, I, I, P]
+    lib.gdn_verify_tree.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
+    lib.gdn_rollback_tree.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.gdn_debug_clamped_accepts.argtypes = [P, I]
+    for name in EXPORTS:
+        getattr(lib, name).restype = ctypes.c_char_p if name == "gdn_last_error" else I
+    return lib
 
 
 def _check(rc: int):
     if rc != GDN_OK:
-        raise GdnError(rc, load().gdn_last_error().decode())
+        raise GdnError(rc, _L().gdn_last_error().decode())
 
 
 def _p(t):
@@ -101,7 +135,7 @@ def _dev(*ts):
 
 
 def version() -> int:
-    return load().gdn_version()
+    return _L().gdn_version()
 
 
 def conv_step(x, w, hist, y, win=None, lens=None, stream=None):
@@ -110,7 +144,7 @@ def conv_step(x, w, hist, y, win=None, lens=None, stream=None):
     _dev(x, w, hist, y, win, lens)
     B, T, C = x.shape
     W = w.shape[1]
-    _check(load().gdn_conv_step_ex(_p(x), _p(w), _p(hist), _p(y), _p(win), _p(lens), B, T, C, W, _dtype(x),
+    _check(_L().gdn_conv_step_ex(_p(x), _p(w), _p(hist), _p(y), _p(win), _p(lens), B, T, C, W, _dtype(x),
                                    _stream(stream)))
 
 
@@ -127,7 +161,7 @@ def verify(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, H, o, Hk, eps=1e-6
     B, K, _ = qkv.shape
     _, Hv, dv, dk = S_in.shape
     gs = Hv if gate_stride is None else int(gate_stride)
-    _check(load().gdn_verify_ex(_p(qkv), _p(beta_raw), _p(alpha), gs, _p(dt_bias), _p(A_log), _p(S_in),
+    _check(_L().gdn_verify_ex(_p(qkv), _p(beta_raw), _p(alpha), gs, _p(dt_bias), _p(A_log), _p(S_in),
                                 _p(S_out), _p(H), _p(o), _p(lens), B, K, Hk, Hv, dk, dv, _dtype(qkv), _dtype(o),
                                 float(eps), _stream(stream)))
 
@@ -143,7 +177,7 @@ def rollback(accept, K, S_in, H, S_out, hist=None, win=None, lens=None, stream=N
         io = _dtype(hist)
     else:
         W, C, io = 2, 1, GDN_F32
-    _check(load().gdn_rollback_ex(_p(accept), _p(lens), int(K), _p(S_in), _p(H), _p(S_out), _p(hist), _p(win),
+    _check(_L().gdn_rollback_ex(_p(accept), _p(lens), int(K), _p(S_in), _p(H), _p(S_out), _p(hist), _p(win),
                                   B, Hv, dv, dk, C, W, io, _stream(stream)))
 
 
@@ -154,7 +188,7 @@ def rollback_conv_step(accept, K_prev, S_in, H, S_out, win_prev, x, w, hist, y, 
     B, Hv, dv, dk = S_in.shape
     _, T, C = x.shape
     W = w.shape[1]
-    _check(load().gdn_rollback_conv_step(_p(accept), int(K_prev), _p(S_in), _p(H), _p(S_out), _p(win_prev), _p(x),
+    _check(_L().gdn_rollback_conv_step(_p(accept), int(K_prev), _p(S_in), _p(H), _p(S_out), _p(win_prev), _p(x),
                                          _p(w), _p(hist), _p(y), _p(win), B, Hv, dv, dk, T, C, W, _dtype(x),
                                          _stream(stream)))
 
@@ -167,7 +201,7 @@ def replay(accept, qkv, beta_raw, alpha, dt_bias, A_log, S_ckpt, S_out, Hk, hist
     B, K, _ = qkv.shape
     _, Hv, dv, dk = S_ckpt.shape
     W = hist.shape[1] + 1 if hist is not None else 2
-    _check(load().gdn_replay(_p(accept), _p(qkv), _p(beta_raw), _p(alpha), Hv, _p(dt_bias), _p(A_log), _p(S_ckpt),
+    _check(_L().gdn_replay(_p(accept), _p(qkv), _p(beta_raw), _p(alpha), Hv, _p(dt_bias), _p(A_log), _p(S_ckpt),
                              _p(S_out), _p(hist), _p(win), B, K, Hk, Hv, dk, dv, W, _dtype(qkv), float(eps),
                              _stream(stream)))
 
@@ -177,7 +211,7 @@ def prefill_chunked(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, o, Hk, ch
     _dev(qkv, beta_raw, alpha, dt_bias, A_log, S_in, S_out, o)
     B, T, _ = qkv.shape
     _, Hv, dv, dk = S_in.shape
-    _check(load().gdn_prefill_chunked(_p(qkv), _p(beta_raw), _p(alpha), _p(dt_bias), _p(A_log), _p(S_in),
+    _check(_L().gdn_prefill_chunked(_p(qkv), _p(beta_raw), _p(alpha), _p(dt_bias), _p(A_log), _p(S_in),
                                       _p(S_out), _p(o), B, T, int(chunk), Hk, Hv, dk, dv, _dtype(qkv), _dtype(o),
                                       float(eps), _stream(stream)))
 
@@ -187,7 +221,7 @@ def conv_tree(x, w, hist, parent, y, stream=None):
     _dev(x, w, hist, parent, y)
     B, N, C = x.shape
     W = w.shape[1]
-    _check(load().gdn_conv_tree(_p(x), _p(w), _p(hist), _p(parent), _p(y), B, N, C, W, _dtype(x), _stream(stream)))
+    _check(_L().gdn_conv_tree(_p(x), _p(w), _p(hist), _p(parent), _p(y), B, N, C, W, _dtype(x), _stream(stream)))
 
 
 def verify_tree(qkv, beta_raw, alpha, dt_bias, A_log, parent, S_in, H, o, Hk, eps=1e-6, gate_stride=None,
@@ -202,7 +236,7 @@ def verify_tree(qkv, beta_raw, alpha, dt_bias, A_log, parent, S_in, H, o, Hk, ep
     _dev(qkv, dt_bias, A_log, parent, S_in, H, o)
     B, N, _ = qkv.shape
     _, Hv, dv, dk = S_in.shape
-    _check(load().gdn_verify_tree(_p(qkv), _p(beta_raw), _p(alpha), int(gate_stride), _p(dt_bias), _p(A_log),
+    _check(_L().gdn_verify_tree(_p(qkv), _p(beta_raw), _p(alpha), int(gate_stride), _p(dt_bias), _p(A_log),
                                   _p(parent), _p(S_in), _p(H), _p(o), B, N, Hk, Hv, dk, dv, _dtype(qkv), _dtype(o),
                                   float(eps), _stream(stream)))
 
@@ -217,7 +251,7 @@ def rollback_tree(node, parent, S_in, H, S_out, x=None, hist=None, stream=None):
         W, C, io = hist.shape[1] + 1, hist.shape[2], _dtype(hist)
     else:
         W, C, io = 2, 1, GDN_F32
-    _check(load().gdn_rollback_tree(_p(node), _p(parent), N, _p(S_in), _p(H), _p(S_out), _p(x), _p(hist),
+    _check(_L().gdn_rollback_tree(_p(node), _p(parent), N, _p(S_in), _p(H), _p(S_out), _p(x), _p(hist),
                                     B, Hv, dv, dk, C, W, io, _stream(stream)))
 
 
@@ -244,7 +278,7 @@ def verify_step(x, w, beta_raw, alpha, dt_bias, A_log, S_out, H, o, Hk, prev=Non
     else:
         acc = p_ckpt = p_H = p_out = p_win = None
         K_prev = 0
-    _check(load().gdn_verify_step(_p(acc), int(K_prev), _p(p_ckpt), _p(p_H), _p(p_out), _p(p_win), _p(S_in),
+    _check(_L().gdn_verify_step(_p(acc), int(K_prev), _p(p_ckpt), _p(p_H), _p(p_out), _p(p_win), _p(S_in),
                                   _p(hist), _p(x), _p(w), _p(beta_raw), _p(alpha), int(gate_stride), _p(dt_bias),
                                   _p(A_log), _p(S_ckpt), _p(S_out), _p(H), _p(o), _p(y), _p(win), B, K, Hk, Hv, dk,
                                   dv, W, _dtype(x), _dtype(o), float(eps), _stream(stream)))

@@ -46,6 +46,25 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(declared_functions()) <= exported
 
 
+def test_debug_library_exports_every_declared_symbol():
+    if not os.path.exists(gdn.DEBUG_LIB_PATH):
+        pytest.skip("libgdn_debug.so not built")
+    dbg = gdn.open_library(gdn.DEBUG_LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(dbg, name), name
+    # a null count is rejected on the host (no device access)
+    assert dbg.gdn_debug_clamped_accepts(None, 0) == gdn.GDN_EINVAL
+
+
+def test_release_library_counts_no_clamped_accepts(lib):
+    n = ctypes.c_longlong(-1)
+    assert lib.gdn_debug_clamped_accepts(ctypes.byref(n), 0) == gdn.GDN_EUNSUPPORTED
+    assert n.value == -1
+    assert b"debug build" in lib.gdn_last_error()
+    with pytest.raises(gdn.GdnError):
+        gdn.debug_clamped_accepts()
+
+
 def test_version_matches_header(lib):
     m = re.search(r"#define GDN_VERSION (\d+)", open(HEADER).read())
     assert lib.gdn_version() == int(m.group(1))
