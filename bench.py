@@ -42,10 +42,10 @@ sys.path.insert(0, ROOT)
 METRIC = "GDN verify tokens/s per layer (K=16) + achieved HBM GB/s vs peak"
 # the sources of the step's kernel (gdn_verify_step on bf16 slabs); the committed counter profile of
 # the kernel is used only while they hash to the value recorded with it
-STEP_SOURCES = ("gdn_step.hip", "gdn_verify_common.h", "gdn_device.h", "gdn_conv_math.h", "gdn_timeline.h")
+STEP_SOURCES = ("gdn_step.hip", "gdn_verify_common.h", "gdn_device.h", "gdn_conv_math.h", "gdn_timeline.h", "gdn_debug.h")
 # the sources of gdn_verify with bf16 in and bf16 o (the instance the bench times)
 VERIFY_SOURCES = ("gdn_verify_impl.h", "gdn_verify_bf16_bf16.hip", "gdn_verify_common.h", "gdn_device.h",
-                  "gdn_conv_math.h", "gdn_timeline.h")
+                  "gdn_conv_math.h", "gdn_timeline.h", "gdn_debug.h")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 O_DTYPE = [None]               # torch dtype of o, set in main (bf16 unless --o-f32)
 MALL_BYTES = 256 * 2 ** 20     # Infinity Cache
