@@ -24,7 +24,7 @@ the launch stream around graph-replayed back-to-back launches of that kernel
 alone; the measured device-copy rate beside the published peak), and the CPU
 oracle timed on the host as a baseline (one thread and all usable cores).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials 5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials 20]
 """
 from __future__ import annotations
 
@@ -505,7 +505,7 @@ def main():
     ap.add_argument("--three-kernel", action="store_true",
                     help="step as conv_step -> verify -> rollback (three launches) instead of "
                          "rollback_conv_step -> verify")
-    ap.add_argument("--trials", type=int, default=5,
+    ap.add_argument("--trials", type=int, default=20,
                     help="timed trials of K steps each; the median trial is reported, with min and max")
     ap.add_argument("--settle-ms", type=float, default=50.0,
                     help="after the W warm-up steps, replay the step for at least this long (untimed) so the "

@@ -495,9 +495,9 @@ hipError_t launch_rb(const VerifyArgs& a, int rb, hipStream_t s)
     constexpr int RPG = kWaves * (64 / (DK / 4));
     const dim3 block(kStepThreads);
     if constexpr (CAPTURE && LIVE && KMAX <= 16) {
-        if (rb == 4) {
-            const dim3 grid((a.dv + 4 * RPG - 1) / (4 * RPG), a.Hv / kGroups, a.B);
-            step_kernel<DK, KMAX, O_BF16, CAPTURE, LIVE, 4><<<grid, block, 0, s>>>(a);
+        if (rb == 2) {
+            const dim3 grid((a.dv + 2 * RPG - 1) / (2 * RPG), a.Hv / kGroups, a.B);
+            step_kernel<DK, KMAX, O_BF16, CAPTURE, LIVE, 2><<<grid, block, 0, s>>>(a);
             return hipGetLastError();
         }
     }
@@ -509,10 +509,11 @@ hipError_t launch_rb(const VerifyArgs& a, int rb, hipStream_t s)
 template <int DK, bool O_BF16, bool CAPTURE, bool LIVE>
 hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
 {
-    // four row blocks per workgroup once the launch has at least eight workgroups per CU that way
+    // two row blocks per workgroup once the launch has at least sixteen workgroups per CU that way
+    // (B = 32 at K = 8: 189 us against 191 with four blocks and 252 with one)
     constexpr int RPG = kWaves * (64 / (DK / 4));
-    const long long wg4 = (long long)a.B * (a.Hv / kGroups) * (a.dv / (4 * RPG));
-    const int rb = (CAPTURE && LIVE && a.K <= 16 && a.dv % (4 * RPG) == 0 && wg4 >= 8 * 256) ? 4 : 1;
+    const long long wg2 = (long long)a.B * (a.Hv / kGroups) * (a.dv / (2 * RPG));
+    const int rb = (CAPTURE && LIVE && a.K <= 16 && a.dv % (2 * RPG) == 0 && wg2 >= 16 * 256) ? 2 : 1;
     if (a.K <= 1) return launch_rb<DK, 1, O_BF16, CAPTURE, LIVE>(a, rb, s);
     if (a.K <= 2) return launch_rb<DK, 2, O_BF16, CAPTURE, LIVE>(a, rb, s);
     if (a.K <= 4) return launch_rb<DK, 4, O_BF16, CAPTURE, LIVE>(a, rb, s);
