@@ -406,7 +406,23 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
                 d["S_out"] = torch.empty_like(d["S_in"])
                 d["H"] = torch.empty(wl.B, N, wl.Hv, wl.dv, wl.dk, device=dev)
                 d["o"] = torch.empty(wl.B, N, wl.Hv, wl.dv, device=dev)
+                d["S_ckpt"] = torch.empty_like(d["S_in"])
+                d["hist_out"] = torch.empty_like(d["hist"])
                 sets.append(d)
+            tidx = {id(d): r for r, d in enumerate(sets)}
+
+            def tfused(d, wl=wl, first=False):
+                # gdn_verify_tree_step: set r continues from set r-1's tree (its accepted node, states, tokens)
+                pv = sets[tidx[id(d)] - 1]
+                if first:
+                    gdn.verify_tree_step(d["x"], d["w"], d["parent"], d["beta_raw"], d["alpha"], d["dt_bias"],
+                                         d["A_log"], d["H"], d["o"], d["y"], wl.Hk, d["S_in"], d["hist"],
+                                         S_ckpt=d["S_ckpt"], hist_out=d["hist_out"])
+                else:
+                    gdn.verify_tree_step(d["x"], d["w"], d["parent"], d["beta_raw"], d["alpha"], d["dt_bias"],
+                                         d["A_log"], d["H"], d["o"], d["y"], wl.Hk, pv["S_ckpt"], pv["hist_out"],
+                                         prev=(pv["node"], pv["parent"], pv["H"], pv["x"]), S_ckpt=d["S_ckpt"],
+                                         hist_out=d["hist_out"])
 
             def tconv(d):
                 gdn.conv_tree(d["x"], d["w"], d["hist"], d["parent"], d["y"])
@@ -424,9 +440,11 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
                 troll(d)
             for fn in sets:
                 tconv(fn)
+                tfused(fn, first=True)
             reps = max(1, 200 // R)
             t_v = timed(tver, sets, reps)
             t_s = timed(tstep, sets, reps)
+            t_f = timed(tfused, sets, reps)
             b = verify_tree_bytes(wl)
             res["tree%d%s" % (N, "" if shape == "random" else "_" + shape)] = {
                                  "verify_tree_us": round(t_v, 3), "bytes_per_launch": b,
@@ -434,6 +452,7 @@ def other_workloads(torch, gdn, synth, dev, only=("decode", "batched", "tree", "
                                  "conv_tree_us": round(timed(tconv, sets, reps), 3),
                                  "rollback_tree_us": round(timed(troll, sets, reps), 3),
                                  "step_us": round(t_s, 3), "nodes_per_s": round(N / (t_s * 1e-6), 1),
+                                 "fused_step_us": round(t_f, 3),
                                  "tree": {"random": "random, parent among the 4 previous nodes",
                                           "binary": "complete binary, breadth-first numbering"}[shape]}
             del sets

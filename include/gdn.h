@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define GDN_VERSION 2
+#define GDN_VERSION 3
 
 enum gdn_status {
     GDN_OK = 0,
@@ -398,6 +398,48 @@ int gdn_rollback_tree(const int32_t *node, const int32_t *parent, int N,
                       const float *S_in, const float *H, float *S_out,
                       const void *x, void *hist,
                       int B, int Hv, int dv, int dk, int C, int W, int io_dtype, void *stream);
+
+/*
+ * gdn_verify_tree_step -- one whole tree verify step: the rollback of the
+ * previous tree to its accepted node, the conv of this tree's nodes and the
+ * tree verify with every node's state -- gdn_rollback_tree + gdn_conv_tree +
+ * gdn_verify_tree, bit for bit, without the state copy (the same tree
+ * drafting as above; the step a serving loop runs, with the DDTree branch of
+ * the spec loop in the lucebox PR #637 commit messages).  Two launches: the conv, then the verify.
+ *
+ * Previous tree (node_prev != NULL): sequence b keeps the path to node
+ * a = node_prev[b] of the previous tree (N_prev nodes, parent_prev, raw
+ * tokens x_prev, history hist_prev, states H_prev, start state S_prev_ckpt);
+ * a outside [0, N_prev) keeps nothing.  This tree starts from H_prev[b][a]
+ * (S_prev_ckpt[b] when nothing is kept), and its conv history is the W-1
+ * newest rows of [hist_prev ; x_prev along the path from the root to a].
+ * First tree (node_prev == NULL): from S_prev_ckpt and hist_prev (the
+ * committed state and history); N_prev, parent_prev, H_prev, x_prev unused.
+ *   node_prev [B] int32, parent_prev [B][N_prev] int32 (4-byte aligned);
+ *   S_prev_ckpt [B][Hv][dv][dk], H_prev [B][N_prev][Hv][dv][dk] float;
+ *   x_prev [B][N_prev][C], hist_prev [B][W-1][C] in_dtype;
+ *   x [B][N][C] raw tokens, w [C][W] float taps, parent [B][N] int32, gates,
+ *   gate_stride, dt_bias, A_log: as gdn_conv_tree and gdn_verify_tree.
+ * Outputs:
+ *   S_ckpt [B][Hv][dv][dk]  this tree's start state (nullable; the next
+ *                           step's S_prev_ckpt)
+ *   H, o                    as gdn_verify_tree
+ *   y [B][N][C]             the conv outputs (required: the verify reads them)
+ *   hist_out [B][W-1][C]    this tree's conv history (nullable; the next
+ *                           step's hist_prev)
+ * Every output is disjoint from every input and from the other outputs: a
+ * loop keeps two sets of (S_ckpt, H, hist_out) and alternates them; to leave
+ * it, gdn_rollback_tree(node, parent, S_ckpt, H, S_out, x, hist_out)
+ * materialises the state and the history.
+ */
+int gdn_verify_tree_step(const int32_t *node_prev, int N_prev, const int32_t *parent_prev,
+                         const float *S_prev_ckpt, const float *H_prev, const void *x_prev,
+                         const void *hist_prev, const void *x, const float *w, const int32_t *parent,
+                         const void *beta_raw, const void *alpha, int gate_stride,
+                         const float *dt_bias, const float *A_log,
+                         float *S_ckpt, float *H, void *o, void *y, void *hist_out,
+                         int B, int N, int Hk, int Hv, int dk, int dv, int W,
+                         int in_dtype, int o_dtype, float l2_eps, void *stream);
 
 #ifdef __cplusplus
 }

@@ -537,4 +537,81 @@ int gdn_rollback_tree(const int32_t* node, const int32_t* parent, int N, const f
     return launch_status(gdn::launch_tree_rollback(a, (hipStream_t)stream), fn);
 }
 
+int gdn_verify_tree_step(const int32_t* node_prev, int N_prev, const int32_t* parent_prev, const float* S_prev_ckpt,
+                         const float* H_prev, const void* x_prev, const void* hist_prev, const void* x, const float* w,
+                         const int32_t* parent, const void* beta_raw, const void* alpha, int gate_stride,
+                         const float* dt_bias, const float* A_log, float* S_ckpt, float* H, void* o, void* y,
+                         void* hist_out, int B, int N, int Hk, int Hv, int dk, int dv, int W, int in_dtype,
+                         int o_dtype, float l2_eps, void* stream)
+{
+    const char* fn = "gdn_verify_tree_step";
+    int rc = check_gdn_shape(fn, B, N, Hk, Hv, dk, dv, in_dtype, o_dtype, l2_eps);
+    if (rc) return rc;
+    REQUIRE(N <= gdn::kTreeMax, GDN_EUNSUPPORTED, "%s: N = %d > %d", fn, N, gdn::kTreeMax);
+    REQUIRE(W >= 2 && W <= 8, GDN_EUNSUPPORTED, "%s: W = %d not in 2..8", fn, W);
+    REQUIRE(B <= 65535 && Hv <= 65535, GDN_EUNSUPPORTED, "%s: B or Hv too large", fn);
+    REQUIRE((dt_bias == nullptr) == (A_log == nullptr), GDN_EINVAL,
+            "%s: dt_bias and A_log must be both given (raw gates) or both NULL (activated gates)", fn);
+    if (node_prev)
+        REQUIRE(N_prev >= 1 && N_prev <= gdn::kTreeMax, GDN_EINVAL, "%s: N_prev = %d not in 1..%d", fn, N_prev,
+                gdn::kTreeMax);
+    if (B == 0) return ok();
+    REQUIRE(S_prev_ckpt && hist_prev && x && w && parent && beta_raw && alpha && H && o && y, GDN_EINVAL,
+            "%s: null pointer", fn);
+    if (node_prev)
+        REQUIRE(parent_prev && H_prev && x_prev, GDN_EINVAL,
+                "%s: a previous tree needs parent_prev, H_prev and x_prev", fn);
+    REQUIRE(gate_stride >= Hv, GDN_EINVAL, "%s: gate_stride = %d < Hv = %d", fn, gate_stride, Hv);
+    const size_t ie = elem_size(in_dtype), oe = elem_size(o_dtype);
+    auto a16 = [](const void* q) { return q == nullptr || aligned16(q); };
+    REQUIRE(a16(S_prev_ckpt) && a16(H_prev) && a16(x_prev) && a16(hist_prev) && a16(x) && a16(w) && a16(dt_bias) &&
+                a16(A_log) && a16(S_ckpt) && a16(H) && a16(o) && a16(y) && a16(hist_out),
+            GDN_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+    REQUIRE(((uintptr_t)beta_raw % ie) == 0 && ((uintptr_t)alpha % ie) == 0 && ((uintptr_t)parent & 3) == 0 &&
+                ((uintptr_t)node_prev & 3) == 0 && ((uintptr_t)parent_prev & 3) == 0,
+            GDN_EINVAL, "%s: gate, node or parent pointers not aligned to their element size", fn);
+    const size_t C = (size_t)2 * Hk * dk + (size_t)Hv * dv;
+    const size_t st = (size_t)Hv * dv * dk * 4;
+    const size_t gspan = ((size_t)B * N - 1) * gate_stride + Hv;
+    const size_t hrows = (size_t)B * (W - 1) * C * ie;
+    const Span ins[] = {Span{node_prev, node_prev ? (size_t)B * 4 : 0},
+                        Span{node_prev ? parent_prev : nullptr, node_prev ? (size_t)B * N_prev * 4 : 0},
+                        Span{S_prev_ckpt, B * st},
+                        Span{node_prev ? H_prev : nullptr, node_prev ? (size_t)B * N_prev * st : 0},
+                        Span{node_prev ? x_prev : nullptr, node_prev ? (size_t)B * N_prev * C * ie : 0},
+                        Span{hist_prev, hrows},
+                        Span{x, (size_t)B * N * C * ie},
+                        Span{w, C * W * 4},
+                        Span{parent, (size_t)B * N * 4},
+                        Span{beta_raw, gspan * ie},
+                        Span{alpha, gspan * ie},
+                        Span{dt_bias, dt_bias ? (size_t)Hv * 4 : 0},
+                        Span{A_log, A_log ? (size_t)Hv * 4 : 0}};
+    const Span outs[] = {Span{S_ckpt, B * st}, Span{H, (size_t)B * N * st}, Span{o, (size_t)B * N * Hv * dv * oe},
+                         Span{y, (size_t)B * N * C * ie}, Span{hist_out, hist_out ? hrows : 0}};
+    for (const Span& q : outs)
+        for (const Span& i : ins) REQUIRE(!overlap(q, i), GDN_EINVAL, "%s: an output overlaps an input", fn);
+    for (int i = 0; i < 5; ++i)
+        for (int j = i + 1; j < 5; ++j) REQUIRE(!overlap(outs[i], outs[j]), GDN_EINVAL, "%s: two outputs overlap", fn);
+    // 1. the conv of every node, its history the previous tree's accepted path (then hist_prev)
+    gdn::ConvTreeArgs c{x, w, hist_prev, parent, y, B, N, (int)C, W};
+    c.node_prev = node_prev;
+    c.parent_prev = parent_prev;
+    c.x_prev = x_prev;
+    c.N_prev = node_prev ? N_prev : 0;
+    c.hist_out = hist_out;
+    rc = launch_status(gdn::launch_conv_tree(c, in_dtype == GDN_BF16, (hipStream_t)stream), fn);
+    if (rc) return rc;
+    // 2. the tree verify from the start state the accepted node picks, written out as the checkpoint
+    gdn::VerifyArgs a{y, beta_raw, alpha, dt_bias, A_log, S_prev_ckpt, nullptr, H, o, B, N, Hk, Hv, dk, dv, l2_eps,
+                      nullptr, gate_stride, nullptr, parent};
+    a.acc_prev = node_prev;
+    a.Kp = node_prev ? N_prev : 0;
+    a.Sp_ckpt = S_prev_ckpt;
+    a.Sp_H = H_prev;
+    a.S_ckpt = S_ckpt;
+    a.pick = true;
+    return launch_status(gdn::launch_verify(a, in_dtype == GDN_BF16, o_dtype == GDN_BF16, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

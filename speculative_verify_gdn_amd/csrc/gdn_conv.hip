@@ -254,30 +254,60 @@ template <bool BF16, int W>
 __global__ __launch_bounds__(kThreads) void conv_tree_kernel(ConvTreeArgs a)
 {
     __shared__ int spar[kTreeMax];
+    __shared__ int sprev[kTreeMax];               // parents of the previous tree (fused step)
     const int b = blockIdx.z, N = a.N, C = a.C;
     if ((int)threadIdx.x < N) {
         const int i = threadIdx.x;
         const int p = a.parent[(size_t)b * N + i];
         spar[i] = (p >= 0 && p < i) ? p : -1;
     }
+    // the previous tree's accepted node (-1: none kept, or no previous tree)
+    int acc = -1;
+    if (a.node_prev) {
+        const int nd = a.node_prev[b];
+        acc = (nd >= 0 && nd < a.N_prev) ? nd : -1;
+        if ((int)threadIdx.x < a.N_prev) {
+            const int i = threadIdx.x;
+            const int p = a.parent_prev[(size_t)b * a.N_prev + i];
+            sprev[i] = (p >= 0 && p < i) ? p : -1;
+        }
+    }
     __syncthreads();
     const int g = threadIdx.x % kGroups, tl = threadIdx.x / kGroups;
     const int c0 = (blockIdx.x * kGroups + g) * kCh;
     const int t = blockIdx.y * kTok + tl;
-    if (c0 >= C || t >= N) return;
-    const int nch = min(kCh, C - c0);
+    const int nch = c0 < C ? min(kCh, C - c0) : 0;
     const bool vec = (nch == kCh) && ((C & 3) == 0);
     const size_t xb = (size_t)b * N * C;
     const size_t hb = (size_t)b * (W - 1) * C;
+    const size_t pb = (size_t)b * a.N_prev * C;
 
-    // col[W-1] = x_t, then up the path; past a root the history rows, newest first
+    // the history this tree's conv takes (fused step): row tl of hist_out, by the first token tile
+    if (a.hist_out && blockIdx.y == 0 && tl < W - 1 && c0 < C) {
+        int m = acc, hr = W - 2;
+        for (int r = W - 2; r > tl; --r) {
+            if (m >= 0) m = sprev[m];
+            else --hr;
+        }
+        float row[kCh];
+        if (m >= 0) load_row8<BF16>(a.x_prev, pb + (size_t)m * C + c0, nch, vec, row);
+        else load_row8<BF16>(a.hist, hb + (size_t)hr * C + c0, nch, vec, row);
+        store_row8<BF16>(a.hist_out, hb + (size_t)tl * C + c0, nch, vec, row);
+    }
+    if (c0 >= C || t >= N) return;
+
+    // col[W-1] = x_t, then up the path; past a root the history rows, newest first (in the fused step
+    // the previous tree's path from its accepted node comes first, then the history)
     float col[W][kCh];
-    int n = t, hr = W - 2;
+    int n = t, m = acc, hr = W - 2;
 #pragma unroll
     for (int jj = W - 1; jj >= 0; --jj) {
         if (n >= 0) {
             load_row8<BF16>(a.x, xb + (size_t)n * C + c0, nch, vec, col[jj]);
             n = spar[n];
+        } else if (m >= 0) {
+            load_row8<BF16>(a.x_prev, pb + (size_t)m * C + c0, nch, vec, col[jj]);
+            m = sprev[m];
         } else {
             load_row8<BF16>(a.hist, hb + (size_t)hr * C + c0, nch, vec, col[jj]);
             --hr;

@@ -47,6 +47,10 @@ struct VerifyArgs {
     float* S_ckpt = nullptr;           // [B][Hv][dv][dk] this window's start state, or nullptr
     void* y = nullptr;                 // [B][K][C] conv outputs, or nullptr
     void* win = nullptr;               // [B][3+K][C] this window's conv window, or nullptr
+    // tree verify whose start state is picked by the previous tree's accepted node: acc_prev (node,
+    // outside [0, Kp): none kept), Kp (its node count), Sp_H (its node states), Sp_ckpt (its start
+    // state, also the start when acc_prev is nullptr); the start state is written to S_ckpt
+    bool pick = false;
 };
 
 // longest verify window (tokens per sequence) of the chain calls
@@ -62,6 +66,13 @@ struct ConvTreeArgs {
     const int32_t* parent;   // [B][N]
     void* y;                 // [B][N][C]
     int B, N, C, W;
+    // the fused tree step: the history is the W-1 newest rows of [hist ; x_prev along the path from the
+    // previous tree's accepted node to its root]; hist_out receives them
+    const int32_t* node_prev = nullptr;    // [B] accepted node of the previous tree (outside [0, N_prev): none)
+    const int32_t* parent_prev = nullptr;  // [B][N_prev]
+    const void* x_prev = nullptr;          // [B][N_prev][C]
+    int N_prev = 0;
+    void* hist_out = nullptr;              // [B][W-1][C] or nullptr
 };
 
 struct TreeRollbackArgs {

@@ -153,7 +153,7 @@ __device__ __forceinline__ f32x4_t state_tile(const in_t (*X)[QW], const s_t (*S
     return acc;
 }
 
-template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT, bool TREE, bool STEP, int NG = 1>
+template <int DK, int KMAX, bool IN_BF16, bool O_BF16, bool NT, bool TREE, bool STEP, int NG = 1, bool SEL = false>
 __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
 {
     constexpr int LPR = DK / 4;                  // lanes per state row (one float4 each)
@@ -219,8 +219,18 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     // The accept length is loaded only once every load that does not depend on it has
     // been issued (pick_start), so its round trip overlaps theirs.
     const in_t* HS = nullptr;
+    // (SEL, the fused tree step: the start state is the previous tree's state at its accepted node, or its
+    // start state when no node was kept, and is written out as this tree's checkpoint)
     auto pick_start = [&]() {
-        if constexpr (STEP) {
+        if constexpr (SEL) {
+            if (a.acc_prev) {
+                const int nd = a.acc_prev[b];
+                Sh = (nd >= 0 && nd < a.Kp) ? a.Sp_H + (((size_t)b * a.Kp + nd) * Hv + h) * SD
+                                            : a.Sp_ckpt + ((size_t)b * Hv + h) * SD;
+            } else {
+                Sh = a.Sp_ckpt + ((size_t)b * Hv + h) * SD;
+            }
+        } else if constexpr (STEP) {
             int ap = 0;
             if (a.acc_prev) {
                 const int ap_raw = a.acc_prev[b];
@@ -389,18 +399,26 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                 }
             }
         }
-        f32x4_t S0 = load_f4(Sh + (size_t)ic * DK + c);
         float vv[NV];
-        if constexpr (!STEP) {
+        auto load_v = [&]() {
+            if constexpr (!STEP) {
 #pragma unroll
-            for (int n = 0; n < NV; ++n) {
-                const int idx = tid + n * kThreads;
-                const int t = idx / RPG, rr = idx % RPG;
-                const int gr = blockIdx.x * RPG + rr;
-                const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
-                vv[n] = idx < KMAX * RPG ? load1<IN_BF16>(X + (size_t)(t < K ? t : K - 1) * C, vch) : 0.f;
+                for (int n = 0; n < NV; ++n) {
+                    const int idx = tid + n * kThreads;
+                    const int t = idx / RPG, rr = idx % RPG;
+                    const int gr = blockIdx.x * RPG + rr;
+                    const size_t vch = 2 * (size_t)Hk * DK + (size_t)h * dv + (gr < dv ? gr : dv - 1);
+                    vv[n] = idx < KMAX * RPG ? load1<IN_BF16>(X + (size_t)(t < K ? t : K - 1) * C, vch) : 0.f;
+                }
             }
+        };
+        // SEL: the v loads go before the accepted node, whose value the start state's address waits for
+        if constexpr (SEL) {
+            load_v();
+            pick_start();
         }
+        f32x4_t S0 = load_f4(Sh + (size_t)ic * DK + c);
+        if constexpr (!SEL) load_v();
         if constexpr (STEP) {
             do_gates();
             // the conv, as the conv kernels compute it; the conv outputs and the window
@@ -498,6 +516,10 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
                     }
                 }
             }
+        }
+        if constexpr (SEL) {
+            // the checkpoint: this tree's start state
+            if (a.S_ckpt && live) store_f4<true>(a.S_ckpt + ((size_t)b * Hv + h) * SD + (size_t)i * DK + c, S0);
         }
         if (!live) S0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
         S = S0;
@@ -836,10 +858,14 @@ hipError_t launch_k(const VerifyArgs& a, hipStream_t s)
     dim3 grid((a.dv + RPG - 1) / RPG, a.Hv, a.B);
     if (a.parent) {
         // (the tree calls take at most kTreeMax nodes: their ancestor masks are 32-bit words)
-        if constexpr (KMAX <= kTreeMax)
-            verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, true, false><<<grid, dim3(kThreads), 0, s>>>(a);
-        else
+        if constexpr (KMAX <= kTreeMax) {
+            if (a.pick)   // the fused tree step: start state picked by the previous tree's accepted node
+                verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, true, false, 1, true><<<grid, dim3(kThreads), 0, s>>>(a);
+            else
+                verify_kernel<DK, KMAX, IN_BF16, O_BF16, true, true, false><<<grid, dim3(kThreads), 0, s>>>(a);
+        } else {
             return hipErrorInvalidValue;
+        }
     } else if (a.x) {
         // the fused step: three value heads per workgroup when the heads come in groups of
         // three and three copies of the head's LDS fit in a CU

@@ -26,7 +26,7 @@ GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_version", "gdn_last_error", "gdn_conv_step", "gdn_verify", "gdn_rollback", "gdn_prefill_chunked",
            "gdn_rollback_conv_step", "gdn_conv_step_ex", "gdn_verify_ex", "gdn_rollback_ex", "gdn_replay",
            "gdn_conv_tree", "gdn_verify_tree", "gdn_rollback_tree", "gdn_verify_step",
-           "gdn_debug_clamped_accepts")
+           "gdn_debug_clamped_accepts", "gdn_verify_tree_step")
 
 
 class GdnError(RuntimeError):
@@ -97,6 +97,8 @@ def open_library(path: str):
     lib.gdn_verify_tree.argtypes = [P, P, P, I, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, P]
     lib.gdn_rollback_tree.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.gdn_debug_clamped_accepts.argtypes = [P, I]
+    lib.gdn_verify_tree_step.argtypes = [P, I, P, P, P, P, P, P, P, P, P, P, I, P, P, P, P, P, P, P,
+                                         I, I, I, I, I, I, I, I, I, F, P]
     for name in EXPORTS:
         getattr(lib, name).restype = ctypes.c_char_p if name == "gdn_last_error" else I
     return lib
@@ -282,3 +284,32 @@ def verify_step(x, w, beta_raw, alpha, dt_bias, A_log, S_out, H, o, Hk, prev=Non
                                   _p(hist), _p(x), _p(w), _p(beta_raw), _p(alpha), int(gate_stride), _p(dt_bias),
                                   _p(A_log), _p(S_ckpt), _p(S_out), _p(H), _p(o), _p(y), _p(win), B, K, Hk, Hv, dk,
                                   dv, W, _dtype(x), _dtype(o), float(eps), _stream(stream)))
+
+
+def verify_tree_step(x, w, parent, beta_raw, alpha, dt_bias, A_log, H, o, y, Hk, S_prev_ckpt, hist_prev,
+                     prev=None, S_ckpt=None, hist_out=None, eps=1e-6, gate_stride=None, stream=None):
+    """gdn_verify_tree_step: rollback of the previous tree to its accepted node + conv_tree + verify_tree, two
+    launches. x [B][N][C] raw tokens, parent [B][N] int32, H [B][N][Hv][dv][dk], o [B][N][Hv][dv], y [B][N][C];
+    S_prev_ckpt [B][Hv][dv][dk] and hist_prev [B][W-1][C]: the previous tree's start state and history (for the
+    first tree the committed state and history); prev = (node_prev [B] int32, parent_prev [B][N_prev],
+    H_prev [B][N_prev][...], x_prev [B][N_prev][C]) or None for the first tree; S_ckpt and hist_out receive this
+    tree's start state and history."""
+    _dev(x, w, parent, dt_bias, A_log, H, o, y, S_prev_ckpt, hist_prev, S_ckpt, hist_out)
+    if gate_stride is None:
+        _dev(beta_raw, alpha)
+    elif not (beta_raw.is_cuda and alpha.is_cuda):
+        raise ValueError("libgdn takes device tensors")
+    B, N, C = x.shape
+    W = w.shape[1]
+    _, Hv, dv, dk = S_prev_ckpt.shape
+    node_prev = parent_prev = H_prev = x_prev = None
+    N_prev = 0
+    if prev is not None:
+        node_prev, parent_prev, H_prev, x_prev = prev
+        _dev(node_prev, parent_prev, H_prev, x_prev)
+        N_prev = parent_prev.shape[1]
+    gs = Hv if gate_stride is None else int(gate_stride)
+    _check(_L().gdn_verify_tree_step(_p(node_prev), N_prev, _p(parent_prev), _p(S_prev_ckpt), _p(H_prev), _p(x_prev),
+                                     _p(hist_prev), _p(x), _p(w), _p(parent), _p(beta_raw), _p(alpha), gs,
+                                     _p(dt_bias), _p(A_log), _p(S_ckpt), _p(H), _p(o), _p(y), _p(hist_out),
+                                     B, N, Hk, Hv, dk, dv, W, _dtype(x), _dtype(o), float(eps), _stream(stream)))

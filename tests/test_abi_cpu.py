@@ -389,3 +389,44 @@ def test_verify_step_first_window_and_empty_batch(lib):
     assert step_call(lib, B=0) == gdn.GDN_OK
     assert step_call(lib, acc=None, S_in=p(20), hist=p(21), B=0) == gdn.GDN_OK
     assert step_call(lib, acc=None, S_in=p(20), hist=None) == gdn.GDN_EINVAL
+
+
+def tree_step_call(lib, **kw):
+    a = dict(node=p(0), Np=16, ppar=p(1), pck=p(2), pH=p(3), px=p(4), phist=p(5), x=p(6), w=p(7), par=p(8),
+             beta=p(9), alpha=p(10), gs=2, dt=p(11), alog=p(12), ck=p(13), H=p(14), o=p(15), y=p(16), hout=p(17),
+             B=1, N=16, Hk=2, Hv=2, dk=32, dv=32, W=4, ind=gdn.GDN_BF16, od=gdn.GDN_F32, eps=1e-6)
+    a.update(kw)
+    return lib.gdn_verify_tree_step(a["node"], a["Np"], a["ppar"], a["pck"], a["pH"], a["px"], a["phist"], a["x"],
+                                    a["w"], a["par"], a["beta"], a["alpha"], a["gs"], a["dt"], a["alog"], a["ck"],
+                                    a["H"], a["o"], a["y"], a["hout"], a["B"], a["N"], a["Hk"], a["Hv"], a["dk"],
+                                    a["dv"], a["W"], a["ind"], a["od"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=33), gdn.GDN_EUNSUPPORTED),                      # ancestor masks are 32-bit words
+    (dict(W=9), gdn.GDN_EUNSUPPORTED),
+    (dict(Np=0), gdn.GDN_EINVAL),
+    (dict(Np=33), gdn.GDN_EINVAL),
+    (dict(ppar=None), gdn.GDN_EINVAL),                       # a previous tree needs its parents,
+    (dict(pH=None), gdn.GDN_EINVAL),                         # its node states
+    (dict(px=None), gdn.GDN_EINVAL),                         # and its tokens
+    (dict(pck=None), gdn.GDN_EINVAL),
+    (dict(phist=None), gdn.GDN_EINVAL),
+    (dict(y=None), gdn.GDN_EINVAL),                          # the verify reads the conv outputs
+    (dict(H=None), gdn.GDN_EINVAL),
+    (dict(hout=p(5)), gdn.GDN_EINVAL),                       # the history out over the history in
+    (dict(ck=p(3)), gdn.GDN_EINVAL),                         # the checkpoint over the previous states
+    (dict(ck=p(14)), gdn.GDN_EINVAL),                        # two outputs overlap
+    (dict(node=ctypes.c_void_p(A + 2)), gdn.GDN_EINVAL),     # node not 4-byte aligned
+    (dict(gs=1), gdn.GDN_EINVAL),
+    (dict(dk=48), gdn.GDN_EUNSUPPORTED),
+])
+def test_verify_tree_step_rejects(lib, kw, code):
+    assert tree_step_call(lib, **kw) == code
+
+
+def test_verify_tree_step_first_tree_and_empty_batch(lib):
+    assert tree_step_call(lib, B=0) == gdn.GDN_OK
+    # the first tree needs none of the previous tree's buffers
+    assert tree_step_call(lib, node=None, Np=0, ppar=None, pH=None, px=None, B=0) == gdn.GDN_OK
+    assert tree_step_call(lib, node=None, Np=0, ppar=None, pH=None, px=None, phist=None) == gdn.GDN_EINVAL

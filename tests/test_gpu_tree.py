@@ -259,3 +259,111 @@ def test_tree_step_conv_verify_rollback_against_oracle():
     oracle.tree_rollback(node.numpy(), par.numpy(), S_dummy, np.zeros((wl.B, wl.T, 1), np.float32), S_dummy.copy(),
                          x=inp["x"].view(torch.int16).numpy(), hist=hist_ref)
     assert np.array_equal(d["hist"].cpu().view(torch.int16).numpy(), hist_ref)
+
+
+# ------------------------------------------------------------------ the fused tree step
+def _tree_step_outputs(wl, o_dtype=torch.float32):
+    B, N, Hv, dv, dk, C, W = wl.B, wl.T, wl.Hv, wl.dv, wl.dk, wl.C, wl.W
+    io = torch.bfloat16 if wl.bf16 else torch.float32
+    return dict(S_ckpt=torch.empty(B, Hv, dv, dk, device="cuda"), H=torch.empty(B, N, Hv, dv, dk, device="cuda"),
+                o=torch.empty(B, N, Hv, dv, device="cuda", dtype=o_dtype),
+                y=torch.empty(B, N, C, device="cuda", dtype=io),
+                hist_out=torch.empty(B, W - 1, C, device="cuda", dtype=io))
+
+
+def _tree_step(wl, d, par, out, S_prev_ckpt, hist_prev, prev=None):
+    gdn.verify_tree_step(d["x"], d["w"], par, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], out["H"],
+                         out["o"], out["y"], wl.Hk, S_prev_ckpt, hist_prev, prev=prev, S_ckpt=out["S_ckpt"],
+                         hist_out=out["hist_out"])
+
+
+def _tree_separate(wl, d, par, out, S_start, hist):
+    """conv_tree + verify_tree from S_start and hist: what the fused step must give."""
+    gdn.conv_tree(d["x"], d["w"], hist, par, out["y"])
+    gdn.verify_tree(out["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], par, S_start, out["H"], out["o"],
+                    wl.Hk)
+    out["S_ckpt"].copy_(S_start)
+    out["hist_out"].copy_(hist)
+
+
+TREE_STEP_CASES = [
+    # (overrides, first tree's shape, second tree's shape, accepted nodes of the first tree)
+    (dict(B=4, T=16, Hk=4, Hv=12), "random", "random", [9, -1, 0, 15]),
+    (dict(B=3, T=12, Hk=2, Hv=6, W=2), "forest", "binary", [11, 3, 40]),
+    (dict(B=2, T=7, Hk=2, Hv=4, dk=64, dv=64, W=8), "binary", "star", [6, 2]),
+    (dict(B=2, T=32, Hk=2, Hv=6), "binary", "random", [31, 17]),
+    (dict(B=2, T=5, Hk=2, Hv=6, dk=32, dv=32), "chain", "forest", [4, 0]),
+    (dict(), "random", "random", [13]),                       # the bench's verify16 shape, N = 16
+]
+
+
+@pytest.mark.parametrize("over,shape1,shape2,acc", TREE_STEP_CASES)
+def test_tree_step_equals_separate_calls(over, shape1, shape2, acc):
+    """gdn_verify_tree_step gives the bits of gdn_rollback_tree + gdn_conv_tree + gdn_verify_tree: a first tree
+    from the committed state, then a second tree from the first one's buffers and accepted nodes."""
+    wl = synth.small("verify16", **over)
+    say("verify_tree_step", over, shape1, shape2, "accept", acc)
+    inp1 = synth.make_inputs(wl, seed=43)
+    inp2 = synth.make_inputs(wl, seed=44)
+    d1 = {k: dev(v) for k, v in inp1.items()}
+    d2 = {k: dev(v) for k, v in inp2.items()}
+    d2["w"] = d1["w"]
+    par1 = dev(synth.make_tree(wl.B, wl.T, seed=45, shape=shape1))
+    par2 = dev(synth.make_tree(wl.B, wl.T, seed=46, shape=shape2))
+    node = torch.tensor(acc, dtype=torch.int32, device="cuda")
+
+    A, A_ref = _tree_step_outputs(wl), _tree_step_outputs(wl)
+    _tree_step(wl, d1, par1, A, d1["S_in"], d1["hist"])
+    _tree_separate(wl, d1, par1, A_ref, d1["S_in"], d1["hist"])
+    torch.cuda.synchronize()
+    for k in A:
+        assert torch.equal(A[k], A_ref[k]), "first tree: %s differs" % k
+
+    Bo, B_ref = _tree_step_outputs(wl), _tree_step_outputs(wl)
+    _tree_step(wl, d2, par2, Bo, A["S_ckpt"], A["hist_out"], prev=(node, par1, A["H"], d1["x"]))
+    S_start = torch.empty_like(d1["S_in"])
+    hist = A_ref["hist_out"].clone()
+    gdn.rollback_tree(node, par1, A_ref["S_ckpt"], A_ref["H"], S_start, d1["x"], hist)
+    _tree_separate(wl, d2, par2, B_ref, S_start, hist)
+    torch.cuda.synchronize()
+    for k in Bo:
+        assert torch.equal(Bo[k], B_ref[k]), "second tree: %s differs" % k
+
+
+def test_tree_step_chain_against_oracle():
+    """Two fused tree steps against the oracle: conv and GDN of tree 1, the rollback to its accepted node, then
+    tree 2 from there (conv bit for bit, states within the bar)."""
+    wl = synth.small("verify16", B=2, T=16, Hk=4, Hv=12)
+    say("verify_tree_step two trees vs oracle", wl)
+    inp1 = synth.make_inputs(wl, seed=53)
+    inp2 = synth.make_inputs(wl, seed=54)
+    d1 = {k: dev(v) for k, v in inp1.items()}
+    d2 = {k: dev(v) for k, v in inp2.items()}
+    d2["w"] = d1["w"]
+    par1 = synth.make_tree(wl.B, wl.T, seed=55, shape="random")
+    par2 = synth.make_tree(wl.B, wl.T, seed=56, shape="forest")
+    node = torch.tensor([10, -1], dtype=torch.int32)
+    A, Bo = _tree_step_outputs(wl), _tree_step_outputs(wl)
+    _tree_step(wl, d1, dev(par1), A, d1["S_in"], d1["hist"])
+    _tree_step(wl, d2, dev(par2), Bo, A["S_ckpt"], A["hist_out"], prev=(dev(node), dev(par1), A["H"], d1["x"]))
+    torch.cuda.synchronize()
+
+    w = inp1["w"].numpy()
+    gates = lambda inp: (f64(inp["beta_raw"]), f64(inp["alpha"]), f64(inp["dt_bias"]), f64(inp["A_log"]))
+    y1 = oracle.conv_tree_f32(inp1["x"].float().numpy(), w, inp1["hist"].float().numpy(), par1.numpy(), True)
+    y1b = torch.from_numpy(y1).to(torch.bfloat16)
+    H1, _ = oracle.gdn_tree_f64(f64(y1b), *gates(inp1), par1.numpy(), f64(inp1["S_in"]), wl.Hk)
+    # rollback of tree 1 to its accepted nodes: the state and the history
+    S_keep = np.empty_like(f64(inp1["S_in"]))
+    hist2 = inp1["hist"].view(torch.int16).numpy().copy()
+    oracle.tree_rollback(node.numpy(), par1.numpy(), f64(inp1["S_in"]), H1, S_keep,
+                         x=inp1["x"].view(torch.int16).numpy(), hist=hist2)
+    hist2_f = torch.from_numpy(hist2).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(Bo["hist_out"].cpu().view(torch.int16).numpy(), hist2)
+    check_states(Bo["S_ckpt"].cpu().numpy(), S_keep, "S_ckpt")
+    y2 = oracle.conv_tree_f32(inp2["x"].float().numpy(), w, hist2_f, par2.numpy(), True)
+    y2b = torch.from_numpy(y2).to(torch.bfloat16)
+    assert torch.equal(Bo["y"].cpu(), y2b)
+    H2, o2 = oracle.gdn_tree_f64(f64(y2b), *gates(inp2), par2.numpy(), S_keep, wl.Hk)
+    check_states(Bo["H"].cpu().numpy(), H2, "H")
+    check_outputs(Bo["o"].cpu().numpy(), o2, H2, False)
