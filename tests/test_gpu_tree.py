@@ -367,3 +367,31 @@ def test_tree_step_chain_against_oracle():
     H2, o2 = oracle.gdn_tree_f64(f64(y2b), *gates(inp2), par2.numpy(), S_keep, wl.Hk)
     check_states(Bo["H"].cpu().numpy(), H2, "H")
     check_outputs(Bo["o"].cpu().numpy(), o2, H2, False)
+
+
+@pytest.mark.parametrize("N1,N2,acc", [(8, 16, [7, 3]), (32, 5, [31, -4]), (1, 12, [0, 1])])
+def test_tree_step_previous_tree_of_another_size(N1, N2, acc):
+    """A tree of N2 nodes after one of N1 != N2: the previous tree's node states (N1 planes), parents and tokens
+    are read with N1, checked against gdn_rollback_tree + the separate calls."""
+    wl1 = synth.small("verify16", B=2, T=N1, Hk=2, Hv=6)
+    wl2 = synth.small("verify16", B=2, T=N2, Hk=2, Hv=6)
+    say("verify_tree_step N_prev=%d N=%d" % (N1, N2), "accept", acc)
+    inp1 = synth.make_inputs(wl1, seed=63)
+    inp2 = synth.make_inputs(wl2, seed=64)
+    d1 = {k: dev(v) for k, v in inp1.items()}
+    d2 = {k: dev(v) for k, v in inp2.items()}
+    d2["w"] = d1["w"]
+    par1 = dev(synth.make_tree(wl1.B, N1, seed=65, shape="random"))
+    par2 = dev(synth.make_tree(wl2.B, N2, seed=66, shape="forest"))
+    node = torch.tensor(acc, dtype=torch.int32, device="cuda")
+    A = _tree_step_outputs(wl1)
+    _tree_step(wl1, d1, par1, A, d1["S_in"], d1["hist"])
+    Bo, B_ref = _tree_step_outputs(wl2), _tree_step_outputs(wl2)
+    _tree_step(wl2, d2, par2, Bo, A["S_ckpt"], A["hist_out"], prev=(node, par1, A["H"], d1["x"]))
+    S_start = torch.empty_like(d1["S_in"])
+    hist = A["hist_out"].clone()
+    gdn.rollback_tree(node, par1, A["S_ckpt"], A["H"], S_start, d1["x"], hist)
+    _tree_separate(wl2, d2, par2, B_ref, S_start, hist)
+    torch.cuda.synchronize()
+    for k in Bo:
+        assert torch.equal(Bo[k], B_ref[k]), "second tree: %s differs" % k
