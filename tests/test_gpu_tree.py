@@ -297,11 +297,13 @@ TREE_STEP_CASES = [
 ]
 
 
-@pytest.mark.parametrize("over,shape1,shape2,acc", TREE_STEP_CASES)
+@pytest.mark.parametrize("over,shape1,shape2,acc", TREE_STEP_CASES + [(dict(name="tiny", B=2), "random", "forest",
+                                                                          [3, 1])])   # fp32 inputs
 def test_tree_step_equals_separate_calls(over, shape1, shape2, acc):
     """gdn_verify_tree_step gives the bits of gdn_rollback_tree + gdn_conv_tree + gdn_verify_tree: a first tree
     from the committed state, then a second tree from the first one's buffers and accepted nodes."""
-    wl = synth.small("verify16", **over)
+    over = dict(over)
+    wl = synth.small(over.pop("name", "verify16"), **over)
     say("verify_tree_step", over, shape1, shape2, "accept", acc)
     inp1 = synth.make_inputs(wl, seed=43)
     inp2 = synth.make_inputs(wl, seed=44)
