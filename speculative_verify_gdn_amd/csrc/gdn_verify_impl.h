@@ -182,6 +182,14 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     const int i = blockIdx.x * RPG + rloc;
     // Kb: the window of the buffers (strides); K: this sequence's tokens (masks)
     const int Kb = a.K, Hk = a.Hk, Hv = a.Hv, dv = a.dv;
+    // SEL: the previous tree's accepted node is the first load (a vector load whose index is zero but
+    // lane-dependent -- eps >= 0 is checked on the host -- so the loads issued after it need not wait for it;
+    // the start state's address waits for it)
+    int nd_raw = -1;
+    if constexpr (SEL) {
+        const int z0 = (int)(a.eps < 0.f) & (int)(threadIdx.x & 63);
+        if (a.acc_prev) nd_raw = a.acc_prev[b + z0];
+    }
     int K = a.lens ? min(max(a.lens[b], 1), Kb) : Kb;
     const int gs = a.gstride > 0 ? a.gstride : Hv;
     if (a.replay) {
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(kThreads * NG) void verify_kernel(VerifyArgs a)
     auto pick_start = [&]() {
         if constexpr (SEL) {
             if (a.acc_prev) {
-                const int nd = a.acc_prev[b];
+                const int nd = __builtin_amdgcn_readfirstlane(nd_raw);
                 Sh = (nd >= 0 && nd < a.Kp) ? a.Sp_H + (((size_t)b * a.Kp + nd) * Hv + h) * SD
                                             : a.Sp_ckpt + ((size_t)b * Hv + h) * SD;
             } else {
