@@ -511,6 +511,49 @@ def copy_peak(torch, dev, mib=512, trials=5):
             "bytes_per_copy": 2 * n * 4, "copy": "%d MiB device to device (torch copy kernel), read + write" % mib}
 
 
+def write_peak(torch, dev, mib=1024, trials=5, step_bytes_=0, sets=10):
+    """Plain device writes (torch's fill kernel, no reads), replayed from HIP graphs, median of the trials:
+    one buffer of mib MiB (the sustained write rate, 4x the Infinity Cache), and -- when step_bytes_ is given --
+    `sets` buffers of that size filled back to back, one fill per launch (the step's store volume in the bench's
+    rotation of buffer sets: the time a kernel that only wrote those bytes would take per launch)."""
+    import statistics
+
+    def rate(bufs, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                for b in bufs:
+                    b.fill_(1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(trials):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1) * 1e3 / (reps * len(bufs)))   # us per fill
+        return statistics.median(runs), min(runs), max(runs)
+
+    n = mib * 2 ** 20 // 4
+    big = torch.empty(n, device=dev)
+    us, lo, hi = rate([big], 4)
+    del big
+    out = {"GBs": round(n * 4 / (us * 1e-6) / 1e9, 1), "min": round(n * 4 / (hi * 1e-6) / 1e9, 1),
+           "max": round(n * 4 / (lo * 1e-6) / 1e9, 1), "bytes_per_fill": n * 4,
+           "write": "%d MiB device fill (torch fill kernel), writes only" % mib}
+    if step_bytes_:
+        m = step_bytes_ // 4
+        bufs = [torch.empty(m, device=dev) for _ in range(sets)]
+        us, lo, hi = rate(bufs, 2)
+        del bufs
+        out["step_sized"] = {"us_per_fill": round(us, 3), "GBs": round(m * 4 / (us * 1e-6) / 1e9, 1),
+                             "bytes_per_fill": m * 4, "sets": sets,
+                             "fill": "%d buffers of the step's state bytes, one fill per launch, back to back" % sets}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -808,6 +851,9 @@ def main():
     vb = verify_bytes(wl)
     sb = step_bytes(wl)
     cpk = copy_peak(torch, dev)
+    # the step's state bytes: the checkpoint, K-1 captured states and the final state
+    state_out = wl.B * wl.Hv * wl.dv * wl.dk * 4 * (wl.T + 1)
+    wpk = write_peak(torch, dev, step_bytes_=state_out, sets=R)
     if mode == "fused":
         # the dominant (and only) kernel of the step: gdn_verify_step
         dom, dom_bytes, dom_us = "gdn_verify_step", sb, t_fused
@@ -855,6 +901,8 @@ def main():
             "traffic": traffic,
             "device_copy_GBs": cpk["GBs"],
             "frac_of_device_copy": round(achieved / cpk["GBs"], 4),
+            "device_write_GBs": wpk["GBs"],
+            "frac_of_device_write": round(achieved / wpk["GBs"], 4),
         },
         "detail": {
             "kernel": dom,
@@ -885,6 +933,7 @@ def main():
             "wall_ms_timed": round(wall_ms, 3),
             "settle": {"steps": settle_steps, "min_ms": args.settle_ms},
             "device_copy": cpk,
+            "device_write": wpk,
             "o_dtype": "f32" if args.o_f32 else "bf16",
             "source_sha": sha,
             "accept_lengths": accepts,
