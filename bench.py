@@ -21,7 +21,7 @@ is the figure (min and max beside it).
 Printed: one JSON line with the metric, the roofline of the step's kernel
 (algorithmic bytes per launch / its median duration, timed with HIP events on
 the launch stream around graph-replayed back-to-back launches of that kernel
-alone; the measured device-copy rate beside the published peak), and the CPU
+alone; the measured device-copy and device-write rates beside the published peak), and the CPU
 oracle timed on the host as a baseline (one thread and all usable cores).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--trials 20]
