@@ -430,3 +430,19 @@ def test_verify_tree_step_first_tree_and_empty_batch(lib):
     # the first tree needs none of the previous tree's buffers
     assert tree_step_call(lib, node=None, Np=0, ppar=None, pH=None, px=None, B=0) == gdn.GDN_OK
     assert tree_step_call(lib, node=None, Np=0, ppar=None, pH=None, px=None, phist=None) == gdn.GDN_EINVAL
+
+
+def test_binding_routes_calls_to_another_build(lib):
+    """gdn.using(lib) sends this thread's calls to another build of the library (here the debug build), and
+    only inside the block."""
+    if not os.path.exists(gdn.DEBUG_LIB_PATH):
+        pytest.skip("libgdn_debug.so not built")
+    dbg = gdn.open_library(gdn.DEBUG_LIB_PATH)
+    assert gdn._L() is lib
+    with gdn.using(dbg):
+        assert gdn._L() is dbg
+        assert gdn.version() == lib.gdn_version()
+        with gdn.using(lib):
+            assert gdn._L() is lib
+        assert gdn._L() is dbg
+    assert gdn._L() is lib
