@@ -1,0 +1,193 @@
+"""GPU: seeded random shapes for the one-call steps against the calls they fuse, bit for bit.
+
+gdn_verify_step against gdn_rollback + gdn_conv_step + gdn_verify, and gdn_verify_tree_step against
+gdn_rollback_tree + gdn_conv_tree + gdn_verify_tree, over two chained windows (trees) whose sizes differ,
+on shapes drawn from a fixed seed: head counts and ratios, dk, dv (rows past a workgroup's block), window
+and tree sizes up to the limits, conv widths, bf16 and fp32 inputs and outputs, accept lengths and
+accepted nodes inside and outside their range.  The oracle checks of the same calls are in
+test_gpu_step.py and test_gpu_tree.py; this file widens the shapes the fused forms are held to.
+Every case prints its shape before touching the device.
+"""
+import random
+
+import pytest
+import torch
+
+from speculative_verify_gdn_amd import gdn, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu case]", *a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gdn.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(t):
+    return t.contiguous().cuda()
+
+
+def draw_heads(rng):
+    dk = rng.choice([32, 64, 128])
+    Hk = rng.choice([1, 2, 3])
+    Hv = Hk * rng.choice([1, 2, 3, 4, 6])
+    dv = rng.choice([8, 16, 24, 40, 64, 128, 136])
+    return dict(Hk=Hk, Hv=Hv, dk=dk, dv=dv)
+
+
+def step_cases(n, seed=2024):
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        h = draw_heads(rng)
+        K1 = rng.choice([1, 2, 3, 5, 8, 13, 16, 17, 31, 33, 48, 64])
+        K2 = rng.choice([1, 2, 4, 7, 16, 29, 64])
+        B = rng.randint(1, 4)
+        # keep every case small: the captured states of the longer window under 48 MB
+        if B * max(K1, K2) * h["Hv"] * h["dv"] * h["dk"] * 4 > 48 << 20:
+            continue
+        bf16 = rng.random() < 0.75
+        o_bf16 = rng.random() < 0.5
+        acc = [rng.randint(-2, K1 + 2) for _ in range(B)]
+        out.append((dict(B=B, bf16=bf16, **h), K1, K2, o_bf16, acc))
+    return out
+
+
+def tree_cases(n, seed=4049):
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        h = draw_heads(rng)
+        N1, N2 = rng.randint(1, 32), rng.randint(1, 32)
+        B = rng.randint(1, 3)
+        if B * max(N1, N2) * h["Hv"] * h["dv"] * h["dk"] * 4 > 48 << 20:
+            continue
+        W = rng.randint(2, 8)
+        bf16 = rng.random() < 0.75
+        o_bf16 = rng.random() < 0.5
+        shapes = (rng.choice(["random", "forest", "binary", "star", "chain"]),
+                  rng.choice(["random", "forest", "binary", "star", "chain"]))
+        node = [rng.randint(-2, N1 + 1) for _ in range(B)]
+        out.append((dict(B=B, W=W, bf16=bf16, **h), N1, N2, o_bf16, shapes, node))
+    return out
+
+
+def _step_out(wl, o_dtype):
+    B, K, Hv, dv, dk, C, W = wl.B, wl.T, wl.Hv, wl.dv, wl.dk, wl.C, wl.W
+    io = torch.bfloat16 if wl.bf16 else torch.float32
+    return dict(S_ckpt=torch.empty(B, Hv, dv, dk, device="cuda"), S_out=torch.empty(B, Hv, dv, dk, device="cuda"),
+                H=torch.empty(B, K - 1, Hv, dv, dk, device="cuda") if K > 1 else None,
+                o=torch.empty(B, K, Hv, dv, device="cuda", dtype=o_dtype),
+                y=torch.empty(B, K, C, device="cuda", dtype=io), win=torch.empty(B, W - 1 + K, C, device="cuda", dtype=io))
+
+
+def _fused(wl, d, out, prev=None):
+    gdn.verify_step(d["x"], d["w"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], out["S_out"], out["H"],
+                    out["o"], wl.Hk, prev=prev, S_in=None if prev else d["S_in"], hist=None if prev else d["hist"],
+                    S_ckpt=out["S_ckpt"], y=out["y"], win=out["win"])
+
+
+def _separate(wl, d, out, S_start, hist):
+    hist = hist.clone()
+    gdn.conv_step(d["x"], d["w"], hist, out["y"], out["win"])
+    gdn.verify(out["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], S_start, out["S_out"], out["H"],
+               out["o"], wl.Hk)
+    out["S_ckpt"].copy_(S_start)
+
+
+def _same(a, b, what, K):
+    for k in a:
+        if a[k] is None:
+            continue
+        if K == 1 and k in ("S_out", "o"):
+            # at K = 1 the separate gdn_verify takes its decode kernel (another rounding order)
+            ref = b[k].double()
+            assert (a[k].double() - ref).abs().max() <= 1e-5 * max(1.0, float(ref.abs().max())), \
+                "%s: %s differs" % (what, k)
+            continue
+        assert torch.equal(a[k], b[k]), "%s: %s differs" % (what, k)
+
+
+@pytest.mark.parametrize("over,K1,K2,o_bf16,acc", step_cases(36))
+def test_verify_step_random_shapes(over, K1, K2, o_bf16, acc):
+    wl1 = synth.small("verify16", T=K1, **over)
+    wl2 = synth.small("verify16", T=K2, **over)
+    o_dtype = torch.bfloat16 if o_bf16 else torch.float32
+    say("verify_step sweep", over, "K", K1, "->", K2, "o bf16" if o_bf16 else "o f32", "accept", acc)
+    d1 = {k: dev(v) for k, v in synth.make_inputs(wl1, seed=K1 + 7 * K2).items()}
+    d2 = {k: dev(v) for k, v in synth.make_inputs(wl2, seed=K1 + 7 * K2 + 1).items()}
+    d2["w"] = d1["w"]
+    accept = torch.tensor(acc, dtype=torch.int32, device="cuda")
+    A, A_ref = _step_out(wl1, o_dtype), _step_out(wl1, o_dtype)
+    _fused(wl1, d1, A)
+    _separate(wl1, d1, A_ref, d1["S_in"], d1["hist"])
+    torch.cuda.synchronize()
+    _same(A, A_ref, "first window", K1)
+    Bo, B_ref = _step_out(wl2, o_dtype), _step_out(wl2, o_dtype)
+    _fused(wl2, d2, Bo, prev=(accept, A["S_ckpt"], A["H"], A["S_out"], A["win"]))
+    # the reference continues from the fused first window, so the second window is compared on its own
+    S_start = A["S_out"].clone()
+    hist = d1["hist"].clone()
+    gdn.rollback(accept, K1, A["S_ckpt"], A["H"], S_start, hist, A["win"])
+    _separate(wl2, d2, B_ref, S_start, hist)
+    torch.cuda.synchronize()
+    _same(Bo, B_ref, "second window", K2)
+
+
+def _tree_out(wl, o_dtype):
+    B, N, Hv, dv, dk, C, W = wl.B, wl.T, wl.Hv, wl.dv, wl.dk, wl.C, wl.W
+    io = torch.bfloat16 if wl.bf16 else torch.float32
+    return dict(S_ckpt=torch.empty(B, Hv, dv, dk, device="cuda"), H=torch.empty(B, N, Hv, dv, dk, device="cuda"),
+                o=torch.empty(B, N, Hv, dv, device="cuda", dtype=o_dtype),
+                y=torch.empty(B, N, C, device="cuda", dtype=io), hist_out=torch.empty(B, W - 1, C, device="cuda", dtype=io))
+
+
+def _tree_fused(wl, d, par, out, S_prev_ckpt, hist_prev, prev=None):
+    gdn.verify_tree_step(d["x"], d["w"], par, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], out["H"],
+                         out["o"], out["y"], wl.Hk, S_prev_ckpt, hist_prev, prev=prev, S_ckpt=out["S_ckpt"],
+                         hist_out=out["hist_out"])
+
+
+def _tree_separate(wl, d, par, out, S_start, hist):
+    gdn.conv_tree(d["x"], d["w"], hist, par, out["y"])
+    gdn.verify_tree(out["y"], d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], par, S_start, out["H"], out["o"],
+                    wl.Hk)
+    out["S_ckpt"].copy_(S_start)
+    out["hist_out"].copy_(hist)
+
+
+@pytest.mark.parametrize("over,N1,N2,o_bf16,shapes,node", tree_cases(30))
+def test_verify_tree_step_random_shapes(over, N1, N2, o_bf16, shapes, node):
+    wl1 = synth.small("verify16", T=N1, **over)
+    wl2 = synth.small("verify16", T=N2, **over)
+    o_dtype = torch.bfloat16 if o_bf16 else torch.float32
+    say("verify_tree_step sweep", over, "N", N1, "->", N2, shapes, "o bf16" if o_bf16 else "o f32", "node", node)
+    d1 = {k: dev(v) for k, v in synth.make_inputs(wl1, seed=N1 + 5 * N2).items()}
+    d2 = {k: dev(v) for k, v in synth.make_inputs(wl2, seed=N1 + 5 * N2 + 1).items()}
+    d2["w"] = d1["w"]
+    par1 = dev(synth.make_tree(wl1.B, N1, seed=N1, shape=shapes[0]))
+    par2 = dev(synth.make_tree(wl2.B, N2, seed=N2 + 1, shape=shapes[1]))
+    nd = torch.tensor(node, dtype=torch.int32, device="cuda")
+    A, A_ref = _tree_out(wl1, o_dtype), _tree_out(wl1, o_dtype)
+    _tree_fused(wl1, d1, par1, A, d1["S_in"], d1["hist"])
+    _tree_separate(wl1, d1, par1, A_ref, d1["S_in"], d1["hist"])
+    torch.cuda.synchronize()
+    for k in A:
+        assert torch.equal(A[k], A_ref[k]), "first tree: %s differs" % k
+    Bo, B_ref = _tree_out(wl2, o_dtype), _tree_out(wl2, o_dtype)
+    _tree_fused(wl2, d2, par2, Bo, A["S_ckpt"], A["hist_out"], prev=(nd, par1, A["H"], d1["x"]))
+    S_start = torch.empty_like(d1["S_in"])
+    hist = A["hist_out"].clone()
+    gdn.rollback_tree(nd, par1, A["S_ckpt"], A["H"], S_start, d1["x"], hist)
+    _tree_separate(wl2, d2, par2, B_ref, S_start, hist)
+    torch.cuda.synchronize()
+    for k in Bo:
+        assert torch.equal(Bo[k], B_ref[k]), "second tree: %s differs" % k
