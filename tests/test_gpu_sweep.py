@@ -1,18 +1,22 @@
-"""GPU: seeded random shapes for the one-call steps against the calls they fuse, bit for bit.
+"""GPU: seeded random shapes, widening the shapes the fixed cases of the other GPU files cover.
 
-gdn_verify_step against gdn_rollback + gdn_conv_step + gdn_verify, and gdn_verify_tree_step against
-gdn_rollback_tree + gdn_conv_tree + gdn_verify_tree, over two chained windows (trees) whose sizes differ,
-on shapes drawn from a fixed seed: head counts and ratios, dk, dv (rows past a workgroup's block), window
-and tree sizes up to the limits, conv widths, bf16 and fp32 inputs and outputs, accept lengths and
-accepted nodes inside and outside their range.  The oracle checks of the same calls are in
-test_gpu_step.py and test_gpu_tree.py; this file widens the shapes the fused forms are held to.
-Every case prints its shape before touching the device.
+- gdn_verify_step against gdn_rollback + gdn_conv_step + gdn_verify, and gdn_verify_tree_step against
+  gdn_rollback_tree + gdn_conv_tree + gdn_verify_tree, bit for bit, over two chained windows (trees) whose
+  sizes differ;
+- gdn_verify and gdn_prefill_chunked against the oracle, at the stated bar (2e-3 of each state's Frobenius
+  norm) and the 1e-4 regression guard beside it.
+Shapes are drawn from fixed seeds: head counts and ratios, dk, dv (rows past a workgroup's block), window,
+tree and prompt sizes up to the limits, chunk lengths, conv widths, bf16 and fp32 inputs and outputs, weak
+decay, accept lengths and accepted nodes inside and outside their range.  Every case prints its shape
+before touching the device.
 """
 import random
 
+import numpy as np
 import pytest
 import torch
 
+import oracle
 from speculative_verify_gdn_amd import gdn, synth
 
 pytestmark = pytest.mark.gpu
@@ -191,3 +195,108 @@ def test_verify_tree_step_random_shapes(over, N1, N2, o_bf16, shapes, node):
     torch.cuda.synchronize()
     for k in Bo:
         assert torch.equal(Bo[k], B_ref[k]), "second tree: %s differs" % k
+
+
+# ------------------------------------------------------------------ against the oracle
+TOL = 2e-3
+GUARD = 1e-4    # regression guard beside the bar (observed worst ~1e-6 of the state norm)
+
+
+def f64(t):
+    return t.double().cpu().numpy()
+
+
+def check_states(gpu, ref, what):
+    err = np.abs(gpu.astype(np.float64) - ref).max(axis=(-1, -2))
+    fro = np.linalg.norm(ref, axis=(-1, -2))
+    worst = float(np.max(err / np.maximum(fro, 1e-30)))
+    print("[parity] %s worst err/fro %.3g" % (what, worst), flush=True)
+    assert np.all(err <= TOL * fro), "%s: worst err/fro = %.3g" % (what, worst)
+    assert worst <= GUARD, "%s: worst err/fro %.3g above the regression guard" % (what, worst)
+
+
+def check_o(o_gpu, o_ref, norms, bf16_out):
+    # norms [B][T][Hv]: the Frobenius norm of the state after each token (|o_t| <= it when |q^| = 1)
+    bound = TOL * norms[..., None] + (np.abs(o_ref) * 2.0 ** -8 if bf16_out else 0.0)
+    err = np.abs(o_gpu.astype(np.float64) - o_ref)
+    assert np.all(err <= bound), "o: worst err/bound = %.3g" % float(np.max(err / np.maximum(bound, 1e-30)))
+
+
+def verify_cases(n, seed=8081):
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        h = draw_heads(rng)
+        K = rng.randint(1, 64)
+        B = rng.randint(1, 3)
+        if B * K * h["Hv"] * h["dv"] * h["dk"] > 24 << 20:
+            continue
+        out.append((dict(B=B, T=K, bf16=rng.random() < 0.75, **h), rng.random() < 0.5, rng.random() < 0.3))
+    return out
+
+
+@pytest.mark.parametrize("over,o_bf16,weak", verify_cases(20))
+def test_verify_random_shapes_against_oracle(over, o_bf16, weak):
+    wl = synth.small("verify16", **over)
+    say("verify sweep vs oracle", over, "o bf16" if o_bf16 else "o f32", "weak decay" if weak else "")
+    inp = synth.make_inputs(wl, seed=wl.T + 3 * wl.Hv, weak_decay=weak)
+    qkv = synth.make_qkv(wl, seed=wl.T + 3 * wl.Hv)
+    d = {k: dev(v) for k, v in inp.items()}
+    S_out = torch.empty_like(d["S_in"])
+    H = torch.empty(wl.B, wl.T - 1, wl.Hv, wl.dv, wl.dk, device="cuda") if wl.T > 1 else None
+    o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda", dtype=torch.bfloat16 if o_bf16 else torch.float32)
+    gdn.verify(dev(qkv), d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, H, o, wl.Hk)
+    torch.cuda.synchronize()
+    S_ref, H_ref, o_ref = oracle.gdn_recurrent_f64(f64(qkv), f64(inp["beta_raw"]), f64(inp["alpha"]),
+                                                   f64(inp["dt_bias"]), f64(inp["A_log"]), f64(inp["S_in"]), wl.Hk)
+    check_states(S_out.cpu().numpy(), S_ref, "S_out")
+    states = S_ref[:, None] if H is None else np.concatenate([H_ref, S_ref[:, None]], axis=1)
+    if H is not None:
+        check_states(H.cpu().numpy(), H_ref, "H")
+    check_o(o.float().cpu().numpy(), o_ref, np.linalg.norm(states, axis=(-1, -2)), o_bf16)
+
+
+def prefill_cases(n, seed=1213):
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        dk = rng.choice([32, 64, 128])
+        Hk = rng.choice([1, 2])
+        Hv = Hk * rng.choice([1, 2, 3])
+        dv = rng.choice([16, 40, 64, 128, 160])
+        T = rng.choice([1, 9, 64, 65, 130, 257, 400])
+        chunk = rng.choice([16, 32, 64])
+        B = rng.randint(1, 2)
+        bf16 = rng.random() < 0.85
+        out.append((dict(B=B, T=T, Hk=Hk, Hv=Hv, dk=dk, dv=dv, bf16=bf16), chunk, rng.random() < 0.3,
+                    rng.random() < 0.5))
+    return out
+
+
+@pytest.mark.parametrize("over,chunk,o_bf16,weak", prefill_cases(16))
+def test_prefill_random_shapes_against_oracle(over, chunk, o_bf16, weak):
+    wl = synth.small("prefill", **over)
+    say("prefill sweep vs oracle", over, "chunk", chunk, "o bf16" if o_bf16 else "o f32",
+        "weak decay" if weak else "")
+    inp = synth.make_inputs(wl, seed=wl.T + wl.dv, weak_decay=weak)
+    qkv = synth.make_qkv(wl, seed=wl.T + wl.dv)
+    d = {k: dev(v) for k, v in inp.items()}
+    S_out = torch.empty_like(d["S_in"])
+    o = torch.empty(wl.B, wl.T, wl.Hv, wl.dv, device="cuda", dtype=torch.bfloat16 if o_bf16 else torch.float32)
+    gdn.prefill_chunked(dev(qkv), d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, o, wl.Hk,
+                        chunk=chunk)
+    torch.cuda.synchronize()
+    # the oracle in segments of 64 tokens, the state chained, with the state norm after every token
+    S = f64(inp["S_in"])
+    q, br, al = f64(qkv), f64(inp["beta_raw"]), f64(inp["alpha"])
+    os_, norms = [], []
+    for t0 in range(0, wl.T, 64):
+        t1 = min(wl.T, t0 + 64)
+        S_new, H, o_seg = oracle.gdn_recurrent_f64(q[:, t0:t1], br[:, t0:t1], al[:, t0:t1], f64(inp["dt_bias"]),
+                                                   f64(inp["A_log"]), S, wl.Hk)
+        states = S_new[:, None] if H is None or H.shape[1] == 0 else np.concatenate([H, S_new[:, None]], axis=1)
+        norms.append(np.linalg.norm(states, axis=(-1, -2)))
+        os_.append(o_seg)
+        S = S_new
+    check_states(S_out.cpu().numpy(), S, "prefill S_out")
+    check_o(o.float().cpu().numpy(), np.concatenate(os_, axis=1), np.concatenate(norms, axis=1), o_bf16)
