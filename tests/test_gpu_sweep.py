@@ -4,7 +4,8 @@
   gdn_rollback_tree + gdn_conv_tree + gdn_verify_tree, bit for bit, over two chained windows (trees) whose
   sizes differ;
 - gdn_verify and gdn_prefill_chunked against the oracle, at the stated bar (2e-3 of each state's Frobenius
-  norm) and the 1e-4 regression guard beside it.
+  norm) and the 1e-4 regression guard beside it;
+- ragged gdn_verify_ex and gdn_conv_step_ex against one call per sequence with its own length, bit for bit.
 Shapes are drawn from fixed seeds: head counts and ratios, dk, dv (rows past a workgroup's block), window,
 tree and prompt sizes up to the limits, chunk lengths, conv widths, bf16 and fp32 inputs and outputs, weak
 decay, accept lengths and accepted nodes inside and outside their range.  Every case prints its shape
@@ -300,3 +301,85 @@ def test_prefill_random_shapes_against_oracle(over, chunk, o_bf16, weak):
         S = S_new
     check_states(S_out.cpu().numpy(), S, "prefill S_out")
     check_o(o.float().cpu().numpy(), np.concatenate(os_, axis=1), np.concatenate(norms, axis=1), o_bf16)
+
+
+# ------------------------------------------------------------------ ragged batches against one call per sequence
+def ragged_cases(n, seed=5151):
+    rng = random.Random(seed)
+    out = []
+    while len(out) < n:
+        h = draw_heads(rng)
+        K = rng.choice([2, 5, 8, 16, 23, 32, 64])
+        B = rng.randint(2, 5)
+        if B * K * h["Hv"] * h["dv"] * h["dk"] * 4 > 48 << 20:
+            continue
+        lens = [rng.randint(1, K) for _ in range(B)]
+        out.append((dict(B=B, T=K, bf16=rng.random() < 0.75, **h), lens, rng.random() < 0.5))
+    return out
+
+
+@pytest.mark.parametrize("over,lens,stacked", ragged_cases(16))
+def test_ragged_verify_equals_one_call_per_sequence(over, lens, stacked):
+    """gdn_verify_ex with per-sequence lengths (and, half the cases, gates read out of one stacked beta|alpha row)
+    against gdn_verify on each sequence alone with its own length: the same bits (a one-token sequence alone takes
+    the decode kernel, another rounding order: within 1e-5); slots past a sequence's length stay untouched."""
+    wl = synth.small("verify16", **over)
+    say("ragged verify sweep", over, "lens", lens, "stacked gates" if stacked else "")
+    inp = synth.make_inputs(wl, seed=sum(lens) + wl.Hv)
+    qkv = dev(synth.make_qkv(wl, seed=sum(lens) + wl.Hv))
+    d = {k: dev(v) for k, v in inp.items()}
+    B, K, Hv, dv, dk = wl.B, wl.T, wl.Hv, wl.dv, wl.dk
+    S_out = torch.full_like(d["S_in"], 7.0)
+    H = torch.full((B, K - 1, Hv, dv, dk), 7.0, device="cuda")
+    o = torch.full((B, K, Hv, dv), 7.0, device="cuda")
+    if stacked:
+        st = torch.cat([d["beta_raw"], d["alpha"]], dim=-1).contiguous()
+        gdn.verify(qkv, st[..., :Hv], st[..., Hv:], d["dt_bias"], d["A_log"], d["S_in"], S_out, H, o, wl.Hk,
+                   lens=dev(torch.tensor(lens, dtype=torch.int32)), gate_stride=2 * Hv)
+    else:
+        gdn.verify(qkv, d["beta_raw"], d["alpha"], d["dt_bias"], d["A_log"], d["S_in"], S_out, H, o, wl.Hk,
+                   lens=dev(torch.tensor(lens, dtype=torch.int32)))
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        S1 = torch.empty_like(d["S_in"][b:b + 1])
+        H1 = torch.empty(1, L - 1, Hv, dv, dk, device="cuda") if L > 1 else None
+        o1 = torch.empty(1, L, Hv, dv, device="cuda")
+        gdn.verify(qkv[b:b + 1, :L].contiguous(), d["beta_raw"][b:b + 1, :L].contiguous(),
+                   d["alpha"][b:b + 1, :L].contiguous(), d["dt_bias"], d["A_log"], d["S_in"][b:b + 1].contiguous(),
+                   S1, H1, o1, wl.Hk)
+        torch.cuda.synchronize()
+        if L == 1:
+            ref = S1[0].double()
+            assert (S_out[b].double() - ref).abs().max() <= 1e-5 * max(1.0, float(ref.abs().max()))
+            ref = o1[0].double()
+            assert (o[b, :1].double() - ref).abs().max() <= 1e-5 * max(1.0, float(ref.abs().max()))
+        else:
+            assert torch.equal(S_out[b], S1[0]), "sequence %d: S_out" % b
+            assert torch.equal(H[b, :L - 1], H1[0]), "sequence %d: H" % b
+            assert torch.equal(o[b, :L], o1[0]), "sequence %d: o" % b
+        assert bool((H[b, L - 1:] == 7.0).all()) and bool((o[b, L:] == 7.0).all()), "sequence %d: slots past it" % b
+
+
+@pytest.mark.parametrize("over,lens,stacked", ragged_cases(8, seed=6262))
+def test_ragged_conv_step_equals_one_call_per_sequence(over, lens, stacked):
+    """gdn_conv_step_ex with per-sequence lengths against gdn_conv_step on each sequence alone, bit for bit:
+    y, the window and the written-back history (window rows lens[b] .. lens[b]+W-2)."""
+    wl = synth.small("verify16", **over)
+    say("ragged conv sweep", over, "lens", lens)
+    inp = synth.make_inputs(wl, seed=sum(lens) + 3)
+    x, w, hist0 = dev(inp["x"]), dev(inp["w"]), dev(inp["hist"])
+    B, K, C, W = wl.B, wl.T, wl.C, wl.W
+    hist = hist0.clone()
+    y = torch.zeros_like(x)
+    win = torch.zeros(B, W - 1 + K, C, device="cuda", dtype=x.dtype)
+    gdn.conv_step(x, w, hist, y, win, lens=dev(torch.tensor(lens, dtype=torch.int32)))
+    torch.cuda.synchronize()
+    for b, L in enumerate(lens):
+        h1 = hist0[b:b + 1].clone()
+        y1 = torch.empty(1, L, C, device="cuda", dtype=x.dtype)
+        w1 = torch.empty(1, W - 1 + L, C, device="cuda", dtype=x.dtype)
+        gdn.conv_step(x[b:b + 1, :L].contiguous(), w, h1, y1, w1)
+        torch.cuda.synchronize()
+        assert torch.equal(y[b, :L], y1[0]), "sequence %d: y" % b
+        assert torch.equal(win[b, :W - 1 + L], w1[0]), "sequence %d: window" % b
+        assert torch.equal(hist[b], h1[0]), "sequence %d: history" % b
