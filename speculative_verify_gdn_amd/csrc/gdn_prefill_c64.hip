@@ -190,6 +190,9 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
         // lane t: raw beta and raw alpha of token t, each in its own register (combining them at load
         // time would wait for the prefetch right away)
         uint32_t gbr = 0, gal = 0;
+        float dtb, eal;                           // the head's dt_bias and e^{A_log}
+        head_gate_consts(a.dt_bias, a.A_log, h, dtb, eal);
+        const bool raw_gates = a.dt_bias != nullptr;
         float gbeta = 0.f, gG = 0.f;              // lane t: beta_t and G_t of the chunk staged last
         f32x4_t gNa, gNb;                         // diagonal block p of A of the chunk staged last, A and B order
         const int qoff = ((16 * p + u) * C + hk * kDK + 8 * jp) * 2;
@@ -256,7 +259,7 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
             // the gates (lane = token) and their running sum, from the raw bits loaded with the chunk
             // (the next prefetch overwrites them)
             float beta = 0.f, gg = 0.f;
-            if (lane < Lv) gate(bf16_lo(gbr), bf16_lo(gal), a.dt_bias, a.A_log, h, beta, gg);
+            if (lane < Lv) gate(bf16_lo(gbr), bf16_lo(gal), raw_gates, dtb, eal, beta, gg);
             gbeta = beta;
             gG = wave_scan(gg);
             if (mk) GDN_TLV(8, gG);
@@ -432,9 +435,9 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
     }
     // v[token 16 tt + 4 g + e][row of rt] of the chunk to process next (raw bf16)
     uint32_t vreg[4][4];             // v of rows row0, row0 + 1 (bf16 pair) for token 16 tt + 4 g + e
-    const int voff = ((4 * g) * C + 2 * Hk * kDK + h * dv + row0) * 2;
+    // rows past dv address past the resource and read zeros (no select per value)
+    const int voff = live0 ? ((4 * g) * C + 2 * Hk * kDK + h * dv + row0) * 2 : 0x7ffffff0;
     auto prefetch_v = [&](int c0) __attribute__((always_inline)) {
-        // rows past dv read another channel or past the chunk (zero): unused
         const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(c0);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
@@ -500,10 +503,9 @@ __global__ __launch_bounds__(kC64Threads) void prefill_c64_kernel(PrefillArgs a)
                 const float ev[4] = {fe4.x, fe4.y, fe4.z, fe4.w};
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
-                    const bool lv = rt ? live1 : live0;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float v = lv ? (rt ? bf16_hi(vreg[tt][e]) : bf16_lo(vreg[tt][e])) : 0.f;
+                        const float v = rt ? bf16_hi(vreg[tt][e]) : bf16_lo(vreg[tt][e]);
                         X[tt][rt][e] = __builtin_fmaf(-av[e], P[tt][rt][e], bv[e] * v);
                         O[tt][rt][e] = ev[e] * R[tt][rt][e];
                     }

@@ -159,6 +159,9 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
     // prep wave 0, lane t: raw beta and raw alpha, each in its own register (combining them at load
     // time would wait for the prefetch right away)
     uint32_t gbr = 0, gal = 0;
+    float dtb, eal;                               // the head's dt_bias and e^{A_log}
+    head_gate_consts(a.dt_bias, a.A_log, h, dtb, eal);
+    const bool raw_gates = a.dt_bias != nullptr;
     // staging role: piece sr of token row stp (+ TPP per pass)
     const int qoff = ((ptid / CPR) * C + hk * DK + 8 * (ptid % CPR)) * 2;
     const int goff = (lane0 * Hv + h) * 2;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void prefill_wy_kernel(PrefillArgs a)
         if (pwave == 0) {
             // gates, their running sum and the decay factors; lane = token
             float beta = 0.f, g = 0.f;
-            if (lane < Lv) gate(bf16_lo(gbr), bf16_lo(gal), a.dt_bias, a.A_log, h, beta, g);
+            if (lane < Lv) gate(bf16_lo(gbr), bf16_lo(gal), raw_gates, dtb, eal, beta, g);
             float G = g;
 #pragma unroll
             for (int d = 1; d < L; d <<= 1) {

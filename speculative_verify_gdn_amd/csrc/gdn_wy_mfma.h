@@ -27,20 +27,29 @@ __device__ __forceinline__ int pi_slot(int x) { return ((x >> 4) << 2) | (x & 3)
 // it spreads the staging writes over the banks)
 __device__ __forceinline__ int qk_rec(int lane, int m) { return lane ^ ((m & 3) << 2); }
 
-// gates of one token for value head h: beta = sigmoid(raw beta), g = -softplus(alpha + dt_bias) e^{A_log};
-// with dt_bias == NULL the inputs are beta and g themselves
-__device__ __forceinline__ void gate(float braw, float al, const float* dt_bias, const float* A_log, int h,
-                                     float& beta, float& g)
+// gates of one token: beta = sigmoid(raw beta), g = -softplus(alpha + dt_bias) e^{A_log}, with
+// dtb = dt_bias and eal = e^{A_log} of the value head, read once per workgroup by the caller (a load
+// in the chunk loop is repeated every chunk and waited for there); raw == false: the inputs are beta
+// and g themselves
+__device__ __forceinline__ void gate(float braw, float al, bool raw, float dtb, float eal, float& beta, float& g)
 {
-    if (dt_bias != nullptr) {
+    if (raw) {
         beta = __frcp_rn(1.0f + __expf(-braw));
-        const float a = al + dt_bias[h];
+        const float a = al + dtb;
         const float sp = a > 20.0f ? a : __logf(1.0f + __expf(a));
-        g = -sp * __expf(A_log[h]);
+        g = -sp * eal;
     } else {
         beta = braw;
         g = al;
     }
+}
+
+// dt_bias and e^{A_log} of value head h (zeros without raw gates)
+__device__ __forceinline__ void head_gate_consts(const float* dt_bias, const float* A_log, int h, float& dtb,
+                                                 float& eal)
+{
+    dtb = dt_bias != nullptr ? dt_bias[h] : 0.f;
+    eal = dt_bias != nullptr ? __expf(A_log[h]) : 0.f;
 }
 
 // value head of workgroup row y: the value heads of key head kh sit at rows congruent mod 8
