@@ -157,7 +157,7 @@ int gdn_conv_step(const void *x, const float *w, void *hist, void *y, void *win_
  *                         0..t; may be NULL (no capture); must not overlap
  *                         S_in / S_out
  *   o        [B][K][Hv][dv] o_dtype, o_t = S_t q^_t
- *   B >= 0; 1 <= K <= 32; Hk >= 1; Hv % Hk == 0;
+ *   B >= 0; 1 <= K <= 64 (GDN_EUNSUPPORTED above); Hk >= 1; Hv % Hk == 0;
  *   dk in {32, 64, 128}; dv a multiple of 8
  *   l2_eps >= 0
  */
